@@ -1,0 +1,332 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself: the checks are hand-worked
+values from tests/golden (each with its citation), brute force against
+numpy's integer matmul, closed forms (sigmoid, softmax), the dequantisation
+error bound, and invariants.  Each is chosen so that a plausible slip in the
+oracle -- a dropped term, a wrong sign, a swapped index, a transposed
+operand, gate and up exchanged -- fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- quantisation
+@pytest.mark.parametrize("case", _gold("quant_pins.json")["cases"])
+def test_quant_hand_worked(case):
+    q, s = oracle.quantize_rows(np.array(case["x"], np.float32))
+    assert s[0] == np.float32(case["s"])
+    assert q[0].tolist() == case["q"]
+
+
+def test_quant_invariants():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((37, 203)).astype(np.float32)
+    x[:, 5] *= 40.0
+    q, s = oracle.quantize_rows(x)
+    # |q| <= 127 and the row's largest magnitude maps to +-127
+    assert np.abs(q.astype(np.int32)).max() <= 127
+    am = np.argmax(np.abs(x), axis=1)
+    assert np.all(np.abs(q[np.arange(37), am].astype(np.int32)) == 127)
+    assert np.all(np.sign(q[np.arange(37), am]) == np.sign(x[np.arange(37), am]))
+    # sign symmetry
+    qn, sn = oracle.quantize_rows(-x)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    # power-of-two scaling: codes unchanged, scale scaled exactly
+    for p in (-7, 3, 20):
+        qp, sp = oracle.quantize_rows(x * np.float32(2.0 ** p))
+        assert np.array_equal(qp, q)
+        assert np.array_equal(sp, s * np.float32(2.0 ** p))
+    # s is max|x| / 127 (to one fp32 rounding)
+    amax = np.abs(x).max(axis=1).astype(np.float64)
+    assert np.all(np.abs(s.astype(np.float64) - amax / 127.0) <= amax / 127.0 * 2.0 ** -23)
+    # dequantisation error bound of round-to-nearest: |x - q*s| <= s/2 (+ fp32 slack)
+    err = np.abs(x.astype(np.float64) - q.astype(np.float64) * s[:, None].astype(np.float64))
+    assert np.all(err <= s[:, None] * (0.5 + 1e-5))
+
+
+def test_quant_is_round_half_even_of_fp32_quotient():
+    # the decision is taken on the fp32 quotient x/s: q is its nearest
+    # integer, ties going to the even one.
+    rng = np.random.default_rng(2)
+    x = (rng.integers(-508, 509, size=(8, 64)) / 4.0).astype(np.float32)  # many exact halves
+    x[:, 0] = 127.0  # s = 1 exactly, so x/s = x
+    q, s = oracle.quantize_rows(x)
+    assert np.all(s == 1.0)
+    v = x.astype(np.float64)
+    fl = np.floor(v)
+    frac = v - fl
+    expect = np.where(frac < 0.5, fl, np.where(frac > 0.5, fl + 1, np.where(fl % 2 == 0, fl, fl + 1)))
+    assert np.array_equal(q.astype(np.float64), np.clip(expect, -128, 127))
+
+
+# ---------------------------------------------------------------- int GEMM
+def test_gemm_hand_worked():
+    g = _gold("gemm_pins.json")
+    acc = oracle.gemm_i32(np.array(g["a"], np.int8), np.array(g["b_nk"], np.int8))
+    assert acc.tolist() == g["acc"]
+    out = oracle.dense_w8a8(np.array(g["a"], np.int8), np.array(g["s_a"], np.float32),
+                            np.array(g["b_nk"], np.int8), np.array(g["s_b"], np.float32))
+    assert out.tolist() == g["out"]
+    ex = g["extreme"]
+    acc = oracle.gemm_i32(np.array(ex["a"], np.int8), np.array(ex["b_nk"], np.int8))
+    assert acc.tolist() == ex["acc"]
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 7), (17, 33, 65), (64, 48, 256), (5, 130, 1000)])
+def test_gemm_brute_force(M, N, K):
+    rng = np.random.default_rng(M * 1000 + N * 10 + K)
+    a = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+    b = rng.integers(-128, 128, size=(N, K)).astype(np.int8)
+    a[0, 0] = -128
+    b[0, 0] = -128
+    ref = a.astype(np.int64) @ b.astype(np.int64).T
+    assert np.array_equal(oracle.gemm_i32(a, b).astype(np.int64), ref)
+
+
+def test_dense_scales_against_fp64():
+    rng = np.random.default_rng(5)
+    M, N, K = 9, 31, 300
+    a = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    b = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    sa = rng.uniform(0.001, 0.1, M).astype(np.float32)
+    sb = rng.uniform(0.001, 0.01, N).astype(np.float32)
+    out = oracle.dense_w8a8(a, sa, b, sb)
+    ref = (a.astype(np.int64) @ b.astype(np.int64).T).astype(np.float64) * sa[:, None] * sb[None, :]
+    # two fp32 roundings of an exact product, plus the int->float rounding
+    assert np.all(np.abs(out - ref) <= np.abs(ref) * 3 * 2.0 ** -24)
+
+
+# ---------------------------------------------------------------- router
+def test_router_hand_and_library():
+    x = np.array([[1.0, 2.0]], np.float32)
+    wr = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0]], np.float32)
+    b = np.array([0.5, 0.0, -1.0], np.float32)
+    assert oracle.router_logits(x, wr, b).tolist() == [[1.5, 2.0, 2.0]]
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((11, 257)).astype(np.float32)
+    wr = (rng.standard_normal((6, 257)) * 0.02).astype(np.float32)
+    b = rng.standard_normal(6).astype(np.float32)
+    ref = x.astype(np.float64) @ wr.astype(np.float64).T + b
+    got = oracle.router_logits(x, wr, b)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+    assert np.allclose(oracle.router_logits(x, wr, None), ref - b, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- top-k
+@pytest.mark.parametrize("case", _gold("topk_pins.json")["cases"])
+def test_topk_hand_worked(case):
+    ids, w = oracle.topk_softmax(np.array([case["logits"]], np.float64), case["k"])
+    assert ids[0].tolist() == case["ids"]
+    assert np.allclose(w[0], np.array(case["w"], np.float32), rtol=0, atol=1e-7)
+
+
+def test_topk_closed_forms_and_invariants():
+    rng = np.random.default_rng(4)
+    T, E = 200, 16
+    l = rng.standard_normal((T, E)) * 3
+    # k = E: the full softmax, in descending order
+    ids, w = oracle.topk_softmax(l, E)
+    sm = np.exp(l - l.max(1, keepdims=True))
+    sm /= sm.sum(1, keepdims=True)
+    assert np.array_equal(ids, np.argsort(-l, axis=1, kind="stable"))
+    assert np.allclose(w, np.take_along_axis(sm, ids, 1), rtol=1e-6, atol=1e-7)
+    # k = 2: w0 = sigmoid(l0 - l1)
+    ids, w = oracle.topk_softmax(l, 2)
+    top = np.take_along_axis(l, ids, 1)
+    assert np.allclose(w[:, 0], 1 / (1 + np.exp(-(top[:, 0] - top[:, 1]))), rtol=1e-6)
+    # k = 5: sum to one, descending, and the picked set is the top-5 by logit
+    ids, w = oracle.topk_softmax(l, 5)
+    assert np.allclose(w.sum(1), 1.0, atol=1e-6)
+    assert np.all(np.diff(w, axis=1) <= 0)
+    assert np.array_equal(ids, np.argsort(-l, axis=1, kind="stable")[:, :5])
+    # shifting all logits of a token changes nothing
+    ids2, w2 = oracle.topk_softmax(l + 123.0, 5)
+    assert np.array_equal(ids, ids2) and np.allclose(w, w2, atol=1e-7)
+
+
+# ---------------------------------------------------------------- permute
+def test_permute_against_stable_sort():
+    rng = np.random.default_rng(6)
+    T, E, k = 300, 12, 3
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    counts, offsets, sa = oracle.permute(ids, E)
+    assert np.array_equal(counts, np.bincount(ids.reshape(-1), minlength=E))
+    assert offsets[0] == 0 and np.array_equal(np.diff(offsets), counts)
+    assert np.array_equal(sa, np.argsort(ids.reshape(-1), kind="stable"))
+    for e in range(E):
+        seg = sa[offsets[e]:offsets[e + 1]]
+        assert np.all(ids.reshape(-1)[seg] == e)
+        assert np.all(np.diff(seg // k) > 0)  # ascending token order
+
+
+def test_permute_empty_experts():
+    ids = np.array([[3, 0], [3, 0], [0, 3]], np.int32)
+    counts, offsets, sa = oracle.permute(ids, 6)
+    assert counts.tolist() == [3, 0, 0, 3, 0, 0]
+    assert offsets.tolist() == [0, 3, 3, 3, 6, 6, 6]
+    assert sa.tolist() == [1, 3, 4, 0, 2, 5]
+
+
+# ---------------------------------------------------------------- SiLU
+def test_silu_values():
+    assert oracle.silu(np.float32(0.0)) == 0.0
+    assert oracle.silu(np.float32(1.0)) == np.float32(1.0 / (1.0 + math.exp(-1.0)))
+    assert oracle.silu(np.float32(-1.0)) == np.float32(-1.0 / (1.0 + math.exp(1.0)))
+    v = oracle.silu(np.float32(-100.0))
+    assert v == 0.0 and np.signbit(v)  # exp overflows to inf: -100/inf = -0, no NaN
+    assert oracle.silu(np.float32(100.0)) == np.float32(100.0)
+    g = np.linspace(-30, 30, 601).astype(np.float32)
+    got = oracle.silu(g).astype(np.float64)
+    ref = g.astype(np.float64) / (1.0 + np.exp(-g.astype(np.float64)))
+    # three fp32 roundings (exp, add, divide) of the exact value
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 4 * 2.0 ** -24 + 1e-45)
+
+
+# ---------------------------------------------------------------- expert FFN
+def _small_layer(T=12, H=64, E=4, k=2, I=32, seed=7, zero_bias=True):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x[:, 3] *= 20
+    wr = (rng.standard_normal((E, H)) * 0.05).astype(np.float32)
+    b = np.zeros(E, np.float32) if zero_bias else rng.standard_normal(E).astype(np.float32)
+    w_gu = rng.integers(-127, 128, size=(E, 2 * I, H)).astype(np.int8)
+    w_d = rng.integers(-127, 128, size=(E, H, I)).astype(np.int8)
+    s_gu = rng.uniform(1e-4, 1e-3, (E, 2 * I)).astype(np.float32)
+    s_d = rng.uniform(1e-4, 1e-3, (E, H)).astype(np.float32)
+    return x, wr, b, w_gu, s_gu, w_d, s_d
+
+
+def _ffn_fp64(xq_row, sx, e, wt, w_gu, s_gu, w_d, s_d, I, h_q=None, s_h=None):
+    """fp64 evaluation of one assignment from library matmuls."""
+    acc = w_gu[e].astype(np.int64) @ xq_row.astype(np.int64)
+    g = acc[:I] * float(sx) * s_gu[e, :I].astype(np.float64)
+    u = acc[I:] * float(sx) * s_gu[e, I:].astype(np.float64)
+    h = g / (1 + np.exp(-g)) * u
+    out = dict(acc=acc, h=h)
+    if h_q is not None:
+        accd = w_d[e].astype(np.int64) @ h_q.astype(np.int64)
+        out["accd"] = accd
+        out["o"] = wt * accd * float(s_h) * s_d[e].astype(np.float64)
+    return out
+
+
+def test_expert_ffn_against_library_matmul_fp64():
+    x, wr, b, w_gu, s_gu, w_d, s_d = _small_layer()
+    k, I = 2, 32
+    r = oracle.moe_forward(x, wr, b, w_gu, s_gu, w_d, s_d, k, want_acc=True, want_h=True)
+    for a in range(x.shape[0] * k):
+        t, j = divmod(a, k)
+        e = int(r["ids"][t, j])
+        ref = _ffn_fp64(r["x_q"][t], r["s_x"][t], e, float(r["w"][t, j]), w_gu, s_gu, w_d, s_d, I,
+                        r["h_q"][a], r["s_h"][a])
+        assert np.array_equal(r["acc_gu"][a].astype(np.int64), ref["acc"])
+        hmax = np.abs(ref["h"]).max()
+        assert np.all(np.abs(r["h"][a] - ref["h"]) <= 1e-5 * hmax)
+        assert np.array_equal(r["acc_d"][a].astype(np.int64), ref["accd"])
+        assert np.allclose(r["o"][a], ref["o"], rtol=1e-5, atol=1e-6 * np.abs(ref["o"]).max())
+        # requantised codes: the rounding of h/s_h, within one code where fp32 noise
+        # could move a value across a half-integer
+        v = ref["h"] / (np.abs(ref["h"]).max() / 127)
+        assert np.all(np.abs(r["h_q"][a].astype(np.int64) - np.rint(v)) <= 1)
+        clear = np.abs(np.abs(v - np.floor(v)) - 0.5) > 1e-3
+        assert np.array_equal(r["h_q"][a][clear].astype(np.int64), np.rint(v[clear]).astype(np.int64))
+
+
+def test_gate_and_up_not_exchanged():
+    # all gate rows large positive and all up rows +1: h = SiLU(g)*u > 0, with g = up-weighted
+    # only through the gate half.  Exchanging the halves gives a different sign pattern.
+    T, H, E, k, I = 2, 64, 1, 1, 16
+    x = np.ones((T, H), np.float32)
+    x[1] = -1.0
+    wr = np.zeros((E, H), np.float32)
+    w_gu = np.zeros((E, 2 * I, H), np.int8)
+    w_gu[0, :I, :] = 1    # gate: g = +H*s for token 0, -H*s for token 1
+    w_gu[0, I:, :] = 2    # up:   u = 2x gate
+    w_d = np.ones((E, H, I), np.int8)
+    s_gu = np.full((E, 2 * I), 1.0 / 64, np.float32)
+    s_d = np.ones((E, H), np.float32)
+    r = oracle.moe_forward(x, wr, None, w_gu, s_gu, w_d, s_d, k, want_h=True)
+    # token 0: g = 1*1*... x_q = 127, s_x = 1/127, acc_g = 127*64, g = 64*(1/127*127)/64 = 1
+    g0 = np.float32(1.0)
+    u0 = np.float32(2.0)
+    assert np.allclose(r["h"][0], oracle.silu(g0) * u0, rtol=1e-6)
+    # token 1: g = -1, u = -2  -> h = SiLU(-1) * -2 > 0 (exchanging would give SiLU(-2)*-1)
+    assert np.allclose(r["h"][1], oracle.silu(np.float32(-1.0)) * np.float32(-2.0), rtol=1e-6)
+
+
+# ---------------------------------------------------------------- whole layer
+def test_zero_input_zero_output():
+    x, wr, b, w_gu, s_gu, w_d, s_d = _small_layer()
+    x[:] = 0
+    r = oracle.moe_forward(x, wr, b, w_gu, s_gu, w_d, s_d, 2)
+    assert np.all(r["s_x"] == 0) and np.all(r["x_q"] == 0)
+    assert np.all(r["y"] == 0)
+
+
+def test_token_permutation_equivariance_and_batch_invariance():
+    x, wr, b, w_gu, s_gu, w_d, s_d = _small_layer(T=20)
+    full = oracle.moe_forward(x, wr, b, w_gu, s_gu, w_d, s_d, 2)
+    perm = np.random.default_rng(9).permutation(20)
+    p = oracle.moe_forward(x[perm], wr, b, w_gu, s_gu, w_d, s_d, 2)
+    assert np.array_equal(p["y"], full["y"][perm])
+    sub = [2, 5, 11, 19]
+    alone = oracle.moe_forward(x, wr, b, w_gu, s_gu, w_d, s_d, 2, route_tokens=sub)
+    assert np.array_equal(alone["y"], full["y"][sub])
+    part = oracle.moe_forward(x, wr, b, w_gu, s_gu, w_d, s_d, 2, tokens=sub)
+    assert np.array_equal(part["y"], full["y"][sub])
+
+
+def test_single_expert_reduces_to_dense_swiglu_ffn():
+    T, H, I = 6, 64, 32
+    x, wr, b, w_gu, s_gu, w_d, s_d = _small_layer(T=T, H=H, E=1, I=I)
+    r = oracle.moe_forward(x, wr, b, w_gu, s_gu, w_d, s_d, 1, want_h=True)
+    assert np.all(r["ids"] == 0) and np.all(r["w"] == 1.0)
+    # dense path from the oracle's own single-step routines (quant + dense GEMM) and numpy
+    xq, sx = oracle.quantize_rows(x)
+    gate = oracle.dense_w8a8(xq, sx, w_gu[0][:I], s_gu[0, :I])
+    up = oracle.dense_w8a8(xq, sx, w_gu[0][I:], s_gu[0, I:])
+    h = oracle.silu(gate) * up
+    assert np.array_equal(h, r["h"])
+    hq, sh = oracle.quantize_rows(h)
+    y = oracle.dense_w8a8(hq, sh, w_d[0], s_d[0])
+    assert np.array_equal(y, r["y"])
+
+
+def test_all_experts_reduces_to_softmax_mixture():
+    T, H, E, I = 5, 64, 4, 32
+    x, wr, b, w_gu, s_gu, w_d, s_d = _small_layer(T=T, H=H, E=E, I=I, zero_bias=False)
+    r = oracle.moe_forward(x, wr, b, w_gu, s_gu, w_d, s_d, E)
+    l = x.astype(np.float64) @ wr.astype(np.float64).T + b
+    p = np.exp(l - l.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    for t in range(T):
+        y = np.zeros(H)
+        for e in range(E):
+            a = t * E + list(r["ids"][t]).index(e)
+            f = _ffn_fp64(r["x_q"][t], r["s_x"][t], e, p[t, e], w_gu, s_gu, w_d, s_d, I,
+                          r["h_q"][a], r["s_h"][a])
+            y += f["o"]
+        assert np.allclose(r["y"][t], y, rtol=1e-5, atol=1e-5 * np.abs(y).max())
+
+
+def test_combine_order_and_k1():
+    rng = np.random.default_rng(8)
+    o = rng.standard_normal((4 * 3, 10)).astype(np.float32)
+    y = oracle.combine(o, 4, 3)
+    ref = (o[0::3].astype(np.float32) + o[1::3]) + o[2::3]
+    assert np.array_equal(y, ref)
+    assert np.array_equal(oracle.combine(o, 12, 1), o)
