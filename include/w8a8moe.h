@@ -1,0 +1,206 @@
+/*
+ * w8a8moe -- a W8A8 Mixture-of-Experts expert layer for AMD MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only; every device pointer is memory the
+ * caller owns (hipMalloc'd or a PyTorch tensor's storage).  The library never
+ * allocates, frees or keeps a pointer after a call returns, and it never
+ * synchronises the host: every entry point checks its arguments on the host,
+ * enqueues its kernels on the caller's stream and returns.  Results are valid
+ * once that stream has reached the point of the call.
+ *
+ * The computation follows these web pages (cited by title and section):
+ *  [K100AI]  "W8A8 quantisation of MiniMax-M3 on K100AI: an MoE inference
+ *            deployment guide", sec. 2.1 (q = clamp(round(x/s), -128, 127),
+ *            per-token activation scales, per-channel weight scales, the
+ *            [A,1] x [1,N] scale outer product applied inside the GEMM
+ *            epilogue), sec. 3.1 (batch the small per-expert GEMMs),
+ *            sec. 3.2 (pre-planned buffers for the routing reorder).
+ *  [HUNYUAN] "Tencent Hunyuan AI Infra: inference optimisation of a
+ *            100B-parameter model on Hopper GPUs", sec. 1.3 (FusedMoE:
+ *            gate, top-k, index preparation into contiguous per-expert
+ *            segments, gate-up GEMM reading the input through the routing
+ *            index, expert GEMM, weighted combine).
+ *  [DSV4]    "DeepSeek V4 '950' unified FP8 dataflow on H100", sec. 2.3
+ *            (low-precision inputs, wide accumulator, requantised output),
+ *            sec. 2.4 (weight scales per output channel), sec. 4.1 (router
+ *            kept in fp32).
+ *
+ * Status codes: every entry point returns a w8a8_status.  On an error no
+ * kernel has been enqueued (except W8A8_ERR_HIP, which reports a launch
+ * failure after earlier kernels of the same call may have been enqueued).
+ * w8a8_last_error() returns a thread-local message for the last failure.
+ *
+ * Thread safety: reentrant.  Calls that may run concurrently on the GPU need
+ * distinct workspaces and outputs.
+ */
+#ifndef W8A8MOE_H
+#define W8A8MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define W8A8_API __attribute__((visibility("default")))
+#else
+#define W8A8_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W8A8_OK = 0,
+    W8A8_ERR_INVALID_ARGUMENT = 1,  /* NULL pointer, negative size, bad enum */
+    W8A8_ERR_UNSUPPORTED_SHAPE = 2, /* a size outside the documented limits */
+    W8A8_ERR_WORKSPACE_TOO_SMALL = 3,
+    W8A8_ERR_MISALIGNED = 4,        /* a pointer or leading dimension not 16-byte aligned */
+    W8A8_ERR_HIP = 5                /* the HIP runtime reported an error */
+} w8a8_status;
+
+/* A hipStream_t passed as an opaque pointer; NULL is the default stream. */
+typedef void* w8a8_stream;
+
+/* Name of a status code (static storage; never NULL). */
+W8A8_API const char* w8a8_status_string(int status);
+
+/* Thread-local detail of the last non-OK status returned on this thread. */
+W8A8_API const char* w8a8_last_error(void);
+
+/* ABI version of this header: 1. */
+W8A8_API int w8a8_abi_version(void);
+
+/* -------------------------------------------------------------------------
+ * Per-row dynamic INT8 quantisation.  [K100AI] sec. 2.1.
+ *   s[r] = max_c |x[r][c]| / 127          (fp32, IEEE division)
+ *   q[r][c] = clamp(rne(x[r][c] / s[r]), -128, 127)   (fp32 quotient,
+ *                                                      round half to even)
+ * An all-zero row gives s = 0 and q = 0.  Used per token for activations
+ * and, offline, per output channel for weights ([DSV4] sec. 2.4).
+ *
+ * x      device, fp32, rows x cols with leading dimension ld (elements)
+ * q      device, int8, rows x cols, dense (leading dimension cols)
+ * scale  device, fp32, rows
+ * rows >= 0 (0 is a no-op), 1 <= cols <= 2^24, ld >= cols.
+ * Inputs must be finite (NaN/Inf give unspecified codes).
+ * ------------------------------------------------------------------------- */
+W8A8_API w8a8_status w8a8_quantize_rows(const float* x, int64_t rows, int64_t cols, int64_t ld, int8_t* q,
+                               float* scale, w8a8_stream stream);
+
+/* -------------------------------------------------------------------------
+ * Weight packing.  The GEMM kernels read the int8 weight operand in a
+ * tiled order: for each group g, each block of 16 output channels nb and
+ * each block of 64 reduction elements kb, one contiguous 1 KiB tile.
+ *
+ * kind W8A8_PACK_PLAIN   : output channels kept in order (dense GEMM and the
+ *                          MoE down projection, w[g] = [N][K]).
+ * kind W8A8_PACK_GATE_UP : w[g] = [2I][K] with rows 0..I-1 the gate and rows
+ *                          I..2I-1 the up projection; packed so each 16-row
+ *                          gate block is followed by the up block of the same
+ *                          16 channels (the SwiGLU epilogue then holds gate
+ *                          and up of one channel side by side).
+ *
+ * w       device, int8 [groups][n][k], dense
+ * packed  device, int8, w8a8_pack_weights_size() bytes (= groups*n*k)
+ * Limits: n % 32 == 0 (GATE_UP: n even and n/2 % 16 == 0), k % 64 == 0.
+ * ------------------------------------------------------------------------- */
+enum { W8A8_PACK_PLAIN = 0, W8A8_PACK_GATE_UP = 1 };
+
+W8A8_API w8a8_status w8a8_pack_weights_size(int64_t groups, int64_t n, int64_t k, int kind, size_t* bytes);
+W8A8_API w8a8_status w8a8_pack_weights(const int8_t* w, int64_t groups, int64_t n, int64_t k, int kind,
+                              int8_t* packed, w8a8_stream stream);
+
+/* -------------------------------------------------------------------------
+ * Dense W8A8 GEMM with the scale outer product in the epilogue.
+ * [K100AI] sec. 2.1:  out[m][n] = ((float)acc[m][n] * s_a[m]) * s_b[n],
+ *                     acc[m][n] = sum_k a_q[m][k] * b[n][k]   (int32, exact)
+ *
+ * a_q       device, int8 [M][K] row-major
+ * s_a       device, fp32 [M]   (per-token activation scale)
+ * b_packed  device, int8, w8a8_pack_weights(b [N][K], groups=1, PLAIN)
+ * s_b       device, fp32 [N]   (per-output-channel weight scale)
+ * out       device, fp32 [M][N] row-major
+ * Limits: M >= 0, N % 128 == 0, K % 128 == 0, 1 <= K <= 2^17 (so the int32
+ * accumulator cannot overflow), N, K >= 128.
+ * w8a8_gemm_i32 returns the raw int32 accumulators instead (for checking).
+ * ------------------------------------------------------------------------- */
+W8A8_API w8a8_status w8a8_gemm(const int8_t* a_q, const float* s_a, const int8_t* b_packed, const float* s_b,
+                      int64_t M, int64_t N, int64_t K, float* out, w8a8_stream stream);
+W8A8_API w8a8_status w8a8_gemm_i32(const int8_t* a_q, const int8_t* b_packed, int64_t M, int64_t N,
+                          int64_t K, int32_t* acc, w8a8_stream stream);
+
+/* -------------------------------------------------------------------------
+ * The MoE expert layer.
+ *
+ *   1. x_q, s_x   = per-token quantisation of x          ([K100AI] sec. 2.1)
+ *   2. logits     = x . router_w^T + router_b, fp32 on the unquantised x
+ *                                                         ([DSV4] sec. 4.1)
+ *   3. top-k experts per token by logit (descending, ties to the lower
+ *      index); weights w = softmax over the k picked logits, which equals
+ *      softmax over all experts renormalised over the picked ones
+ *                                                         ([HUNYUAN] 1.3)
+ *   4. assignments a = t*k + j grouped into contiguous per-expert segments,
+ *      ascending token order inside a segment              ([HUNYUAN] 1.3)
+ *   5. gate-up: acc = x_q[t] . W_gu[e]^T (int32); g = ((float)acc_g * s_x[t])
+ *      * s_gu[e][i], u likewise with s_gu[e][I+i]; h = SiLU(g) * u with
+ *      SiLU(g) = g / (1 + exp(-g)), the exponential correctly rounded to
+ *      fp32; h requantised per assignment row like step 1  ([DSV4] sec. 2.3)
+ *   6. down: acc = h_q . W_d[e]^T (int32); o = w * (((float)acc * s_h) *
+ *      s_d[e][n])                                          ([K100AI] 2.1)
+ *   7. y[t] = sum over j = 0..k-1 (in order) of o[t*k+j]   ([HUNYUAN] 1.3)
+ *
+ * Layouts (all device memory, row-major, 16-byte aligned):
+ *   x [T][H] fp32 in, y [T][H] fp32 out (y may not alias x)
+ *   router_w [E][H] fp32, router_b [E] fp32 or NULL (zero bias)
+ *   w_gate_up: w8a8_pack_weights([E][2I][H], GATE_UP); s_gate_up [E][2I]
+ *   w_down:    w8a8_pack_weights([E][H][I], PLAIN);    s_down    [E][H]
+ * Limits: T >= 0 (0 is a no-op), T*k <= 2^24; H % 128 == 0, 128 <= H <= 16384;
+ * I % 128 == 0, 128 <= I <= 16384; 1 <= E <= 256; 1 <= top_k <= min(E, 8).
+ *
+ * workspace: device memory of at least w8a8_moe_workspace_query().total_bytes,
+ * 256-byte aligned.  After the call completes on the stream the workspace
+ * holds the intermediates at the offsets the query reports (for checking).
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    int64_t T, H, E, top_k, I;
+} w8a8_moe_shape;
+
+typedef struct {
+    const float* router_w;
+    const float* router_b;
+    const int8_t* w_gate_up;
+    const float* s_gate_up;
+    const int8_t* w_down;
+    const float* s_down;
+} w8a8_moe_weights;
+
+/* Byte offsets of the intermediates inside the workspace. */
+typedef struct {
+    size_t total_bytes;
+    size_t x_q;            /* int8  [T][H]          per-token codes              */
+    size_t x_scale;        /* fp32  [T]                                          */
+    size_t logits;         /* fp32  [T][E]          router logits                */
+    size_t topk_ids;       /* int32 [T][k]                                       */
+    size_t topk_w;         /* fp32  [T][k]                                       */
+    size_t expert_counts;  /* int32 [E]                                          */
+    size_t expert_offsets; /* int32 [E+1]           segment starts               */
+    size_t sorted_assign;  /* int32 [T*k]           a = t*k+j per sorted row     */
+    size_t h;              /* fp32  [T*k][I]        SiLU(g)*u, sorted row order  */
+    size_t h_q;            /* int8  [T*k][I]        requantised h, sorted order  */
+    size_t h_scale;        /* fp32  [T*k]           sorted order                 */
+    size_t o;              /* fp32  [T*k][H]        weighted expert outputs, row
+                                                    a = t*k+j                    */
+    size_t internal;       /* scratch of the routing kernels                     */
+} w8a8_moe_workspace_layout;
+
+W8A8_API w8a8_status w8a8_moe_workspace_query(const w8a8_moe_shape* shape, w8a8_moe_workspace_layout* layout);
+
+W8A8_API w8a8_status w8a8_moe_forward(const w8a8_moe_shape* shape, const w8a8_moe_weights* weights,
+                             const float* x, float* y, void* workspace, size_t workspace_bytes,
+                             w8a8_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8MOE_H */

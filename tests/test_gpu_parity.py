@@ -1,0 +1,328 @@
+"""GPU parity: every kernel of the HIP path against the CPU oracle, through the
+C ABI (via the thin Python binding), on seeded synthetic inputs.
+
+Bars: int8 codes, int32 accumulators, indices and permutations bit-exact;
+top-k ids bit-exact except flagged near ties (see _parity); fp32 outputs
+within max relative error 1e-3 (they are in fact expected to agree exactly or
+to a few ulp, since both sides apply the same fp32 operations in the same
+association).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _parity import (Y_TOL, near_tie_tokens, rel_metric, stable_sort_assign, sum_rel_metric, to_np,
+                     valid_topk)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def w8():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import w8a8_quantized_moe_amd as w8
+    return w8
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------ quantisation
+QUANT_SHAPES = [(1, 4, 4), (3, 130, 130), (37, 128, 128), (1000, 4096, 4096), (64, 7168, 7168),
+                (5, 8192, 8192), (7, 10000, 10000), (2, 1, 1), (9, 256, 300), (4, 2048, 2051)]
+
+
+@pytest.mark.parametrize("rows,cols,ld", QUANT_SHAPES)
+def test_quantize_rows_bitexact(w8, rows, cols, ld):
+    _say(f"quantize rows={rows} cols={cols} ld={ld}")
+    rng = np.random.default_rng(rows * 7 + cols)
+    full = rng.standard_normal((rows, ld)).astype(np.float32)
+    full[:, rng.integers(0, cols, size=max(1, cols // 100))] *= 30
+    if rows > 2:
+        full[1, :] = 0.0          # all-zero row
+        full[2, :cols] = 0.5      # all equal
+    x = torch.from_numpy(full).cuda()
+    q, s = w8.quantize_rows(x[:, :cols])
+    torch.cuda.synchronize()
+    qo, so = oracle.quantize_rows(full[:, :cols])
+    assert np.array_equal(to_np(s), so)
+    assert np.array_equal(to_np(q), qo)
+
+
+def test_quantize_hand_worked(w8):
+    import json
+    with open(os.path.join(os.path.dirname(__file__), "golden", "quant_pins.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        x = torch.tensor([c["x"]], dtype=torch.float32, device="cuda")
+        q, s = w8.quantize_rows(x)
+        assert to_np(s)[0] == np.float32(c["s"])
+        assert to_np(q)[0].tolist() == c["q"]
+
+
+# ------------------------------------------------------------------ dense GEMM
+GEMM_SHAPES = [(1, 128, 128), (5, 256, 384), (128, 128, 128), (300, 384, 256), (129, 128, 1024),
+               (513, 640, 2048)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_i32_exact(w8, M, N, K):
+    _say(f"gemm_i32 M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + N + K)
+    a = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+    b = rng.integers(-128, 128, size=(N, K)).astype(np.int8)
+    a[:, 0] = -128
+    b[:, 0] = -128
+    bp = w8.pack_weights(torch.from_numpy(b).cuda())
+    acc = w8.gemm_i32(torch.from_numpy(a).cuda(), bp, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(acc), oracle.gemm_i32(a, b))
+
+
+@pytest.mark.parametrize("M,N,K", [(77, 256, 512), (130, 128, 8192)])
+def test_gemm_f32_exact(w8, M, N, K):
+    _say(f"gemm_f32 M={M} N={N} K={K}")
+    rng = np.random.default_rng(M * N)
+    a = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    b = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    sa = rng.uniform(1e-3, 1e-1, M).astype(np.float32)
+    sb = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
+    bp = w8.pack_weights(torch.from_numpy(b).cuda())
+    out = w8.gemm(torch.from_numpy(a).cuda(), torch.from_numpy(sa).cuda(), bp,
+                  torch.from_numpy(sb).cuda(), N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(out), oracle.dense_w8a8(a, sa, b, sb))
+
+
+def test_dense_workload_sampled(w8):
+    """The dense W8A8 workload at full size (M=4096, K=8192, N=8192): per-token
+    quantisation exact on all rows; the GEMM output exact on sampled rows."""
+    _say("dense workload 4096x8192x8192")
+    inp = synth.dense_inputs(device="cuda")
+    M, K, N = inp["M"], inp["K"], inp["N"]
+    a_q, s_a = w8.quantize_rows(inp["a"])
+    bp = w8.pack_weights(inp["b"])
+    out = w8.gemm(a_q, s_a, bp, inp["s_b"], N, K)
+    torch.cuda.synchronize()
+    a_h = to_np(inp["a"])
+    qo, so = oracle.quantize_rows(a_h)
+    assert np.array_equal(to_np(a_q), qo) and np.array_equal(to_np(s_a), so)
+    rows = np.unique(np.concatenate([np.random.default_rng(0).choice(M, 40, replace=False),
+                                     [0, 127, 128, M - 1]]))
+    ref = oracle.dense_w8a8(qo[rows], so[rows], to_np(inp["b"]), to_np(inp["s_b"]))
+    assert np.array_equal(to_np(out)[rows], ref)
+
+
+# ------------------------------------------------------------------ MoE layer
+def _weights(w8, inp):
+    if "w_gu_f32" in inp:
+        wts, codes = w8.MoEWeights.from_fp32(inp["wr"], inp["b"], inp["w_gu_f32"], inp["w_d_f32"],
+                                             keep_codes=True)
+        return wts, codes
+    codes = dict(w_gu=inp["w_gu"], s_gu=inp["s_gu"], w_d=inp["w_d"], s_d=inp["s_d"])
+    return w8.MoEWeights.from_int8(inp["wr"], inp["b"], inp["w_gu"], inp["s_gu"], inp["w_d"],
+                                   inp["s_d"]), codes
+
+
+def _gpu_moe(w8, inp, wts):
+    T, H, E, k, I = inp["T"], inp["H"], inp["E"], inp["k"], inp["I"]
+    lay = w8.moe_workspace_layout(T, H, E, k, I)
+    ws = torch.empty((max(lay["total_bytes"], 256),), dtype=torch.uint8, device="cuda")
+    y = w8.moe_forward(inp["x"], wts, k, workspace=ws)
+    torch.cuda.synchronize()
+    g = {n: to_np(v) for n, v in w8.workspace_views(ws, T, H, E, k, I).items()}
+    g["y"] = to_np(y)
+    return g
+
+
+def _oracle_codes(inp, codes):
+    """The oracle's own int8 weights: for fp32 weights it quantises them itself
+    (and the test checks the GPU's offline quantisation against that)."""
+    if "w_gu_f32" in inp:
+        E, twoI, H = inp["w_gu_f32"].shape
+        I = twoI // 2
+        qg, sg = oracle.quantize_rows(to_np(inp["w_gu_f32"]).reshape(E * twoI, H))
+        qd, sd = oracle.quantize_rows(to_np(inp["w_d_f32"]).reshape(E * H, I))
+        ora = dict(w_gu=qg.reshape(E, twoI, H), s_gu=sg.reshape(E, twoI),
+                   w_d=qd.reshape(E, H, I), s_d=sd.reshape(E, H))
+        for n in ora:
+            assert np.array_equal(to_np(codes[n]), ora[n]), f"offline weight quantisation: {n}"
+        return ora
+    return {n: to_np(v) for n, v in codes.items()}
+
+
+def check_moe(w8, inp, tokens=None, report=None):
+    T, H, E, k, I = inp["T"], inp["H"], inp["E"], inp["k"], inp["I"]
+    _say(f"moe T={T} H={H} E={E} k={k} I={I} tokens={'all' if tokens is None else len(tokens)}")
+    wts, codes = _weights(w8, inp)
+    g = _gpu_moe(w8, inp, wts)
+    oc = _oracle_codes(inp, codes)
+    x = to_np(inp["x"])
+    b = to_np(inp["b"])
+    o = oracle.moe_forward(x, to_np(inp["wr"]), b, oc["w_gu"], oc["s_gu"], oc["w_d"], oc["s_d"], k,
+                           tokens=tokens, want_h=True)
+    tok = o["tokens"]
+
+    # 1. per-token quantisation: exact
+    assert np.array_equal(g["x_q"], o["x_q"]) and np.array_equal(g["x_scale"], o["s_x"])
+    # 2. router logits: fp32 on GPU vs fp64 oracle
+    cond = np.abs(x).astype(np.float64) @ np.abs(to_np(inp["wr"])).astype(np.float64).T
+    dl = np.abs(g["logits"].astype(np.float64) - o["logits"])
+    assert np.all(dl <= 1e-6 + 2.0 ** -24 * 8 * np.sqrt(H) * cond), float(dl.max())
+    # 3. top-k: GPU ids a valid top-k of the GPU's own logits; exact vs oracle except near ties
+    assert valid_topk(g["logits"], g["topk_ids"]).all()
+    flag = near_tie_tokens(o["logits"], g["logits"], k)
+    same = np.all(g["topk_ids"] == o["ids"], axis=1)
+    assert np.all(same | flag), f"top-k mismatch on unflagged tokens {np.where(~(same | flag))[0][:10]}"
+    diff_tokens = np.where(~same)[0]
+    # weights: a logit error d moves exp(l_j - l_0) by a relative 2d and the
+    # renormalising sum by at most d more; allow 4d plus fp32 rounding
+    delta = dl.max(axis=1)
+    w_rel = np.abs(g["topk_w"] - o["w"]) / np.abs(o["w"])
+    w_tol = 4.0 * delta[:, None] + 2e-6
+    assert np.all((w_rel <= w_tol)[same]), float((w_rel / w_tol)[same].max())
+    assert np.allclose(g["topk_w"].sum(1), 1.0, atol=1e-5)
+    # 4. permutation: a stable sort of the GPU's own ids; equal to the oracle's without ties
+    assert np.array_equal(g["sorted_assign"], stable_sort_assign(g["topk_ids"]))
+    cnt = np.bincount(g["topk_ids"].reshape(-1), minlength=E)
+    assert np.array_equal(g["expert_counts"], cnt)
+    assert g["expert_offsets"][0] == 0 and np.array_equal(np.diff(g["expert_offsets"]), cnt)
+    if diff_tokens.size == 0:
+        assert np.array_equal(g["sorted_assign"], o["sorted_assign"])
+        assert np.array_equal(g["expert_offsets"], o["offsets"])
+    # 5-6. per assignment (keyed by a = t*k + j) on the checked tokens
+    inv = np.empty(T * k, np.int64)
+    inv[g["sorted_assign"]] = np.arange(T * k)
+    a_rows = (tok[:, None] * k + np.arange(k)[None, :]).reshape(-1)
+    ok_rows = np.repeat(same[tok], k)
+    rows_g = inv[a_rows]
+    h_g = g["h"][rows_g]
+    hq_g = g["h_q"][rows_g]
+    sh_g = g["h_scale"][rows_g]
+    h_exact = np.all(h_g == o["h"], axis=1) & ok_rows
+    n_checked = int(ok_rows.sum())
+    # h is expected bit-exact (same fp32 operations, exp correctly rounded on both
+    # sides); a row may differ only through a double-rounding of exp (vanishingly rare)
+    assert h_exact.sum() >= n_checked - max(1, n_checked // 1000), \
+        f"h mismatch on {n_checked - int(h_exact.sum())} of {n_checked} rows"
+    assert np.array_equal(hq_g[h_exact], o["h_q"][h_exact])
+    assert np.array_equal(sh_g[h_exact], o["s_h"][h_exact])
+    rest = ok_rows & ~h_exact
+    if rest.any():
+        assert np.abs(hq_g[rest].astype(int) - o["h_q"][rest].astype(int)).max() <= 1
+    # o = w * v with v bit-exact on both sides when h_q is: its error is the routing
+    # weight's (bounded above from the logit error) plus the rounding of the product
+    o_g = g["o"][a_rows]
+    w_rel_a = w_rel[tok].reshape(-1)
+    o_err = np.abs(o_g.astype(np.float64) - o["o"])
+    o_tol = (w_rel_a[:, None] + 2.0 ** -22) * np.abs(o["o"]).astype(np.float64)
+    assert np.all((o_err <= o_tol)[h_exact]), float((o_err - o_tol)[h_exact].max())
+    el, mx = rel_metric(o_g[h_exact], o["o"][h_exact]) if h_exact.any() else (0.0, 0.0)
+    assert el <= Y_TOL and mx <= Y_TOL, (el, mx)
+    # 7. output
+    yt = same[tok]
+    terms = np.abs(o["o"]).reshape(len(tok), k, H).sum(axis=1)
+    sr, mx = sum_rel_metric(g["y"][tok][yt], o["y"][yt], terms[yt]) if yt.any() else (0.0, 0.0)
+    assert sr <= Y_TOL and mx <= Y_TOL, (sr, mx)
+    el, _ = rel_metric(g["y"][tok][yt], o["y"][yt]) if yt.any() else (0.0, 0.0)
+    if report is not None:
+        report.update(flagged=int(flag.sum()), differing_ids=int(diff_tokens.size),
+                      h_rows_inexact=int(n_checked - h_exact.sum()), y_sum_rel=sr, y_max=mx,
+                      y_elem_rel=el, y_exact=bool(np.array_equal(g["y"][tok][yt], o["y"][yt])))
+    return g, o
+
+
+def test_moe_tiny_full(w8):
+    inp = synth.moe_inputs("tiny", device="cuda")
+    rep = {}
+    check_moe(w8, inp, report=rep)
+    _say(f"tiny report {rep}")
+
+
+def test_moe_decode_full(w8):
+    inp = synth.moe_inputs("decode", device="cuda")
+    rep = {}
+    check_moe(w8, inp, report=rep)
+    _say(f"decode report {rep}")
+
+
+def test_moe_prefill_sampled(w8):
+    inp = synth.moe_inputs("prefill", device="cuda")
+    T = inp["T"]
+    tokens = np.unique(np.concatenate([np.random.default_rng(1).choice(T, 96, replace=False),
+                                       [0, 63, 64, T - 1]]))
+    rep = {}
+    g, o = check_moe(w8, inp, tokens=tokens, report=rep)
+    cnt = g["expert_counts"]
+    _say(f"prefill report {rep}; top-12 share {synth.zipf_top12_share(cnt):.3f}; "
+         f"experts<=3 tokens {(cnt <= 3).sum()}")
+
+
+def test_moe_large_sampled(w8):
+    inp = synth.moe_inputs("large", device="cuda")
+    T = inp["T"]
+    tokens = np.unique(np.concatenate([np.random.default_rng(2).choice(T, 24, replace=False),
+                                       [0, T - 1]]))
+    rep = {}
+    check_moe(w8, inp, tokens=tokens, report=rep)
+    _say(f"large report {rep}")
+
+
+EDGE = [
+    dict(T=1, H=128, E=8, k=2, I=128),
+    dict(T=100, H=256, E=16, k=4, I=256),
+    dict(T=70, H=128, E=1, k=1, I=128),
+    dict(T=33, H=128, E=8, k=8, I=128),
+    dict(T=40, H=128, E=256, k=8, I=128),
+    dict(T=300, H=256, E=64, k=2, I=128, bias="zipf"),
+    dict(T=129, H=384, E=5, k=3, I=384),
+    dict(T=65, H=512, E=3, k=1, I=640, weights="fp32"),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_moe_edge_cases(w8, case):
+    over = dict(n_outlier=2, outlier_scale=20.0, bf16_x=False, bias="zero", weights="int8")
+    over.update(case)
+    inp = synth.moe_inputs("edge", device="cuda", **over)
+    check_moe(w8, inp)
+
+
+def test_moe_zero_input_gives_zero(w8):
+    inp = synth.moe_inputs("edge0", device="cuda", T=50, H=256, E=8, k=2, I=256, n_outlier=0,
+                           outlier_scale=1.0, bf16_x=False, bias="zero", weights="int8")
+    inp["x"].zero_()
+    wts, _ = _weights(w8, inp)
+    g = _gpu_moe(w8, inp, wts)
+    assert np.all(g["x_scale"] == 0) and np.all(g["x_q"] == 0)
+    assert np.all(g["y"] == 0)
+
+
+def test_moe_empty_batch_is_noop(w8):
+    inp = synth.moe_inputs("edge1", device="cuda", T=4, H=128, E=4, k=2, I=128, n_outlier=0,
+                           outlier_scale=1.0, bf16_x=False, bias="zero", weights="int8")
+    wts, _ = _weights(w8, inp)
+    x = torch.empty((0, 128), dtype=torch.float32, device="cuda")
+    y = w8.moe_forward(x, wts, 2, workspace=torch.empty(256, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert y.shape == (0, 128)
+
+
+def test_moe_deterministic_and_token_independent(w8):
+    inp = synth.moe_inputs("decode", device="cuda")
+    wts, _ = _weights(w8, inp)
+    a = _gpu_moe(w8, inp, wts)
+    b = _gpu_moe(w8, inp, wts)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
+    # permuting tokens permutes the outputs exactly (same token count, same kernels)
+    perm = torch.randperm(inp["T"], generator=torch.Generator().manual_seed(3))
+    inp2 = dict(inp)
+    inp2["x"] = inp["x"][perm.cuda()].contiguous()
+    c = _gpu_moe(w8, inp2, wts)
+    assert np.array_equal(c["y"], a["y"][perm.numpy()])

@@ -1,0 +1,190 @@
+"""Python binding of the w8a8moe C ABI.  Argument marshalling only: every step
+of the computation runs in the HIP kernels of libw8a8moe.so.  PyTorch provides
+device memory and the current stream."""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import check, lib
+
+__all__ = [
+    "quantize_rows", "pack_weights", "gemm", "gemm_i32", "MoEWeights", "moe_workspace_layout",
+    "moe_forward", "workspace_views",
+]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t: torch.Tensor, dtype, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def quantize_rows(x: torch.Tensor, q: Optional[torch.Tensor] = None,
+                  scale: Optional[torch.Tensor] = None):
+    """Per-row int8 quantisation of a [rows, cols] fp32 matrix (any leading
+    dimension via stride(0)).  Returns (q int8 [rows, cols], scale fp32 [rows])."""
+    if not x.is_cuda or x.dtype != torch.float32 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D fp32 GPU tensor with unit column stride")
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    if scale is None:
+        scale = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    check(lib.w8a8_quantize_rows(_ptr(x), rows, cols, x.stride(0), _ptr(q), _ptr(scale), _stream()))
+    return q, scale
+
+
+def pack_weights(w: torch.Tensor, kind: int = _lib.PACK_PLAIN) -> torch.Tensor:
+    """Re-lay int8 weights [groups, n, k] (or [n, k]) into the GEMM tile order."""
+    if w.dim() == 2:
+        w = w.unsqueeze(0)
+    _dev(w, torch.int8, "w")
+    g, n, k = w.shape
+    nbytes = ctypes.c_size_t()
+    check(lib.w8a8_pack_weights_size(g, n, k, kind, ctypes.byref(nbytes)))
+    packed = torch.empty((nbytes.value,), dtype=torch.int8, device=w.device)
+    check(lib.w8a8_pack_weights(_ptr(w), g, n, k, kind, _ptr(packed), _stream()))
+    return packed
+
+
+def gemm(a_q, s_a, b_packed, s_b, N: int, K: int, out=None) -> torch.Tensor:
+    """Dense W8A8 GEMM: out = ((float)(a_q @ b^T) * s_a[:, None]) * s_b[None, :]."""
+    _dev(a_q, torch.int8, "a_q")
+    M = a_q.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a_q.device)
+    check(lib.w8a8_gemm(_ptr(a_q), _ptr(s_a), _ptr(b_packed), _ptr(s_b), M, N, K, _ptr(out),
+                        _stream()))
+    return out
+
+
+def gemm_i32(a_q, b_packed, N: int, K: int, out=None) -> torch.Tensor:
+    """Raw int32 accumulators a_q @ b^T (for checking)."""
+    _dev(a_q, torch.int8, "a_q")
+    M = a_q.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.int32, device=a_q.device)
+    check(lib.w8a8_gemm_i32(_ptr(a_q), _ptr(b_packed), M, N, K, _ptr(out), _stream()))
+    return out
+
+
+@dataclass
+class MoEWeights:
+    """Device-resident weights of one MoE layer in the library's layout."""
+    E: int
+    H: int
+    I: int
+    router_w: torch.Tensor            # [E, H] fp32
+    router_b: Optional[torch.Tensor]  # [E] fp32 or None
+    w_gate_up: torch.Tensor           # packed int8 (GATE_UP) of [E, 2I, H]
+    s_gate_up: torch.Tensor           # [E, 2I] fp32
+    w_down: torch.Tensor              # packed int8 (PLAIN) of [E, H, I]
+    s_down: torch.Tensor              # [E, H] fp32
+
+    @classmethod
+    def from_int8(cls, router_w, router_b, w_gu, s_gu, w_d, s_d):
+        """From int8 codes [E, 2I, H] / [E, H, I] with per-output-channel scales."""
+        E, twoI, H = w_gu.shape
+        return cls(E, H, twoI // 2, router_w.contiguous(),
+                   None if router_b is None else router_b.contiguous(),
+                   pack_weights(w_gu.contiguous(), _lib.PACK_GATE_UP), s_gu.contiguous(),
+                   pack_weights(w_d.contiguous(), _lib.PACK_PLAIN), s_d.contiguous())
+
+    @classmethod
+    def from_fp32(cls, router_w, router_b, w_gu_f32, w_d_f32, keep_codes=False):
+        """Quantise fp32 expert weights per output channel with the library's
+        row quantiser (offline step), then pack.  With keep_codes the unpacked
+        int8 codes and scales are returned as well."""
+        E, twoI, H = w_gu_f32.shape
+        I = twoI // 2
+        q_gu, s_gu = quantize_rows(w_gu_f32.reshape(E * twoI, H).contiguous())
+        q_d, s_d = quantize_rows(w_d_f32.reshape(E * H, I).contiguous())
+        q_gu = q_gu.view(E, twoI, H)
+        q_d = q_d.view(E, H, I)
+        w = cls.from_int8(router_w, router_b, q_gu, s_gu.view(E, twoI), q_d, s_d.view(E, H))
+        if keep_codes:
+            return w, dict(w_gu=q_gu, s_gu=s_gu.view(E, twoI), w_d=q_d, s_d=s_d.view(E, H))
+        return w
+
+    def _struct(self):
+        return _lib.MoeWeights(self.router_w.data_ptr(),
+                               None if self.router_b is None else self.router_b.data_ptr(),
+                               self.w_gate_up.data_ptr(), self.s_gate_up.data_ptr(),
+                               self.w_down.data_ptr(), self.s_down.data_ptr())
+
+
+def _shape(T, H, E, k, I):
+    return _lib.MoeShape(T, H, E, k, I)
+
+
+def moe_workspace_layout(T: int, H: int, E: int, top_k: int, I: int) -> dict:
+    lay = _lib.MoeLayout()
+    sh = _shape(T, H, E, top_k, I)
+    check(lib.w8a8_moe_workspace_query(ctypes.byref(sh), ctypes.byref(lay)))
+    return {f: int(getattr(lay, f)) for f in _lib.LAYOUT_FIELDS}
+
+
+def moe_forward(x: torch.Tensor, weights: MoEWeights, top_k: int, y: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = MoE expert layer(x), x [T, H] fp32 on the GPU.  ``workspace`` is a
+    uint8 GPU tensor of at least moe_workspace_layout(...)['total_bytes']
+    (allocated here if None); it holds the intermediates afterwards."""
+    _dev(x, torch.float32, "x")
+    T, H = x.shape
+    if H != weights.H:
+        raise ValueError("x width does not match the weights")
+    if y is None:
+        y = torch.empty_like(x)
+    lay = moe_workspace_layout(T, H, weights.E, top_k, weights.I)
+    if workspace is None:
+        workspace = torch.empty((max(lay["total_bytes"], 256),), dtype=torch.uint8, device=x.device)
+    sh = _shape(T, H, weights.E, top_k, weights.I)
+    wts = weights._struct()
+    check(lib.w8a8_moe_forward(ctypes.byref(sh), ctypes.byref(wts), _ptr(x), _ptr(y),
+                               _ptr(workspace), workspace.numel(), _stream()))
+    return y
+
+
+def workspace_views(workspace: torch.Tensor, T: int, H: int, E: int, top_k: int, I: int) -> dict:
+    """Tensors viewing the intermediates a moe_forward call left in ``workspace``."""
+    lay = moe_workspace_layout(T, H, E, top_k, I)
+    A = T * top_k
+
+    def view(name, dtype, shape):
+        n = 1
+        for s in shape:
+            n *= s
+        esz = torch.empty((), dtype=dtype).element_size()
+        off = lay[name]
+        return workspace[off:off + n * esz].view(dtype).view(*shape)
+
+    return dict(
+        x_q=view("x_q", torch.int8, (T, H)),
+        x_scale=view("x_scale", torch.float32, (T,)),
+        logits=view("logits", torch.float32, (T, E)),
+        topk_ids=view("topk_ids", torch.int32, (T, top_k)),
+        topk_w=view("topk_w", torch.float32, (T, top_k)),
+        expert_counts=view("expert_counts", torch.int32, (E,)),
+        expert_offsets=view("expert_offsets", torch.int32, (E + 1,)),
+        sorted_assign=view("sorted_assign", torch.int32, (A,)),
+        h=view("h", torch.float32, (A, I)),
+        h_q=view("h_q", torch.int8, (A, I)),
+        h_scale=view("h_scale", torch.float32, (A,)),
+        o=view("o", torch.float32, (A, H)),
+    )

@@ -1,0 +1,333 @@
+// C-ABI layer of libw8a8moe: argument checks, workspace layout and the launch
+// sequence of the MoE layer.  No allocation, no host synchronisation; every
+// kernel goes onto the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "internal.h"
+#include "w8a8moe.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+w8a8_status fail(w8a8_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+w8a8_status check_hip(hipError_t e, const char* what) {
+    if (e == hipSuccess) return W8A8_OK;
+    return fail(W8A8_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int64_t max_m_tiles(int64_t rows, int64_t groups, int64_t bm) {
+    // sum over groups of ceil(count/bm) <= (rows + groups*(bm-1)) / bm, and <= rows
+    const int64_t bound = (rows + groups * (bm - 1)) / bm;
+    return bound < rows ? bound : rows;
+}
+
+struct MoePlan {
+    w8a8_moe_workspace_layout lay;
+    size_t partial, rank, chunk_counts, chunk_base, mt_gu, mt_dn;
+    int splits, nchunks;
+};
+
+w8a8_status check_moe_shape(const w8a8_moe_shape* sh) {
+    if (!sh) return fail(W8A8_ERR_INVALID_ARGUMENT, "shape is NULL");
+    if (sh->T < 0 || sh->H < 0 || sh->E < 0 || sh->top_k < 0 || sh->I < 0)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "negative size in shape");
+    if (sh->H % 128 != 0 || sh->H < 128 || sh->H > 16384)
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "H=%lld: need H %% 128 == 0 and 128 <= H <= 16384",
+                    (long long)sh->H);
+    if (sh->I % 128 != 0 || sh->I < 128 || sh->I > 16384)
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "I=%lld: need I %% 128 == 0 and 128 <= I <= 16384",
+                    (long long)sh->I);
+    if (sh->E < 1 || sh->E > w8a8::MAX_EXPERTS)
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "E=%lld: need 1 <= E <= 256", (long long)sh->E);
+    if (sh->top_k < 1 || sh->top_k > sh->E || sh->top_k > w8a8::MAX_TOPK)
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "top_k=%lld: need 1 <= top_k <= min(E, 8)",
+                    (long long)sh->top_k);
+    if (sh->T * sh->top_k > (int64_t(1) << 24))
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "T*top_k=%lld exceeds 2^24",
+                    (long long)(sh->T * sh->top_k));
+    return W8A8_OK;
+}
+
+MoePlan plan_moe(const w8a8_moe_shape* sh) {
+    MoePlan p{};
+    const int64_t T = sh->T, H = sh->H, E = sh->E, k = sh->top_k, I = sh->I, A = T * k;
+    p.splits = T > 0 ? w8a8::router_splits((int)T, (int)E, (int)H) : 1;
+    p.nchunks = (int)((T + w8a8::ROUTE_CHUNK - 1) / w8a8::ROUTE_CHUNK);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    w8a8_moe_workspace_layout& L = p.lay;
+    L.x_q = take(T * H);
+    L.x_scale = take(T * 4);
+    L.logits = take(T * E * 4);
+    L.topk_ids = take(A * 4);
+    L.topk_w = take(A * 4);
+    L.expert_counts = take(E * 4);
+    L.expert_offsets = take((E + 1) * 4);
+    L.sorted_assign = take(A * 4);
+    L.h = take(A * I * 4);
+    L.h_q = take(A * I);
+    L.h_scale = take(A * 4);
+    L.o = take(A * H * 4);
+    L.internal = off;
+    p.partial = take((size_t)p.splits * T * E * 4);
+    p.rank = take(A * 4);
+    p.chunk_counts = take((size_t)E * p.nchunks * 4);
+    p.chunk_base = take((size_t)E * p.nchunks * 4);
+    p.mt_gu = take((E + 1) * 4);
+    p.mt_dn = take((E + 1) * 4);
+    L.total_bytes = off;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w8a8_status_string(int status) {
+    switch (status) {
+        case W8A8_OK: return "W8A8_OK";
+        case W8A8_ERR_INVALID_ARGUMENT: return "W8A8_ERR_INVALID_ARGUMENT";
+        case W8A8_ERR_UNSUPPORTED_SHAPE: return "W8A8_ERR_UNSUPPORTED_SHAPE";
+        case W8A8_ERR_WORKSPACE_TOO_SMALL: return "W8A8_ERR_WORKSPACE_TOO_SMALL";
+        case W8A8_ERR_MISALIGNED: return "W8A8_ERR_MISALIGNED";
+        case W8A8_ERR_HIP: return "W8A8_ERR_HIP";
+        default: return "W8A8_UNKNOWN_STATUS";
+    }
+}
+
+const char* w8a8_last_error(void) { return g_last_error.c_str(); }
+
+int w8a8_abi_version(void) { return 1; }
+
+w8a8_status w8a8_quantize_rows(const float* x, int64_t rows, int64_t cols, int64_t ld, int8_t* q,
+                               float* scale, w8a8_stream stream) {
+    if (rows < 0 || cols < 0 || ld < 0) return fail(W8A8_ERR_INVALID_ARGUMENT, "negative size");
+    if (cols < 1 || cols > (int64_t(1) << 24))
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "cols=%lld: need 1 <= cols <= 2^24", (long long)cols);
+    if (ld < cols) return fail(W8A8_ERR_INVALID_ARGUMENT, "ld=%lld < cols=%lld", (long long)ld,
+                               (long long)cols);
+    if (rows == 0) return W8A8_OK;
+    if (!x || !q || !scale) return fail(W8A8_ERR_INVALID_ARGUMENT, "NULL pointer");
+    if (!aligned(x, 4) || !aligned(scale, 4)) return fail(W8A8_ERR_MISALIGNED, "x/scale not 4-byte aligned");
+    return check_hip(w8a8::launch_quantize_rows(x, rows, cols, ld, q, scale, (hipStream_t)stream),
+                     "quantize_rows launch");
+}
+
+w8a8_status w8a8_pack_weights_size(int64_t groups, int64_t n, int64_t k, int kind, size_t* bytes) {
+    if (!bytes) return fail(W8A8_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    if (kind != W8A8_PACK_PLAIN && kind != W8A8_PACK_GATE_UP)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "unknown pack kind %d", kind);
+    if (groups < 1 || n < 1 || k < 1) return fail(W8A8_ERR_INVALID_ARGUMENT, "sizes must be >= 1");
+    if (k % 64 != 0) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "k=%lld: need k %% 64 == 0", (long long)k);
+    if (kind == W8A8_PACK_PLAIN && n % 16 != 0)
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "n=%lld: need n %% 16 == 0", (long long)n);
+    if (kind == W8A8_PACK_GATE_UP && (n % 32 != 0))
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "gate-up n=%lld: need n %% 32 == 0", (long long)n);
+    *bytes = (size_t)groups * (size_t)n * (size_t)k;
+    return W8A8_OK;
+}
+
+w8a8_status w8a8_pack_weights(const int8_t* w, int64_t groups, int64_t n, int64_t k, int kind,
+                              int8_t* packed, w8a8_stream stream) {
+    size_t bytes;
+    w8a8_status st = w8a8_pack_weights_size(groups, n, k, kind, &bytes);
+    if (st != W8A8_OK) return st;
+    if (!w || !packed) return fail(W8A8_ERR_INVALID_ARGUMENT, "NULL pointer");
+    if (!aligned(w, 16) || !aligned(packed, 16))
+        return fail(W8A8_ERR_MISALIGNED, "weights must be 16-byte aligned");
+    if (w == packed) return fail(W8A8_ERR_INVALID_ARGUMENT, "packing cannot be in place");
+    return check_hip(w8a8::launch_pack_weights(w, groups, n, k, kind, packed, (hipStream_t)stream),
+                     "pack_weights launch");
+}
+
+static w8a8_status dense_gemm(int epi, const int8_t* a_q, const float* s_a, const int8_t* b_packed,
+                              const float* s_b, int64_t M, int64_t N, int64_t K, float* out,
+                              int32_t* out_i32, w8a8_stream stream) {
+    if (M < 0 || N < 0 || K < 0) return fail(W8A8_ERR_INVALID_ARGUMENT, "negative size");
+    if (N % 128 != 0 || N < 128 || N > (int64_t(1) << 24))
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "N=%lld: need N %% 128 == 0, N >= 128", (long long)N);
+    if (K % 128 != 0 || K < 128 || K > (int64_t(1) << 17))
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "K=%lld: need K %% 128 == 0, 128 <= K <= 2^17",
+                    (long long)K);
+    if (M > (int64_t(1) << 24)) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "M too large");
+    if (M == 0) return W8A8_OK;
+    if (!a_q || !b_packed || (epi == w8a8::EPI_DENSE_F32 && (!s_a || !s_b || !out)) ||
+        (epi == w8a8::EPI_DENSE_I32 && !out_i32))
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "NULL pointer");
+    if (!aligned(a_q, 16) || !aligned(b_packed, 16))
+        return fail(W8A8_ERR_MISALIGNED, "operands must be 16-byte aligned");
+    w8a8::GemmParams p{};
+    p.A = a_q;
+    p.B = b_packed;
+    p.b_group_bytes = N * K;
+    p.M = M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.NT = (int)(N / w8a8::GEMM_BN);
+    p.G = 1;
+    p.s_a = s_a;
+    p.s_b = s_b;
+    p.out_f32 = out;
+    p.out_i32 = out_i32;
+    p.a_rows = M;
+    const int64_t mt = (M + w8a8::GEMM_BM - 1) / w8a8::GEMM_BM;
+    return check_hip(w8a8::launch_gemm(epi, p, mt, (hipStream_t)stream), "gemm launch");
+}
+
+w8a8_status w8a8_gemm(const int8_t* a_q, const float* s_a, const int8_t* b_packed, const float* s_b,
+                      int64_t M, int64_t N, int64_t K, float* out, w8a8_stream stream) {
+    return dense_gemm(w8a8::EPI_DENSE_F32, a_q, s_a, b_packed, s_b, M, N, K, out, nullptr, stream);
+}
+
+w8a8_status w8a8_gemm_i32(const int8_t* a_q, const int8_t* b_packed, int64_t M, int64_t N,
+                          int64_t K, int32_t* acc, w8a8_stream stream) {
+    return dense_gemm(w8a8::EPI_DENSE_I32, a_q, nullptr, b_packed, nullptr, M, N, K, nullptr, acc,
+                      stream);
+}
+
+w8a8_status w8a8_moe_workspace_query(const w8a8_moe_shape* shape, w8a8_moe_workspace_layout* layout) {
+    if (!layout) return fail(W8A8_ERR_INVALID_ARGUMENT, "layout is NULL");
+    w8a8_status st = check_moe_shape(shape);
+    if (st != W8A8_OK) return st;
+    *layout = plan_moe(shape).lay;
+    return W8A8_OK;
+}
+
+w8a8_status w8a8_moe_forward(const w8a8_moe_shape* shape, const w8a8_moe_weights* wts,
+                             const float* x, float* y, void* workspace, size_t workspace_bytes,
+                             w8a8_stream stream) {
+    w8a8_status st = check_moe_shape(shape);
+    if (st != W8A8_OK) return st;
+    if (shape->T == 0) return W8A8_OK;
+    if (!wts || !x || !y || !workspace || !wts->router_w || !wts->w_gate_up || !wts->s_gate_up ||
+        !wts->w_down || !wts->s_down)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "NULL pointer");
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(wts->router_w, 16) ||
+        !aligned(wts->w_gate_up, 16) || !aligned(wts->w_down, 16) || !aligned(wts->s_gate_up, 4) ||
+        !aligned(wts->s_down, 4) || (wts->router_b && !aligned(wts->router_b, 4)))
+        return fail(W8A8_ERR_MISALIGNED, "x, y, router_w and weights must be 16-byte aligned");
+    if (!aligned(workspace, 256)) return fail(W8A8_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+    if (x == y) return fail(W8A8_ERR_INVALID_ARGUMENT, "y must not alias x");
+    const MoePlan plan = plan_moe(shape);
+    if (workspace_bytes < plan.lay.total_bytes)
+        return fail(W8A8_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < required %zu", workspace_bytes,
+                    plan.lay.total_bytes);
+
+    const int T = (int)shape->T, H = (int)shape->H, E = (int)shape->E, k = (int)shape->top_k,
+              I = (int)shape->I;
+    const int64_t A = (int64_t)T * k;
+    hipStream_t s = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    const w8a8_moe_workspace_layout& L = plan.lay;
+    int8_t* x_q = (int8_t*)(ws + L.x_q);
+    float* x_scale = (float*)(ws + L.x_scale);
+    float* topk_w = (float*)(ws + L.topk_w);
+    int32_t* offsets = (int32_t*)(ws + L.expert_offsets);
+    int32_t* sorted = (int32_t*)(ws + L.sorted_assign);
+    float* h = (float*)(ws + L.h);
+    int8_t* h_q = (int8_t*)(ws + L.h_q);
+    float* h_scale = (float*)(ws + L.h_scale);
+    float* o = (float*)(ws + L.o);
+    int32_t* mt_gu = (int32_t*)(ws + plan.mt_gu);
+    int32_t* mt_dn = (int32_t*)(ws + plan.mt_dn);
+
+    // 1. per-token quantisation
+    st = check_hip(w8a8::launch_quantize_rows(x, T, H, H, x_q, x_scale, s), "quantize x");
+    if (st != W8A8_OK) return st;
+
+    // 2-4. router, top-k, permutation
+    w8a8::RouteInputs ri{x, wts->router_w, wts->router_b, T, H, E, k, plan.splits, w8a8::GEMM_BM,
+                         w8a8::GEMM_BM};
+    w8a8::RouteBuffers rb{};
+    rb.partial = (float*)(ws + plan.partial);
+    rb.logits = (float*)(ws + L.logits);
+    rb.topk_ids = (int32_t*)(ws + L.topk_ids);
+    rb.topk_w = topk_w;
+    rb.chunk_counts = (int32_t*)(ws + plan.chunk_counts);
+    rb.chunk_base = (int32_t*)(ws + plan.chunk_base);
+    rb.rank = (int32_t*)(ws + plan.rank);
+    rb.expert_counts = (int32_t*)(ws + L.expert_counts);
+    rb.expert_offsets = offsets;
+    rb.mt_prefix_gu = mt_gu;
+    rb.mt_prefix_dn = mt_dn;
+    rb.sorted_assign = sorted;
+    st = check_hip(w8a8::launch_route(ri, rb, s), "route");
+    if (st != W8A8_OK) return st;
+
+    // 5. grouped gate-up GEMM, epilogue dequant + SiLU*up -> h (fp32)
+    w8a8::GemmParams gu{};
+    gu.A = x_q;
+    gu.B = wts->w_gate_up;
+    gu.b_group_bytes = (int64_t)2 * I * H;
+    gu.M = A;
+    gu.N = 2 * I;
+    gu.K = H;
+    gu.NT = 2 * I / w8a8::GEMM_BN;
+    gu.seg_offsets = offsets;
+    gu.mt_prefix = mt_gu;
+    gu.G = E;
+    gu.sorted_assign = sorted;
+    gu.topk = k;
+    gu.s_a = x_scale;
+    gu.s_b = wts->s_gate_up;
+    gu.out_f32 = h;
+    gu.I = I;
+    gu.a_rows = T;
+    st = check_hip(w8a8::launch_gemm(w8a8::EPI_GATE_UP, gu, max_m_tiles(A, E, w8a8::GEMM_BM), s),
+                   "gate-up gemm");
+    if (st != W8A8_OK) return st;
+
+    // requantise h per assignment row
+    st = check_hip(w8a8::launch_quantize_rows(h, A, I, I, h_q, h_scale, s), "requantize h");
+    if (st != W8A8_OK) return st;
+
+    // 6. grouped down GEMM, epilogue dequant * routing weight -> o[t*k+j]
+    w8a8::GemmParams dn{};
+    dn.A = h_q;
+    dn.B = wts->w_down;
+    dn.b_group_bytes = (int64_t)H * I;
+    dn.M = A;
+    dn.N = H;
+    dn.K = I;
+    dn.NT = H / w8a8::GEMM_BN;
+    dn.seg_offsets = offsets;
+    dn.mt_prefix = mt_dn;
+    dn.G = E;
+    dn.sorted_assign = sorted;
+    dn.topk = k;
+    dn.s_a = h_scale;
+    dn.s_b = wts->s_down;
+    dn.route_w = topk_w;
+    dn.out_f32 = o;
+    dn.a_rows = A;
+    st = check_hip(w8a8::launch_gemm(w8a8::EPI_DOWN, dn, max_m_tiles(A, E, w8a8::GEMM_BM), s),
+                   "down gemm");
+    if (st != W8A8_OK) return st;
+
+    // 7. combine
+    return check_hip(w8a8::launch_combine(o, T, k, H, y, s), "combine");
+}
+
+}  // extern "C"

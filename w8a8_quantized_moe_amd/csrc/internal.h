@@ -1,0 +1,91 @@
+// Internal declarations shared by the HIP sources of libw8a8moe (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Tile shape of the int8 MFMA GEMM (rows x output channels x reduction).
+constexpr int GEMM_BM = 128;
+constexpr int GEMM_BN = 128;
+constexpr int GEMM_BK = 128;
+
+// Routing works on chunks of 64 tokens (one bit per token in a 64-bit mask).
+constexpr int ROUTE_CHUNK = 64;
+constexpr int MAX_EXPERTS = 256;
+constexpr int MAX_TOPK = 8;
+
+enum Epilogue : int {
+    EPI_DENSE_F32 = 0,  // out[m][n] = ((float)acc * s_a[m]) * s_b[n]
+    EPI_DENSE_I32 = 1,  // out[m][n] = acc
+    EPI_GATE_UP = 2,    // h = SiLU(g) * u from interleaved gate/up columns
+    EPI_DOWN = 3,       // o[slot][n] = w[slot] * (((float)acc * s_h[r]) * s_d[e][n])
+};
+
+struct GemmParams {
+    const int8_t* A;          // activations, [rows][K] int8 row-major
+    const int8_t* B;          // packed weights of group 0
+    int64_t b_group_bytes;    // bytes per group of packed weights (N*K)
+    int64_t M;                // dense: rows; grouped: total assignments
+    int N, K;
+    int NT;                   // N / GEMM_BN
+    const int32_t* seg_offsets;  // grouped: [G+1] segment starts, else nullptr
+    const int32_t* mt_prefix;    // grouped: [G+1] prefix of m-tiles per group
+    int G;
+    const int32_t* sorted_assign;  // grouped: assignment a = t*k+j of each sorted row
+    int topk;
+    const float* s_a;    // dense: [M]; gate-up: s_x[T] by token; down: s_h[A] by sorted row
+    const float* s_b;    // [G][N] per-output-channel scales (gate-up: [G][2I] unpermuted)
+    const float* route_w;  // down: routing weight per assignment a
+    float* out_f32;
+    int32_t* out_i32;
+    int I;               // gate-up: intermediate size (N = 2I)
+    int64_t a_rows;      // rows of the A operand (gate-up: T); indices are clamped to it
+};
+
+// ---- launchers (each returns the launch status) ----
+hipError_t launch_quantize_rows(const float* x, int64_t rows, int64_t cols, int64_t ld, int8_t* q,
+                                float* scale, hipStream_t s);
+
+hipError_t launch_pack_weights(const int8_t* w, int64_t groups, int64_t n, int64_t k, int kind,
+                               int8_t* packed, hipStream_t s);
+
+hipError_t launch_gemm(int epi, const GemmParams& p, int64_t m_tiles, hipStream_t s);
+
+// Number of partial sums the router GEMM splits H into (so a small token
+// count still yields enough workgroups); the workspace holds S*T*E floats.
+int router_splits(int T, int E, int H);
+
+struct RouteInputs {
+    const float* x;         // [T][H]
+    const float* router_w;  // [E][H]
+    const float* router_b;  // [E] or nullptr
+    int T, H, E, k;
+    int splits;             // router_splits(T, E, H)
+    int bm_gu, bm_dn;       // m-tile heights of the two grouped GEMMs
+};
+
+struct RouteBuffers {
+    float* partial;           // [S][T][E]
+    float* logits;            // [T][E]
+    int32_t* topk_ids;        // [T][k]
+    float* topk_w;            // [T][k]
+    int32_t* chunk_counts;    // [E][nchunks]
+    int32_t* chunk_base;      // [E][nchunks]
+    int32_t* rank;            // [T*k] rank of an assignment inside its chunk and expert
+    int32_t* expert_counts;   // [E]
+    int32_t* expert_offsets;  // [E+1]
+    int32_t* mt_prefix_gu;    // [E+1]
+    int32_t* mt_prefix_dn;    // [E+1]
+    int32_t* sorted_assign;   // [T*k]
+};
+
+hipError_t launch_route(const RouteInputs& in, const RouteBuffers& b, hipStream_t s);
+
+hipError_t launch_combine(const float* o, int T, int k, int H, float* y, hipStream_t s);
+
+}  // namespace w8a8
