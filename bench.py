@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark of the W8A8 MoE expert layer on one MI355X.
+
+One step = one whole pass of the layer (per-token quantisation, fp32 router +
+top-k + permutation, grouped gate-up GEMM with the SwiGLU epilogue,
+requantisation, grouped down GEMM with the weighted scatter, combine) over one
+batch of seeded synthetic tokens already resident in HBM.  W untimed warm-up
+steps, then exactly K timed steps between two device synchronisations.
+
+Default workload: the large fine-grained layer (T=16384 tokens, H=7168,
+E=256 experts, top-8, I=2048, ~11.3 GB of int8 expert weights), the largest
+MoE configuration of the study, which fits one GPU.
+
+Prints one JSON line: tokens/s of the whole job, the per-stage times (HIP
+events recorded on the layer's stream at every stage boundary of every timed
+step), the roofline of the dominant kernel, whole-layer INT8 TOPS and
+algorithmic HBM GB/s, and the CPU oracle timed on a bounded token sample.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks (dense)
+PEAK_INT8_OPS = 5.0e15      # int8 MFMA, ops/s
+PEAK_FP32_MFMA = 157.3e12   # fp32 matrix, flop/s
+PEAK_HBM = 8.0e12           # bytes/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles created through the HIP runtime (plumbing for timing)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(ev))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            arr[i] = ev
+        return arr
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(ms.value)
+
+    def destroy(self, arr):
+        for ev in arr:
+            self.hip.hipEventDestroy(ev)
+
+
+def stage_work(T, H, E, k, I):
+    """Algorithmic work per launch of each stage: (bound, amount, unit, peak)."""
+    A = T * k
+    return {
+        "quant": ("hbm", 4 * T * H + T * H + 4 * T, "GB/s", PEAK_HBM),
+        "route": ("mfma", 2 * T * H * E, "TFLOP/s", PEAK_FP32_MFMA),
+        "gate_up": ("mfma", 2 * A * H * 2 * I, "TOP/s", PEAK_INT8_OPS),
+        "requant": ("hbm", 4 * A * I + A * I + 4 * A, "GB/s", PEAK_HBM),
+        "down": ("mfma", 2 * A * I * H, "TOP/s", PEAK_INT8_OPS),
+        "combine": ("hbm", 4 * A * H + 4 * T * H, "GB/s", PEAK_HBM),
+    }
+
+
+def cpu_baseline(inp, target_s):
+    """The CPU oracle, as it stands, on the first n tokens of the same batch
+    (whole layer for those tokens), n sized for about target_s seconds."""
+    import numpy as np
+
+    import oracle
+    x = inp["x"].cpu().numpy()
+    wr = inp["wr"].cpu().numpy()
+    b = inp["b"].cpu().numpy()
+    w_gu = inp["w_gu"].cpu().numpy()
+    s_gu = inp["s_gu"].cpu().numpy()
+    w_d = inp["w_d"].cpu().numpy()
+    s_d = inp["s_d"].cpu().numpy()
+    k, T = inp["k"], inp["T"]
+
+    def run(n):
+        t0 = time.perf_counter()
+        oracle.moe_forward(x, wr, b, w_gu, s_gu, w_d, s_d, k, route_tokens=np.arange(n))
+        return time.perf_counter() - t0
+
+    probe_n = min(8, T)
+    t_probe = run(probe_n)
+    n = int(max(probe_n, min(T, target_s / max(t_probe / probe_n, 1e-9))))
+    t = run(n) if n != probe_n else t_probe
+    return dict(value=n / t, unit="tokens/s", cores=oracle.max_threads(), kind="oracle",
+                sample=f"first {n} of {T} tokens of the same batch, whole layer for them "
+                       f"(quant, fp64 router, softmax/top-k, permute, expert FFN, combine); "
+                       f"{t:.1f} s", seconds=t, tokens=n)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="large", choices=["large", "prefill", "decode", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU only: the layer runs on a single "
+                          "MI355X (no collectives); run with --gpus 1"}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import w8a8_quantized_moe_amd as w8
+
+    torch.cuda.set_device(0)
+    log(f"[bench] generating workload '{args.workload}' on the GPU")
+    inp = synth.moe_inputs(args.workload, device="cuda")
+    T, H, E, k, I = inp["T"], inp["H"], inp["E"], inp["k"], inp["I"]
+    A = T * k
+    if "w_gu_f32" in inp:
+        wts, codes = w8.MoEWeights.from_fp32(inp["wr"], inp["b"], inp["w_gu_f32"], inp["w_d_f32"],
+                                             keep_codes=True)
+        inp.update(codes)
+    else:
+        wts = w8.MoEWeights.from_int8(inp["wr"], inp["b"], inp["w_gu"], inp["s_gu"], inp["w_d"],
+                                      inp["s_d"])
+    lay = w8.moe_workspace_layout(T, H, E, k, I)
+    ws = torch.empty((lay["total_bytes"],), dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(inp["x"])
+    torch.cuda.synchronize()
+
+    stages = w8._lib.MOE_STAGES
+    hip = HipEvents()
+    events = [hip.create(len(stages) + 1) for _ in range(args.steps)]
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        w8.moe_forward(inp["x"], wts, k, y=y, workspace=ws)
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        w8.moe_forward(inp["x"], wts, k, y=y, workspace=ws, events=events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    stage_ms = {s: 0.0 for s in stages}
+    event_step_ms = 0.0
+    for ev in events:
+        for j, s in enumerate(stages):
+            stage_ms[s] += hip.elapsed_ms(ev[j], ev[j + 1]) / args.steps
+        event_step_ms += hip.elapsed_ms(ev[0], ev[len(stages)]) / args.steps
+    for ev in events:
+        hip.destroy(ev)
+
+    counts = w8.workspace_views(ws, T, H, E, k, I)["expert_counts"].cpu()
+    touched = int((counts > 0).sum())
+    work = stage_work(T, H, E, k, I)
+    dom = max(stages, key=lambda s: stage_ms[s])
+    bound, amount, unit, peak = work[dom]
+    scale = 1e9 if unit == "GB/s" else 1e12
+    achieved = amount / (stage_ms[dom] * 1e-3)
+    roofline = dict(kernel=dom, bound=bound, achieved=round(achieved / scale, 2),
+                    peak=peak / scale, unit=unit, frac=round(achieved / peak, 4), traffic=None,
+                    work_per_launch=amount)
+
+    step_s = ms_per_step * 1e-3
+    int8_ops = 6 * A * H * I
+    alg_bytes = 8 * T * H + 4 * H * E + 4 * E + touched * (3 * H * I + 4 * (2 * I + H))
+
+    out = {
+        "metric": "MoE-layer tokens/s; INT8 TOPS & HBM GB/s as % of MI355X roofline",
+        "value": round(T / step_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded; random int8 expert weights of the layer's shape)",
+        "config": {"workload": f"{args.workload} MoE layer T={T} H={H} E={E} top-{k} I={I}",
+                   "T": T, "H": H, "E": E, "top_k": k, "I": I, "parallelism": "none (1 GPU)"},
+        "int8_tops": round(int8_ops / step_s / 1e12, 2),
+        "int8_frac_of_peak": round(int8_ops / step_s / PEAK_INT8_OPS, 4),
+        "alg_hbm_gbps": round(alg_bytes / step_s / 1e9, 1),
+        "hbm_frac_of_peak": round(alg_bytes / step_s / PEAK_HBM, 4),
+        "experts_touched": touched,
+        "event_ms_per_step": round(event_step_ms, 4),
+        "stage_ms": {s: round(v, 4) for s, v in stage_ms.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a token sample")
+        cb = cpu_baseline(inp, args.cpu_seconds)
+        out["cpu_baseline"] = {kk: (round(v, 3) if isinstance(v, float) else v)
+                               for kk, v in cb.items() if kk in ("value", "unit", "cores", "kind",
+                                                                 "sample")}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -199,6 +199,22 @@ W8A8_API w8a8_status w8a8_moe_forward(const w8a8_moe_shape* shape, const w8a8_mo
                              const float* x, float* y, void* workspace, size_t workspace_bytes,
                              w8a8_stream stream);
 
+/* -------------------------------------------------------------------------
+ * The same layer with stage-boundary timing events, for measurement.
+ * events[i] (a hipEvent_t created by the caller, passed as void*) is recorded
+ * on the stream right before stage i is enqueued, and events[W8A8_MOE_STAGES]
+ * after the last one.  Stages: 0 per-token quantisation, 1 router + top-k +
+ * permutation, 2 grouped gate-up GEMM (SwiGLU epilogue), 3 requantisation of
+ * h, 4 grouped down GEMM (weighted scatter epilogue), 5 combine.
+ * events == NULL behaves exactly like w8a8_moe_forward.
+ * ------------------------------------------------------------------------- */
+enum { W8A8_MOE_STAGES = 6 };
+
+W8A8_API w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape,
+                                             const w8a8_moe_weights* weights, const float* x,
+                                             float* y, void* workspace, size_t workspace_bytes,
+                                             void* const* events, w8a8_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

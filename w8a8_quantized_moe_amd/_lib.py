@@ -63,14 +63,18 @@ SIGNATURES = {
     "w8a8_moe_workspace_query": (ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeLayout)]),
     "w8a8_moe_forward": (ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeWeights), _P, _P,
                                         _P, ctypes.c_size_t, _P]),
+    "w8a8_moe_forward_events": (ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeWeights),
+                                               _P, _P, _P, ctypes.c_size_t, _P, _P]),
 }
+
+MOE_STAGES = ["quant", "route", "gate_up", "requant", "down", "combine"]
 
 
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"libw8a8moe.so not found at {LIB_PATH}; build it with "
-            "`python -m w8a8_quantized_moe_amd.build` (there is no fallback path)")
+            "`python w8a8_quantized_moe_amd/build.py` (there is no fallback path)")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

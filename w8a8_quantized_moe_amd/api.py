@@ -141,10 +141,12 @@ def moe_workspace_layout(T: int, H: int, E: int, top_k: int, I: int) -> dict:
 
 
 def moe_forward(x: torch.Tensor, weights: MoEWeights, top_k: int, y: Optional[torch.Tensor] = None,
-                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                workspace: Optional[torch.Tensor] = None, events=None) -> torch.Tensor:
     """y = MoE expert layer(x), x [T, H] fp32 on the GPU.  ``workspace`` is a
     uint8 GPU tensor of at least moe_workspace_layout(...)['total_bytes']
-    (allocated here if None); it holds the intermediates afterwards."""
+    (allocated here if None); it holds the intermediates afterwards.
+    ``events``: optional ctypes array of len(MOE_STAGES)+1 hipEvent_t handles
+    recorded at the stage boundaries (see w8a8_moe_forward_events)."""
     _dev(x, torch.float32, "x")
     T, H = x.shape
     if H != weights.H:
@@ -156,8 +158,12 @@ def moe_forward(x: torch.Tensor, weights: MoEWeights, top_k: int, y: Optional[to
         workspace = torch.empty((max(lay["total_bytes"], 256),), dtype=torch.uint8, device=x.device)
     sh = _shape(T, H, weights.E, top_k, weights.I)
     wts = weights._struct()
-    check(lib.w8a8_moe_forward(ctypes.byref(sh), ctypes.byref(wts), _ptr(x), _ptr(y),
-                               _ptr(workspace), workspace.numel(), _stream()))
+    if events is None:
+        check(lib.w8a8_moe_forward(ctypes.byref(sh), ctypes.byref(wts), _ptr(x), _ptr(y),
+                                   _ptr(workspace), workspace.numel(), _stream()))
+    else:
+        check(lib.w8a8_moe_forward_events(ctypes.byref(sh), ctypes.byref(wts), _ptr(x), _ptr(y),
+                                          _ptr(workspace), workspace.numel(), events, _stream()))
     return y
 
 

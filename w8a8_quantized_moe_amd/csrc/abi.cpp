@@ -218,6 +218,13 @@ w8a8_status w8a8_moe_workspace_query(const w8a8_moe_shape* shape, w8a8_moe_works
 w8a8_status w8a8_moe_forward(const w8a8_moe_shape* shape, const w8a8_moe_weights* wts,
                              const float* x, float* y, void* workspace, size_t workspace_bytes,
                              w8a8_stream stream) {
+    return w8a8_moe_forward_events(shape, wts, x, y, workspace, workspace_bytes, nullptr, stream);
+}
+
+w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_weights* wts,
+                                    const float* x, float* y, void* workspace,
+                                    size_t workspace_bytes, void* const* events,
+                                    w8a8_stream stream) {
     w8a8_status st = check_moe_shape(shape);
     if (st != W8A8_OK) return st;
     if (shape->T == 0) return W8A8_OK;
@@ -253,7 +260,13 @@ w8a8_status w8a8_moe_forward(const w8a8_moe_shape* shape, const w8a8_moe_weights
     int32_t* mt_gu = (int32_t*)(ws + plan.mt_gu);
     int32_t* mt_dn = (int32_t*)(ws + plan.mt_dn);
 
+    auto mark = [&](int i) -> w8a8_status {
+        if (!events) return W8A8_OK;
+        return check_hip(hipEventRecord((hipEvent_t)events[i], s), "hipEventRecord");
+    };
+
     // 1. per-token quantisation
+    if ((st = mark(0)) != W8A8_OK) return st;
     st = check_hip(w8a8::launch_quantize_rows(x, T, H, H, x_q, x_scale, s), "quantize x");
     if (st != W8A8_OK) return st;
 
@@ -273,6 +286,7 @@ w8a8_status w8a8_moe_forward(const w8a8_moe_shape* shape, const w8a8_moe_weights
     rb.mt_prefix_gu = mt_gu;
     rb.mt_prefix_dn = mt_dn;
     rb.sorted_assign = sorted;
+    if ((st = mark(1)) != W8A8_OK) return st;
     st = check_hip(w8a8::launch_route(ri, rb, s), "route");
     if (st != W8A8_OK) return st;
 
@@ -295,11 +309,13 @@ w8a8_status w8a8_moe_forward(const w8a8_moe_shape* shape, const w8a8_moe_weights
     gu.out_f32 = h;
     gu.I = I;
     gu.a_rows = T;
+    if ((st = mark(2)) != W8A8_OK) return st;
     st = check_hip(w8a8::launch_gemm(w8a8::EPI_GATE_UP, gu, max_m_tiles(A, E, w8a8::GEMM_BM), s),
                    "gate-up gemm");
     if (st != W8A8_OK) return st;
 
     // requantise h per assignment row
+    if ((st = mark(3)) != W8A8_OK) return st;
     st = check_hip(w8a8::launch_quantize_rows(h, A, I, I, h_q, h_scale, s), "requantize h");
     if (st != W8A8_OK) return st;
 
@@ -322,12 +338,16 @@ w8a8_status w8a8_moe_forward(const w8a8_moe_shape* shape, const w8a8_moe_weights
     dn.route_w = topk_w;
     dn.out_f32 = o;
     dn.a_rows = A;
+    if ((st = mark(4)) != W8A8_OK) return st;
     st = check_hip(w8a8::launch_gemm(w8a8::EPI_DOWN, dn, max_m_tiles(A, E, w8a8::GEMM_BM), s),
                    "down gemm");
     if (st != W8A8_OK) return st;
 
     // 7. combine
-    return check_hip(w8a8::launch_combine(o, T, k, H, y, s), "combine");
+    if ((st = mark(5)) != W8A8_OK) return st;
+    st = check_hip(w8a8::launch_combine(o, T, k, H, y, s), "combine");
+    if (st != W8A8_OK) return st;
+    return mark(6);
 }
 
 }  // extern "C"
