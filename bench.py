@@ -113,12 +113,71 @@ def cpu_baseline(inp, target_s):
                        f"{t:.1f} s", seconds=t, tokens=n)
 
 
+def bench_dense(args, torch, synth, w8):
+    """The dense W8A8 GEMM workload (M=4096, K=8192, N=8192): one step = the
+    per-token quantisation of A plus the int8 GEMM with the scale epilogue."""
+    log("[bench] generating the dense GEMM workload on the GPU")
+    inp = synth.dense_inputs(device="cuda")
+    M, K, N = inp["M"], inp["K"], inp["N"]
+    bp = w8.pack_weights(inp["b"])
+    a_q = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    s_a = torch.empty((M,), dtype=torch.float32, device="cuda")
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    hip = HipEvents()
+    events = [hip.create(3) for _ in range(args.steps)]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    hip.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def step(ev=None):
+        if ev is not None:
+            hip.hip.hipEventRecord(ev[0], stream)
+        w8.quantize_rows(inp["a"], a_q, s_a)
+        if ev is not None:
+            hip.hip.hipEventRecord(ev[1], stream)
+        w8.gemm(a_q, s_a, bp, inp["s_b"], N, K, out=out)
+        if ev is not None:
+            hip.hip.hipEventRecord(ev[2], stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    q_ms = sum(hip.elapsed_ms(e[0], e[1]) for e in events) / args.steps
+    g_ms = sum(hip.elapsed_ms(e[1], e[2]) for e in events) / args.steps
+    ops = 2 * M * N * K
+    q_bytes = 4 * M * K + M * K + 4 * M
+    out_line = {
+        "metric": "dense W8A8 GEMM INT8 TOPS (per-token quant + GEMM with scale epilogue)",
+        "value": round(ops / (ms * 1e-3) / 1e12, 2), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic (seeded)",
+        "config": {"workload": f"dense W8A8 GEMM M={M} K={K} N={N}", "M": M, "K": K, "N": N},
+        "stage_ms": {"quant": round(q_ms, 4), "gemm": round(g_ms, 4)},
+        "roofline": dict(kernel="gemm", bound="mfma", achieved=round(ops / (g_ms * 1e-3) / 1e12, 2),
+                         peak=PEAK_INT8_OPS / 1e12, unit="TOP/s",
+                         frac=round(ops / (g_ms * 1e-3) / PEAK_INT8_OPS, 4), traffic=None,
+                         work_per_launch=ops),
+        "quant_roofline": dict(bound="hbm", achieved=round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+                               peak=PEAK_HBM / 1e9, unit="GB/s",
+                               frac=round(q_bytes / (q_ms * 1e-3) / PEAK_HBM, 4)),
+    }
+    for e in events:
+        hip.destroy(e)
+    print(json.dumps(out_line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="large", choices=["large", "prefill", "decode", "tiny"])
+    ap.add_argument("--workload", default="large",
+                    choices=["large", "prefill", "decode", "tiny", "dense"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
@@ -135,6 +194,8 @@ def main():
     import w8a8_quantized_moe_amd as w8
 
     torch.cuda.set_device(0)
+    if args.workload == "dense":
+        return bench_dense(args, torch, synth, w8)
     log(f"[bench] generating workload '{args.workload}' on the GPU")
     inp = synth.moe_inputs(args.workload, device="cuda")
     T, H, E, k, I = inp["T"], inp["H"], inp["E"], inp["k"], inp["I"]

@@ -185,7 +185,6 @@ static w8a8_status dense_gemm(int epi, const int8_t* a_q, const float* s_a, cons
     p.M = M;
     p.N = (int)N;
     p.K = (int)K;
-    p.NT = (int)(N / w8a8::GEMM_BN);
     p.G = 1;
     p.s_a = s_a;
     p.s_b = s_b;
@@ -298,7 +297,6 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     gu.M = A;
     gu.N = 2 * I;
     gu.K = H;
-    gu.NT = 2 * I / w8a8::GEMM_BN;
     gu.seg_offsets = offsets;
     gu.mt_prefix = mt_gu;
     gu.G = E;
@@ -327,7 +325,6 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     dn.M = A;
     dn.N = H;
     dn.K = I;
-    dn.NT = H / w8a8::GEMM_BN;
     dn.seg_offsets = offsets;
     dn.mt_prefix = mt_dn;
     dn.G = E;

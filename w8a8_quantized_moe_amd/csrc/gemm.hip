@@ -11,30 +11,37 @@
 // '950' unified FP8 dataflow", sec. 2.3: low-precision inputs, a wide
 // accumulator, the output requantised for the next GEMM.
 //
-// Kernel shape: 256 threads (4 wave64 in a 2x2 grid), a 128x128 output tile,
-// K consumed 128 bytes per stage, two LDS stages (64 KiB) so the next stage's
-// global loads overlap the current stage's MFMAs.  Each wave owns a 64x64
-// sub-tile = 4x4 v_mfma_i32_16x16x64_i8 blocks (64 accumulator VGPRs).
-// LDS holds both operands in MFMA fragment order: each 16-row x 64-byte block
-// is 1 KiB with lane l's 16 bytes at l*16, so every fragment read is one
-// conflict-free ds_read_b128.  The weight operand arrives pre-packed in that
-// order (pack.hip), so its global->LDS copy is a straight 16-byte-per-lane copy.
+// Kernel shape (BM x BN output tile, WM x WN waves of 64 lanes):
+//  * every wave owns a (BM/WM) x (BN/WN) sub-tile of v_mfma_i32_16x16x64_i8
+//    blocks;
+//  * K advances 64 bytes per pipeline stage; NS stages live in LDS at once;
+//  * operands move global -> LDS with global_load_lds_dwordx4 (no VGPR
+//    staging): one wave instruction moves one 16-row x 64-byte MFMA fragment
+//    (1 KiB), lane l writing its 16 bytes at l*16, so every fragment read
+//    later is one conflict-free ds_read_b128.  The weight operand arrives
+//    pre-packed in exactly that order (pack.hip); the activation operand's
+//    lanes each point at their own (possibly gathered) row;
+//  * NS-1 stages of copies stay in flight: wait for stage s+1 (explicit
+//    vmcnt), barrier, issue stage s+NS-1, then run stage s's MFMAs from
+//    registers while stage s+1's fragments stream in from LDS.
 //
-// Workgroup -> tile: blockIdx = m_tile * NT + n_tile.  Consecutive m-tiles of
-// one n-tile are NT workgroups apart; with NT a multiple of 8 they land on the
-// same XCD (workgroups are dealt round-robin over the 8 XCDs), so the weight
-// tile they share is fetched from HBM once into that XCD's L2.
-// Grouped mode: m-tiles are numbered expert by expert (mt_prefix); a
-// workgroup finds its expert by binary search and exits if it is past the
-// last tile (the grid is sized for the worst case, so no host sync is needed).
+// Workgroup -> tile order (XCD-aware).  Workgroups are dealt round-robin to the
+// 8 XCDs, so blockIdx % 8 names the XCD; each XCD takes one contiguous range
+// of the logical tile order (group, m-tile, n-tile; n-tile fastest).  Grouped
+// GEMMs thus give each XCD whole experts: an expert's gathered rows and its
+// weights are fetched into that XCD's L2 once.  The dense GEMM is split into
+// 8 column stripes ("virtual groups" sharing the same rows), one per XCD, so
+// each weight tile is fetched once and the activations once per XCD.
+// Grouped tile counts are known only on the device (after routing): the grid
+// is sized for the worst case and surplus workgroups exit at once.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace w8a8 {
 namespace {
 
-constexpr int BM = GEMM_BM, BN = GEMM_BN, BK = GEMM_BK;
-constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+#define LDS_AS __attribute__((address_space(3)))
 
 // SiLU(g) = g / (1 + exp(-g)); the exponential is computed in double and
 // rounded once to fp32 (correctly rounded fp32 exp but for vanishingly rare
@@ -45,35 +52,95 @@ __device__ __forceinline__ float silu_f32(float g) {
     return g / den;
 }
 
-template <int EPI>
-__global__ __launch_bounds__(256) void gemm_i8(GemmParams p) {
-    __shared__ __attribute__((aligned(16))) int8_t smem[2 * STAGE_BYTES];
-    __shared__ float row_scale[BM];
-    __shared__ int row_slot[BM];
-    __shared__ float row_w[BM];
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without the implied memory fence of __syncthreads (which
+// would wait for every load in flight, i.e. drain the copy pipeline); the
+// "memory" clobber keeps the compiler from moving LDS accesses across it.
+// Visibility of a copied stage is established by the vmcnt wait before it.
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+
+// One wave-wide 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4):
+// lane l's 16 bytes land at lds_wave_base + 16*l; M0 carries the LDS base.
+// Issued through inline asm so that the compiler does not model the LDS write:
+// it would otherwise drain the whole copy pipeline (vmcnt(0)) before every
+// LDS read it cannot prove disjoint.  The ring's hazards are handled by hand
+// (explicit vmcnt waits before the workgroup barrier).  Nothing else in the
+// kernel uses M0 (no LDS DMA builtins, no dynamic register indexing).
+__device__ __forceinline__ void dma16(const int8_t* gsrc, const int8_t* lds_wave_base) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const LDS_AS int8_t*)lds_wave_base);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gsrc), "s"(lds)
+                 : "memory", "m0");
+}
+
+template <int BM, int BN, int WM, int WN, int NS, int EPI>
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
+    constexpr int NW = WM * WN;                  // waves per workgroup
+    constexpr int FM = BM / WM / 16;             // fragment rows per wave
+    constexpr int FN = BN / WN / 16;             // fragment cols per wave
+    constexpr int NBA = BM / 16, NBB = BN / 16;  // 1 KiB blocks per stage
+    constexpr int NBLK = NBA + NBB;
+    static_assert(NBLK % NW == 0, "blocks must split evenly over the waves");
+    constexpr int DPW = NBLK / NW;               // copies per wave per stage
+    constexpr int STAGE = NBLK * 1024;
+    static_assert(NS >= 3, "the fragment prefetch needs at least three LDS stages");
+    static_assert(FM % 2 == 0, "half-tile variant");
+    // One LDS object only: the pipeline stages, then the per-row metadata.
+    // (With several __shared__ objects the compiler can no longer tell the
+    // copy target from other LDS data and drains the pipeline before every
+    // LDS read.)
+    __shared__ __attribute__((aligned(1024))) int8_t smem[NS * STAGE + 3 * BM * 4];
+    float* row_scale = reinterpret_cast<float*>(smem + NS * STAGE);
+    int* row_slot = reinterpret_cast<int*>(smem + NS * STAGE + BM * 4);
+    float* row_w = reinterpret_cast<float*>(smem + NS * STAGE + 2 * BM * 4);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int64_t bid = blockIdx.x;
-    const int mt = (int)(bid / p.NT), nt = (int)(bid % p.NT);
+    const int wm = wave / WN, wn = wave % WN;
 
-    // ---- which rows does this tile cover ----
-    int g = 0;
+    // ---- logical tile of this workgroup ----
+    const int64_t n_mt_dense = (p.M + BM - 1) / BM;
+    const int64_t total = (p.seg_offsets ? (int64_t)p.mt_prefix[p.G] : n_mt_dense * p.VG) * p.NTV;
+    const int64_t per_xcd = (total + 7) / 8;
+    const int64_t slot = blockIdx.x >> 3;
+    if (slot >= per_xcd) return;
+    const int64_t L = (int64_t)(blockIdx.x & 7) * per_xcd + slot;
+    if (L >= total) return;
+
+    int g = 0, nt;
     int64_t row0, row_end;
     if (p.seg_offsets) {
-        if (mt >= p.mt_prefix[p.G]) return;
+        const int64_t mtL = L / p.NTV;  // index into the expert-major list of m-tiles
         int lo = 0, hi = p.G;
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
-            if (p.mt_prefix[mid] <= mt) lo = mid; else hi = mid;
+            if (p.mt_prefix[mid] <= mtL) lo = mid; else hi = mid;
         }
         g = lo;
-        row0 = p.seg_offsets[g] + (int64_t)(mt - p.mt_prefix[g]) * BM;
+        const int64_t local = L - (int64_t)p.mt_prefix[g] * p.NTV;
+        const int mtl = (int)(local / p.NTV);
+        nt = (int)(local % p.NTV);
+        row0 = p.seg_offsets[g] + (int64_t)mtl * BM;
         row_end = min(row0 + BM, (int64_t)p.seg_offsets[g + 1]);
     } else {
-        row0 = (int64_t)mt * BM;
+        const int64_t per_vg = n_mt_dense * p.NTV;
+        const int vg = (int)(L / per_vg);
+        const int64_t local = L - vg * per_vg;
+        const int64_t mt = local / p.NTV;
+        nt = vg * p.NTV + (int)(local % p.NTV);
+        row0 = mt * BM;
         row_end = min(row0 + BM, p.M);
     }
+    // fragment rows of this wave holding at least one valid row (the rest of a
+    // segment's last, partial tile is neither read nor multiplied)
+    const int rows_valid = (int)(row_end - row0);
+    const int fm_active =
+        __builtin_amdgcn_readfirstlane(min(FM, max(0, (rows_valid - wm * FM * 16 + 15) / 16)));
 
     // ---- per-row metadata for the epilogue ----
     if (tid < BM) {
@@ -93,153 +160,216 @@ __global__ __launch_bounds__(256) void gemm_i8(GemmParams p) {
         }
     }
 
-    // ---- global source pointers: 4 A chunks and 4 B chunks of 16 B per thread ----
+    // ---- copy sources: this wave moves blocks wave, wave+NW, ... of each stage ----
     const int K = p.K;
-    const int8_t* a_src[4];
-    int a_lds[4];
+    const int64_t KB = K / 64;
+    const int8_t* src[DPW];
+    int stride[DPW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = tid + i * 256;
-        const int row = c >> 3, kc = c & 7;
-        int64_t r = row0 + row;
-        if (r >= row_end) r = row0;  // rows past the segment read a valid row; results dropped
-        int64_t src_row = r;
-        if (EPI == EPI_GATE_UP)
-            src_row = min(max((int64_t)(p.sorted_assign[r] / p.topk), (int64_t)0), p.a_rows - 1);
-        a_src[i] = p.A + src_row * K + kc * 16;
-        const int kb = kc >> 2, gq = kc & 3, mb = row >> 4;
-        a_lds[i] = (kb * (BM / 16) + mb) * 1024 + ((row & 15) + 16 * gq) * 16;
-    }
-    const int KB = K / 64;  // 1 KiB blocks per 16-channel column block
-    const int8_t* b_base = p.B + (int64_t)g * p.b_group_bytes + (int64_t)(nt * (BN / 16)) * KB * 1024;
-    const int8_t* b_src[4];
-    int b_lds[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = tid + i * 256;
-        const int nbl = c >> 7, within = c & 127;
-        const int kbl = within >> 6, ln = within & 63;
-        b_src[i] = b_base + (int64_t)nbl * KB * 1024 + kbl * 1024 + ln * 16;
-        b_lds[i] = A_BYTES + (kbl * (BN / 16) + nbl) * 1024 + ln * 16;
-    }
-
-    v4i ra[4], rb[4];
-    auto gload = [&](int ks) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ra[i] = *reinterpret_cast<const v4i*>(a_src[i] + (int64_t)ks * BK);
-            rb[i] = *reinterpret_cast<const v4i*>(b_src[i] + (int64_t)ks * 2 * 1024);
+    for (int i = 0; i < DPW; ++i) {
+        const int b = wave + NW * i;
+        if (b < NBA) {  // activation rows: lane -> (row l%16, 16-byte chunk l/16)
+            int64_t r = row0 + b * 16 + (lane & 15);
+            if (r >= row_end) r = row0;  // rows past the segment read a valid row; results dropped
+            int64_t src_row = r;
+            if (EPI == EPI_GATE_UP)
+                src_row = min(max((int64_t)(p.sorted_assign[r] / p.topk), (int64_t)0), p.a_rows - 1);
+            src[i] = p.A + src_row * K + (lane >> 4) * 16;
+            stride[i] = 64;
+        } else {        // packed weights: 1 KiB contiguous per (16 channels, 64 k)
+            const int nb = nt * NBB + (b - NBA);
+            src[i] = p.B + (int64_t)g * p.b_group_bytes + (int64_t)nb * KB * 1024 + lane * 16;
+            stride[i] = 1024;
         }
+    }
+    auto issue = [&](int ks) {
+        const int8_t* stage = smem + (ks % NS) * STAGE;
+#pragma unroll
+        for (int i = 0; i < DPW; ++i)
+            dma16(src[i] + (int64_t)ks * stride[i], stage + (wave + NW * i) * 1024);
     };
-    auto sstore = [&](int buf) {
-        int8_t* base = smem + buf * STAGE_BYTES;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<v4i*>(base + a_lds[i]) = ra[i];
-            *reinterpret_cast<v4i*>(base + b_lds[i]) = rb[i];
-        }
+    auto frag_a = [&](int ks, int i) {
+        return *reinterpret_cast<const v4i*>(smem + (ks % NS) * STAGE + (wm * FM + i) * 1024 + lane * 16);
+    };
+    auto frag_b = [&](int ks, int j) {
+        return *reinterpret_cast<const v4i*>(smem + (ks % NS) * STAGE + (NBA + wn * FN + j) * 1024 +
+                                             lane * 16);
     };
 
-    v4i acc[4][4];
+    const int nk = K / 64;
+    // prologue: NS-1 stages in flight, stage 0's fragments in registers
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < nk) issue(s);
+    if (nk - 1 >= NS - 2) wait_vmcnt<(NS - 2) * DPW>();
+    else wait_vmcnt<0>();
+    barrier_nofence();
+    v4i fa[FM], fb[FN], fbn[FN];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v4i{0, 0, 0, 0};
-
-    const int nk = K / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int ks = 0; ks < nk; ++ks) {
-        const int buf = ks & 1;
-        if (ks + 1 < nk) gload(ks + 1);
-        const int8_t* base = smem + buf * STAGE_BYTES;
+    for (int i = 0; i < FM; ++i)
+        if (i < fm_active) fa[i] = frag_a(0, i);
 #pragma unroll
-        for (int kb = 0; kb < BK / 64; ++kb) {
-            v4i fa[4], fb[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                fa[i] = *reinterpret_cast<const v4i*>(base + (kb * (BM / 16) + wm * 4 + i) * 1024 + lane * 16);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                fb[j] = *reinterpret_cast<const v4i*>(base + A_BYTES + (kb * (BN / 16) + wn * 4 + j) * 1024 + lane * 16);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
-        }
-        if (ks + 1 < nk) sstore(buf ^ 1);
-        __syncthreads();
-    }
+    for (int j = 0; j < FN; ++j) fb[j] = frag_b(0, j);
 
     // ---- epilogue: lane l, register r of block (i, j) holds
-    //      row = (wm*4+i)*16 + (l/16)*4 + r, col = (wn*4+j)*16 + l%16 ----
-    const int col_in_blk = lane & 15;
-    if (EPI == EPI_GATE_UP) {
-        // column blocks alternate gate / up for the same 16 channels
-        const int I = p.I;
-        const float* sg = p.s_b + (int64_t)g * 2 * I;
+    //      row = (wm*FM+i)*16 + (l/16)*4 + r, col = (wn*FN+j)*16 + l%16.
+    //      It runs inside each compute variant below, so the accumulators never
+    //      have to be merged across the variants' register assignments. ----
+    auto epilogue = [&](v4i (&acc)[FM][FN]) {
+        __syncthreads();  // row metadata written before the main loop is visible here
+        const int col_in_blk = lane & 15;
+        if (EPI == EPI_GATE_UP) {
+            // column blocks alternate gate / up for the same 16 channels
+            static_assert(EPI != EPI_GATE_UP || FN % 2 == 0, "gate/up pairs");
+            const int I = p.I;
+            const float* sg = p.s_b + (int64_t)g * 2 * I;
 #pragma unroll
-        for (int jp = 0; jp < 2; ++jp) {
-            const int gblk = nt * (BN / 16) + wn * 4 + 2 * jp;  // even: gate block
-            const int ch = (gblk >> 1) * 16 + col_in_blk;
-            const float s_gate = sg[ch], s_up = sg[I + ch];
+            for (int jp = 0; jp < FN / 2; ++jp) {
+                const int gblk = nt * NBB + wn * FN + 2 * jp;  // even: gate block
+                const int ch = (gblk >> 1) * 16 + col_in_blk;
+                const float s_gate = sg[ch], s_up = sg[I + ch];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < FM; ++i) {
+                    if (i >= fm_active) continue;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = (wm * 4 + i) * 16 + (lane >> 4) * 4 + r;
-                    const int64_t grow = row0 + row;
-                    if (grow < row_end) {
-                        const float sx = row_scale[row];
-                        const float gv = ((float)acc[i][2 * jp][r] * sx) * s_gate;
-                        const float uv = ((float)acc[i][2 * jp + 1][r] * sx) * s_up;
-                        p.out_f32[grow * I + ch] = silu_f32(gv) * uv;
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = (wm * FM + i) * 16 + (lane >> 4) * 4 + r;
+                        const int64_t grow = row0 + row;
+                        if (grow < row_end) {
+                            const float sx = row_scale[row];
+                            const float gv = ((float)acc[i][2 * jp][r] * sx) * s_gate;
+                            const float uv = ((float)acc[i][2 * jp + 1][r] * sx) * s_up;
+                            p.out_f32[grow * I + ch] = silu_f32(gv) * uv;
+                        }
                     }
                 }
-        }
-    } else {
-        const int N = p.N;
+            }
+        } else {
+            const int N = p.N;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n = nt * BN + (wn * 4 + j) * 16 + col_in_blk;
-            float sb = 0.0f;
-            if (EPI != EPI_DENSE_I32) sb = p.s_b[(int64_t)g * N + n];
+            for (int j = 0; j < FN; ++j) {
+                const int n = nt * BN + (wn * FN + j) * 16 + col_in_blk;
+                float sb = 0.0f;
+                if (EPI != EPI_DENSE_I32) sb = p.s_b[(int64_t)g * N + n];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < FM; ++i) {
+                    if (i >= fm_active) continue;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = (wm * 4 + i) * 16 + (lane >> 4) * 4 + r;
-                    const int64_t grow = row0 + row;
-                    if (grow >= row_end) continue;
-                    if (EPI == EPI_DENSE_I32) {
-                        p.out_i32[grow * N + n] = acc[i][j][r];
-                    } else if (EPI == EPI_DENSE_F32) {
-                        p.out_f32[grow * N + n] = ((float)acc[i][j][r] * row_scale[row]) * sb;
-                    } else {  // EPI_DOWN
-                        const float v = ((float)acc[i][j][r] * row_scale[row]) * sb;
-                        p.out_f32[(int64_t)row_slot[row] * N + n] = row_w[row] * v;
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = (wm * FM + i) * 16 + (lane >> 4) * 4 + r;
+                        const int64_t grow = row0 + row;
+                        if (grow >= row_end) continue;
+                        if (EPI == EPI_DENSE_I32) {
+                            p.out_i32[grow * N + n] = acc[i][j][r];
+                        } else if (EPI == EPI_DENSE_F32) {
+                            p.out_f32[grow * N + n] = ((float)acc[i][j][r] * row_scale[row]) * sb;
+                        } else {  // EPI_DOWN
+                            const float v = ((float)acc[i][j][r] * row_scale[row]) * sb;
+                            p.out_f32[(int64_t)row_slot[row] * N + n] = row_w[row] * v;
+                        }
                     }
                 }
+            }
         }
+    };
+
+    // Stage ks's MFMAs run from registers while stage ks+1's fragments stream
+    // in from LDS: the B fragments into a second set, each A fragment right
+    // after its last use.  F = fragment rows this wave computes: FM for a full
+    // tile; in a segment's last, partial tile FM/2 or 0.
+    auto mfma_and_refill = [&](auto f_tag, v4i (&acc)[FM][FN], int next_ks, bool refill) {
+        constexpr int F = decltype(f_tag)::value;
+#pragma unroll
+        for (int i = 0; i < F; ++i) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            if (refill) fa[i] = frag_a(next_ks, i);
+            // keep each refill next to the MFMAs it follows (hoisting them all
+            // would need a second set of A registers)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto run = [&](auto f_tag) {
+        constexpr int F = decltype(f_tag)::value;
+        v4i acc[FM][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+        int ks = 0;
+        // steady state: stage ks+1 landed (NS-3 newer stages may still fly),
+        // refill the ring with stage ks+NS-1
+        for (; ks + NS - 1 < nk; ++ks) {
+            wait_vmcnt<(NS - 3) * DPW>();
+            barrier_nofence();
+            issue(ks + NS - 1);
+            if (F > 0) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j) fbn[j] = frag_b(ks + 1, j);
+            }
+            mfma_and_refill(f_tag, acc, ks + 1, true);
+            if (F > 0) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j) fb[j] = fbn[j];
+            }
+        }
+        // drain: nothing left to issue
+        for (; ks + 1 < nk; ++ks) {
+            wait_vmcnt<0>();
+            barrier_nofence();
+            if (F > 0) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j) fbn[j] = frag_b(ks + 1, j);
+            }
+            mfma_and_refill(f_tag, acc, ks + 1, true);
+            if (F > 0) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j) fb[j] = fbn[j];
+            }
+        }
+        mfma_and_refill(f_tag, acc, 0, false);
+        epilogue(acc);
+    };
+    if (fm_active > FM / 2) run(std::integral_constant<int, FM>{});
+    else if (fm_active > 0) run(std::integral_constant<int, FM / 2>{});
+    else run(std::integral_constant<int, 0>{});
+}
+
+template <int BM, int BN, int WM, int WN, int NS>
+hipError_t launch_tile(int epi, const GemmParams& p, int64_t blocks, hipStream_t s) {
+    const dim3 grid((unsigned)blocks), block(WM * WN * 64);
+    switch (epi) {
+        case EPI_DENSE_F32: gemm_i8<BM, BN, WM, WN, NS, EPI_DENSE_F32><<<grid, block, 0, s>>>(p); break;
+        case EPI_DENSE_I32: gemm_i8<BM, BN, WM, WN, NS, EPI_DENSE_I32><<<grid, block, 0, s>>>(p); break;
+        case EPI_GATE_UP: gemm_i8<BM, BN, WM, WN, NS, EPI_GATE_UP><<<grid, block, 0, s>>>(p); break;
+        case EPI_DOWN: gemm_i8<BM, BN, WM, WN, NS, EPI_DOWN><<<grid, block, 0, s>>>(p); break;
+        default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm(int epi, const GemmParams& p, int64_t m_tiles, hipStream_t s) {
-    const int64_t blocks = m_tiles * p.NT;
-    if (blocks == 0) return hipSuccess;
-    const dim3 grid((unsigned)blocks), block(256);
-    switch (epi) {
-        case EPI_DENSE_F32: gemm_i8<EPI_DENSE_F32><<<grid, block, 0, s>>>(p); break;
-        case EPI_DENSE_I32: gemm_i8<EPI_DENSE_I32><<<grid, block, 0, s>>>(p); break;
-        case EPI_GATE_UP: gemm_i8<EPI_GATE_UP><<<grid, block, 0, s>>>(p); break;
-        case EPI_DOWN: gemm_i8<EPI_DOWN><<<grid, block, 0, s>>>(p); break;
-        default: return hipErrorInvalidValue;
+int gemm_tile_n(int64_t N) { return (N % 256 == 0) ? 256 : 128; }
+
+hipError_t launch_gemm(int epi, const GemmParams& p_in, int64_t max_m_tiles, hipStream_t s) {
+    GemmParams p = p_in;
+    const int bn = gemm_tile_n(p.N);
+    const int nt_all = (int)(p.N / bn);
+    if (p.seg_offsets) {
+        p.VG = 1;
+        p.NTV = nt_all;
+    } else {
+        // dense: 8 column stripes (one per XCD) when the n-tiles divide evenly
+        p.VG = (nt_all % 8 == 0) ? 8 : 1;
+        p.NTV = nt_all / p.VG;
     }
-    return hipGetLastError();
+    const int64_t max_tiles = max_m_tiles * nt_all;
+    if (max_tiles == 0) return hipSuccess;
+    const int64_t blocks = 8 * ((max_tiles + 7) / 8);
+    if (bn == 256) return launch_tile<GEMM_BM, 256, 2, 4, 4>(epi, p, blocks, s);
+    return launch_tile<GEMM_BM, 128, 2, 4, 4>(epi, p, blocks, s);
 }
 
 }  // namespace w8a8

@@ -9,10 +9,9 @@ namespace w8a8 {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-// Tile shape of the int8 MFMA GEMM (rows x output channels x reduction).
-constexpr int GEMM_BM = 128;
-constexpr int GEMM_BN = 128;
-constexpr int GEMM_BK = 128;
+// Row-tile height of the int8 MFMA GEMM (the m-tile unit of the routing's
+// per-expert tile prefix).
+constexpr int GEMM_BM = 256;
 
 // Routing works on chunks of 64 tokens (one bit per token in a 64-bit mask).
 constexpr int ROUTE_CHUNK = 64;
@@ -32,7 +31,7 @@ struct GemmParams {
     int64_t b_group_bytes;    // bytes per group of packed weights (N*K)
     int64_t M;                // dense: rows; grouped: total assignments
     int N, K;
-    int NT;                   // N / GEMM_BN
+    int VG, NTV;              // set by launch_gemm: column stripes and n-tiles per stripe
     const int32_t* seg_offsets;  // grouped: [G+1] segment starts, else nullptr
     const int32_t* mt_prefix;    // grouped: [G+1] prefix of m-tiles per group
     int G;
@@ -54,7 +53,9 @@ hipError_t launch_quantize_rows(const float* x, int64_t rows, int64_t cols, int6
 hipError_t launch_pack_weights(const int8_t* w, int64_t groups, int64_t n, int64_t k, int kind,
                                int8_t* packed, hipStream_t s);
 
-hipError_t launch_gemm(int epi, const GemmParams& p, int64_t m_tiles, hipStream_t s);
+// max_m_tiles: an upper bound of the number of BM-row tiles (grouped: over all
+// experts); surplus workgroups exit on the device.
+hipError_t launch_gemm(int epi, const GemmParams& p, int64_t max_m_tiles, hipStream_t s);
 
 // Number of partial sums the router GEMM splits H into (so a small token
 // count still yields enough workgroups); the workspace holds S*T*E floats.
