@@ -17,10 +17,11 @@
 //  * K advances 64 bytes per pipeline stage; NS stages live in LDS at once;
 //  * operands move global -> LDS with global_load_lds_dwordx4 (no VGPR
 //    staging): one wave instruction moves one 16-row x 64-byte MFMA fragment
-//    (1 KiB), lane l writing its 16 bytes at l*16, so every fragment read
+//    (1 KiB), lane l writing its 16 bytes at l*16, and every fragment read
 //    later is one conflict-free ds_read_b128.  The weight operand arrives
-//    pre-packed in exactly that order (pack.hip); the activation operand's
-//    lanes each point at their own (possibly gathered) row;
+//    pre-packed in fragment order (pack.hip); for the activation operand each
+//    4-lane group fetches one (possibly gathered) row's 64 bytes, stored at an
+//    XOR-swizzled slot;
 //  * NS-1 stages of copies stay in flight: wait for stage s+1 (explicit
 //    vmcnt), barrier, issue stage s+NS-1, then run stage s's MFMAs from
 //    registers while stage s+1's fragments stream in from LDS.
@@ -168,13 +169,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
         const int b = wave + NW * i;
-        if (b < NBA) {  // activation rows: lane -> (row l%16, 16-byte chunk l/16)
-            int64_t r = row0 + b * 16 + (lane & 15);
+        if (b < NBA) {
+            // activation rows: each 4-lane group fetches one row's 64 bytes (one
+            // contiguous request); chunk c of row r goes to LDS slot
+            // 4r + (c ^ (r/4)), which keeps the fragment reads conflict-free
+            int64_t r = row0 + b * 16 + (lane >> 2);
             if (r >= row_end) r = row0;  // rows past the segment read a valid row; results dropped
             int64_t src_row = r;
             if (EPI == EPI_GATE_UP)
                 src_row = min(max((int64_t)(p.sorted_assign[r] / p.topk), (int64_t)0), p.a_rows - 1);
-            src[i] = p.A + src_row * K + (lane >> 4) * 16;
+            src[i] = p.A + src_row * K + (((lane & 3) ^ ((lane >> 4) & 3)) * 16);
             stride[i] = 64;
         } else {        // packed weights: 1 KiB contiguous per (16 channels, 64 k)
             const int nb = nt * NBB + (b - NBA);
@@ -188,8 +192,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
         for (int i = 0; i < DPW; ++i)
             dma16(src[i] + (int64_t)ks * stride[i], stage + (wave + NW * i) * 1024);
     };
+    // MFMA A operand: lane l holds row l%16, 16-byte k-chunk l/16 of the block
+    const int a_slot = 4 * (lane & 15) + ((lane >> 4) ^ ((lane >> 2) & 3));
     auto frag_a = [&](int ks, int i) {
-        return *reinterpret_cast<const v4i*>(smem + (ks % NS) * STAGE + (wm * FM + i) * 1024 + lane * 16);
+        return *reinterpret_cast<const v4i*>(smem + (ks % NS) * STAGE + (wm * FM + i) * 1024 + a_slot * 16);
     };
     auto frag_b = [&](int ks, int j) {
         return *reinterpret_cast<const v4i*>(smem + (ks % NS) * STAGE + (NBA + wn * FN + j) * 1024 +
@@ -211,65 +217,95 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) fb[j] = frag_b(0, j);
 
-    // ---- epilogue: lane l, register r of block (i, j) holds
-    //      row = (wm*FM+i)*16 + (l/16)*4 + r, col = (wn*FN+j)*16 + l%16.
-    //      It runs inside each compute variant below, so the accumulators never
-    //      have to be merged across the variants' register assignments. ----
+    // ---- epilogue.  Lane l, register r of accumulator block (i, j) holds
+    //      row (wm*FM+i)*16 + (l/16)*4 + r, column (wn*FN+j)*16 + l%16.  The
+    //      values are finished in registers, staged through the (now idle) LDS
+    //      ring 32 rows at a time, and leave as 16-byte stores that cover whole
+    //      256-byte (128-byte for h) row segments.  It runs inside each compute
+    //      variant below, so the accumulators never have to be merged across
+    //      the variants' register assignments. ----
+    constexpr int OCOLS = (EPI == EPI_GATE_UP) ? FN * 8 : FN * 16;  // output columns per wave
+    constexpr int SROW = OCOLS + 4;                                 // padded staging stride (words)
+    static_assert(NW * 32 * SROW * 4 <= NS * STAGE, "epilogue staging fits in the LDS ring");
     auto epilogue = [&](v4i (&acc)[FM][FN]) {
-        __syncthreads();  // row metadata written before the main loop is visible here
+        __syncthreads();  // the ring is idle; row metadata written before the loop is visible
+        uint32_t* stg = reinterpret_cast<uint32_t*>(smem) + wave * (32 * SROW);
         const int col_in_blk = lane & 15;
-        if (EPI == EPI_GATE_UP) {
-            // column blocks alternate gate / up for the same 16 channels
-            static_assert(EPI != EPI_GATE_UP || FN % 2 == 0, "gate/up pairs");
-            const int I = p.I;
-            const float* sg = p.s_b + (int64_t)g * 2 * I;
+        const int I = p.I, N = p.N;
+        // first output column of this wave
+        const int64_t col0 = (EPI == EPI_GATE_UP) ? (int64_t)(nt * NBB + wn * FN) / 2 * 16
+                                                  : (int64_t)nt * BN + wn * FN * 16;
+        float s_col[FN];
 #pragma unroll
-            for (int jp = 0; jp < FN / 2; ++jp) {
-                const int gblk = nt * NBB + wn * FN + 2 * jp;  // even: gate block
-                const int ch = (gblk >> 1) * 16 + col_in_blk;
-                const float s_gate = sg[ch], s_up = sg[I + ch];
+        for (int j = 0; j < FN; ++j) {
+            if (EPI == EPI_GATE_UP) {
+                const int jp = j >> 1;
+                const int ch = (int)col0 + jp * 16 + col_in_blk;
+                s_col[j] = p.s_b[(int64_t)g * 2 * I + ((j & 1) ? I : 0) + ch];
+            } else if (EPI != EPI_DENSE_I32) {
+                s_col[j] = p.s_b[(int64_t)g * N + col0 + j * 16 + col_in_blk];
+            } else {
+                s_col[j] = 0.0f;
+            }
+        }
 #pragma unroll
-                for (int i = 0; i < FM; ++i) {
-                    if (i >= fm_active) continue;
+        for (int i0 = 0; i0 < FM; i0 += 2) {
+            if (i0 >= fm_active) break;
+            // finish 2 fragment rows (32 rows) in registers, stage them
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int row = (wm * FM + i) * 16 + (lane >> 4) * 4 + r;
-                        const int64_t grow = row0 + row;
-                        if (grow < row_end) {
-                            const float sx = row_scale[row];
-                            const float gv = ((float)acc[i][2 * jp][r] * sx) * s_gate;
-                            const float uv = ((float)acc[i][2 * jp + 1][r] * sx) * s_up;
-                            p.out_f32[grow * I + ch] = silu_f32(gv) * uv;
+            for (int di = 0; di < 2; ++di) {
+                const int i = i0 + di;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int lr = di * 16 + (lane >> 4) * 4 + r;            // staged row
+                    const int row = (wm * FM + i) * 16 + (lane >> 4) * 4 + r;  // tile row
+                    if (EPI == EPI_GATE_UP) {
+                        // column blocks alternate gate / up for the same 16 channels
+                        const float sx = row_scale[row];
+#pragma unroll
+                        for (int jp = 0; jp < FN / 2; ++jp) {
+                            const float gv = ((float)acc[i][2 * jp][r] * sx) * s_col[2 * jp];
+                            const float uv = ((float)acc[i][2 * jp + 1][r] * sx) * s_col[2 * jp + 1];
+                            stg[lr * SROW + jp * 16 + col_in_blk] = __float_as_uint(silu_f32(gv) * uv);
+                        }
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < FN; ++j) {
+                            uint32_t v;
+                            if (EPI == EPI_DENSE_I32) {
+                                v = (uint32_t)acc[i][j][r];
+                            } else if (EPI == EPI_DENSE_F32) {
+                                v = __float_as_uint(((float)acc[i][j][r] * row_scale[row]) * s_col[j]);
+                            } else {  // EPI_DOWN
+                                const float dq = ((float)acc[i][j][r] * row_scale[row]) * s_col[j];
+                                v = __float_as_uint(row_w[row] * dq);
+                            }
+                            stg[lr * SROW + j * 16 + col_in_blk] = v;
                         }
                     }
                 }
             }
-        } else {
-            const int N = p.N;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's staging complete
+            // write out: each lane moves 16 bytes; a wave covers 64*4/OCOLS rows
+            constexpr int LPR = OCOLS / 4;   // lanes per row
+            constexpr int RPI = 64 / LPR;    // rows per instruction
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int n = nt * BN + (wn * FN + j) * 16 + col_in_blk;
-                float sb = 0.0f;
-                if (EPI != EPI_DENSE_I32) sb = p.s_b[(int64_t)g * N + n];
-#pragma unroll
-                for (int i = 0; i < FM; ++i) {
-                    if (i >= fm_active) continue;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int row = (wm * FM + i) * 16 + (lane >> 4) * 4 + r;
-                        const int64_t grow = row0 + row;
-                        if (grow >= row_end) continue;
-                        if (EPI == EPI_DENSE_I32) {
-                            p.out_i32[grow * N + n] = acc[i][j][r];
-                        } else if (EPI == EPI_DENSE_F32) {
-                            p.out_f32[grow * N + n] = ((float)acc[i][j][r] * row_scale[row]) * sb;
-                        } else {  // EPI_DOWN
-                            const float v = ((float)acc[i][j][r] * row_scale[row]) * sb;
-                            p.out_f32[(int64_t)row_slot[row] * N + n] = row_w[row] * v;
-                        }
-                    }
+            for (int q = 0; q < 32 / RPI; ++q) {
+                const int lr = q * RPI + lane / LPR;
+                const int c4 = (lane % LPR) * 4;
+                const int row = (wm * FM + i0) * 16 + lr;
+                const int64_t grow = row0 + row;
+                if (grow < row_end) {
+                    const v4i v = *reinterpret_cast<const v4i*>(stg + lr * SROW + c4);
+                    int64_t dst;
+                    if (EPI == EPI_GATE_UP) dst = grow * I + col0 + c4;
+                    else if (EPI == EPI_DOWN) dst = (int64_t)row_slot[row] * N + col0 + c4;
+                    else dst = grow * N + col0 + c4;
+                    if (EPI == EPI_DENSE_I32) *reinterpret_cast<v4i*>(p.out_i32 + dst) = v;
+                    else *reinterpret_cast<v4i*>(p.out_f32 + dst) = v;
                 }
             }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next pass
         }
     };
 
