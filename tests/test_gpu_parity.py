@@ -326,3 +326,26 @@ def test_moe_deterministic_and_token_independent(w8):
     inp2["x"] = inp["x"][perm.cuda()].contiguous()
     c = _gpu_moe(w8, inp2, wts)
     assert np.array_equal(c["y"], a["y"][perm.numpy()])
+
+
+def test_quantize_rows_half_integer_and_tiny_scales(w8):
+    """Quotients at and next to half-integers (where a reciprocal-multiply
+    shortcut could round differently) and rows of subnormal magnitude."""
+    rng = np.random.default_rng(11)
+    rows = []
+    for amax in (127.0, 254.0, 1.0, 3.0e-38, 1.0e-41):
+        s = np.float32(amax) / np.float32(127.0)
+        k = rng.integers(-126, 126, size=2048).astype(np.float32)  # |k+0.5| < 127: amax stays
+        v = (k + np.float32(0.5)) * s                      # near k + 0.5 after division
+        v = np.nextafter(v, rng.choice([-np.inf, np.inf], size=v.shape).astype(np.float32))
+        v[::3] = (k[::3] + np.float32(0.5)) * s
+        v[0] = np.float32(amax)
+        rows.append(v.astype(np.float32))
+    x = np.stack(rows)
+    for cols in (2048, 1024, 512):
+        xs = np.ascontiguousarray(x[:, :cols])
+        q, sc = w8.quantize_rows(torch.from_numpy(xs).cuda())
+        torch.cuda.synchronize()
+        qo, so = oracle.quantize_rows(xs)
+        assert np.array_equal(to_np(sc), so)
+        assert np.array_equal(to_np(q), qo)

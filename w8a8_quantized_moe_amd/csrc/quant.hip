@@ -6,8 +6,9 @@
 // quotient x/s is an IEEE fp32 division and round() is round-half-to-even
 // (v_rndne).  An all-zero row gives s = 0 and all-zero codes.
 //
-// HBM-bound: each row is read once (cached in VGPRs while the wave reduces its
-// maximum), and its codes and scale written once.  Loads and stores are full
+// HBM-bound: each row is read once (cached in VGPRs while its maximum is
+// reduced: one wave per row up to 1024 columns, one 256-thread workgroup per
+// row above), and its codes and scale written once.  Loads and stores are
 // 16-byte (read) / 4-byte (write) per lane and contiguous across the wave.
 #include "internal.h"
 
@@ -23,6 +24,25 @@ __device__ __forceinline__ float wave_max(float v) {
 __device__ __forceinline__ int quant_one(float v, float s) {
     if (s == 0.0f) return 0;
     float r = __builtin_rintf(v / s);
+    r = fminf(fmaxf(r, -128.0f), 127.0f);
+    return (int)r;
+}
+
+// Same result as quant_one, cheaper: y = v * (1/s) differs from the IEEE
+// quotient fl(v/s) by less than 2.5 ulp, i.e. by less than 2^-15 for
+// |v/s| <= 127.  Rounding y and fl(v/s) to the nearest integer can then only
+// disagree if y lies within 2^-15 of a half-integer; those (rare) elements
+// take the exact division.
+__device__ __forceinline__ int quant_fast(float v, float s, float rs) {
+    if (s == 0.0f) return 0;
+    const float y = v * rs;
+    const float fy = fabsf(y);
+    const float frac = fy - __builtin_floorf(fy);
+    float r;
+    // the comparisons are written so that a non-finite y (1/s overflowing for
+    // a subnormal scale) also takes the exact path
+    if (fy <= 128.0f && fabsf(frac - 0.5f) >= 0x1p-15f) r = __builtin_rintf(y);
+    else r = __builtin_rintf(v / s);
     r = fminf(fmaxf(r, -128.0f), 127.0f);
     return (int)r;
 }
@@ -61,14 +81,56 @@ __global__ __launch_bounds__(256) void quant_rows_cached(const float* __restrict
     }
     amax = wave_max(amax);
     const float s = amax / 127.0f;
+    const float rs = 1.0f / s;
     if (lane == 0) scale[row] = s;
     uint32_t* qr = reinterpret_cast<uint32_t*>(q + row * (int64_t)cols);
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int c = i * 64 + lane;
         if (c < nv)
-            qr[c] = pack4(quant_one(v[i].x, s), quant_one(v[i].y, s), quant_one(v[i].z, s),
-                          quant_one(v[i].w, s));
+            qr[c] = pack4(quant_fast(v[i].x, s, rs), quant_fast(v[i].y, s, rs),
+                          quant_fast(v[i].z, s, rs), quant_fast(v[i].w, s, rs));
+    }
+}
+
+// Long rows (vector path): one 256-thread workgroup per row, VPT float4 per
+// thread held in registers; the row maximum goes through a wave reduction and
+// four LDS slots.
+template <int VPT>
+__global__ __launch_bounds__(256) void quant_rows_block(const float* __restrict__ x, int64_t rows,
+                                                        int cols, int64_t ld, int8_t* __restrict__ q,
+                                                        float* __restrict__ scale) {
+    __shared__ float wmax[4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t row = blockIdx.x;
+    const float4* xr = reinterpret_cast<const float4*>(x + row * ld);
+    const int nv = cols >> 2;
+    float4 v[VPT];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int c = i * 256 + tid;
+        if (c < nv) {
+            v[i] = xr[c];
+            amax = fmaxf(amax, amax4(v[i]));
+        } else {
+            v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+    amax = wave_max(amax);
+    if (lane == 0) wmax[wv] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float s = amax / 127.0f;
+    const float rs = 1.0f / s;
+    if (tid == 0) scale[row] = s;
+    uint32_t* qr = reinterpret_cast<uint32_t*>(q + row * (int64_t)cols);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int c = i * 256 + tid;
+        if (c < nv)
+            qr[c] = pack4(quant_fast(v[i].x, s, rs), quant_fast(v[i].y, s, rs),
+                          quant_fast(v[i].z, s, rs), quant_fast(v[i].w, s, rs));
     }
 }
 
@@ -98,8 +160,18 @@ hipError_t launch_quantize_rows(const float* x, int64_t rows, int64_t cols, int6
     if (rows == 0) return hipSuccess;
     const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
     const bool vec = (cols % 4 == 0) && (ld % 4 == 0) && ((uintptr_t)x % 16 == 0) &&
-                     ((uintptr_t)q % 4 == 0) && cols <= 32 * 256;
-    if (vec) {
+                     ((uintptr_t)q % 4 == 0) && cols <= 8 * 1024;
+    if (vec && cols > 1024) {
+        const int nv = (int)(cols / 4);
+        const int need = (nv + 255) / 256;
+        const dim3 g1((unsigned)rows);
+        if (need <= 2)
+            quant_rows_block<2><<<g1, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
+        else if (need <= 4)
+            quant_rows_block<4><<<g1, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
+        else
+            quant_rows_block<8><<<g1, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
+    } else if (vec) {
         const int nv = (int)(cols / 4);
         const int need = (nv + 63) / 64;
         if (need <= 1)
@@ -108,12 +180,8 @@ hipError_t launch_quantize_rows(const float* x, int64_t rows, int64_t cols, int6
             quant_rows_cached<2><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
         else if (need <= 4)
             quant_rows_cached<4><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
-        else if (need <= 8)
-            quant_rows_cached<8><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
-        else if (need <= 16)
-            quant_rows_cached<16><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
         else
-            quant_rows_cached<32><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
+            quant_rows_cached<4><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
     } else {
         quant_rows_twopass<<<grid, block, 0, s>>>(x, rows, cols, ld, q, scale);
     }

@@ -9,15 +9,18 @@
 // for the routing reorder).
 //
 // Kernels, all on the caller's stream, no host synchronisation:
-//   router_partial  fp32 MFMA GEMM (v_mfma_f32_16x16x4_f32), 64x64 tiles,
-//                   optionally split along H into S partial sums so small
-//                   token counts still fill the GPU;
-//   topk_count      per 64-token chunk: sums the S partials in a fixed order
-//                   (deterministic), adds the bias, picks the top-k by wave
-//                   arg-max rounds (ties to the lower index), computes the
-//                   renormalised softmax weights, and ranks each assignment
-//                   among the chunk's tokens routed to the same expert with a
-//                   64-bit token mask per expert in LDS;
+//   router_partial  fp32 MFMA GEMM (v_mfma_f32_16x16x4_f32), 64-token x
+//                   all-expert tiles (activations read once), optionally
+//                   split along H into S partial sums so small token counts
+//                   still fill the GPU;
+//   router_reduce   (split only) sums the S partials in split order (a fixed,
+//                   deterministic order) and adds the bias;
+//   topk_count      per 64-token chunk: picks the top-k by wave arg-max rounds
+//                   (ties to the lower index), computes the renormalised
+//                   softmax weights, and ranks each assignment among the
+//                   chunk's tokens routed to the same expert with a 64-bit
+//                   token mask per expert (a single chunk also finishes the
+//                   permutation below in the same workgroup);
 //   chunk_scan      per expert: exclusive scan of its per-chunk counts;
 //   finalize        exclusive scan over experts -> segment offsets, and the
 //                   prefix of m-tiles per expert for the grouped GEMMs;
@@ -28,118 +31,159 @@
 namespace w8a8 {
 namespace {
 
-constexpr int RBM = 64, RBN = 64, RBK = 32, RPAD = 16;
+constexpr int RBM = 64, RBK = 32, RPAD = 4;
 
-// partial[s][t][e] = sum over h in split s of x[t][h] * wr[e][h]
+// partial[s][t][e] = sum over h in split s of x[t][h] * wr[e][h]   (fp32 MFMA);
+// with a single split the output is the logits themselves, bias included.
+// One workgroup: 64 tokens x all experts (E padded to 64*EB), so the
+// activations are read once; wave w owns experts [16*EB*w, 16*EB*(w+1)).
+// K advances 32 per stage through a double-buffered, k-major LDS tile.
+template <int EB>
 __global__ __launch_bounds__(256) void router_partial(const float* __restrict__ x,
-                                                      const float* __restrict__ wr, int T, int H,
+                                                      const float* __restrict__ wr,
+                                                      const float* __restrict__ bias, int T, int H,
                                                       int E, int ksplit_len,
                                                       float* __restrict__ partial) {
-    __shared__ float As[2][RBK][RBM + RPAD];
-    __shared__ float Bs[2][RBK][RBN + RPAD];
+    constexpr int EP = 64 * EB;  // padded expert count
+    constexpr int AW = RBM + RPAD, BW = EP + RPAD;
+    __shared__ float As[2][RBK][AW];
+    __shared__ float Bs[2][RBK][BW];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1;
-    const int m0 = blockIdx.x * RBM, n0 = blockIdx.y * RBN;
-    const int split = blockIdx.z;
+    const int m0 = blockIdx.x * RBM;
+    const int split = blockIdx.y;
     const int kbeg = split * ksplit_len;
     const int nstage = ksplit_len / RBK;
 
-    float4 ra[2], rb[2];
+    // global tile loads: A 64x32 (2 float4 per thread), B EPx32 (2*EB float4 per thread)
+    float4 ra0, ra1, rb[2 * EB];
     const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = tid + i * 256;
-            const int row = c >> 3, k4 = c & 7;
-            const int t = m0 + row, e = n0 + row;
-            ra[i] = (t < T) ? *reinterpret_cast<const float4*>(x + (int64_t)t * H + k0 + k4 * 4) : zero4;
-            rb[i] = (e < E) ? *reinterpret_cast<const float4*>(wr + (int64_t)e * H + k0 + k4 * 4) : zero4;
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = tid + i * 256;
-            const int row = c >> 3, k4 = c & 7;
-            As[buf][k4 * 4 + 0][row] = ra[i].x;
-            As[buf][k4 * 4 + 1][row] = ra[i].y;
-            As[buf][k4 * 4 + 2][row] = ra[i].z;
-            As[buf][k4 * 4 + 3][row] = ra[i].w;
-            Bs[buf][k4 * 4 + 0][row] = rb[i].x;
-            Bs[buf][k4 * 4 + 1][row] = rb[i].y;
-            Bs[buf][k4 * 4 + 2][row] = rb[i].z;
-            Bs[buf][k4 * 4 + 3][row] = rb[i].w;
-        }
-    };
+#define ROUTER_GLOAD(k0)                                                                          \
+    do {                                                                                          \
+        {                                                                                         \
+            const int t_ = m0 + (tid >> 3), t1_ = m0 + ((tid + 256) >> 3);                        \
+            ra0 = *reinterpret_cast<const float4*>(x + (int64_t)min(t_, T - 1) * H + (k0) + (tid & 7) * 4); \
+            ra1 = *reinterpret_cast<const float4*>(x + (int64_t)min(t1_, T - 1) * H + (k0) + (tid & 7) * 4); \
+            if (t_ >= T) ra0 = zero4;                                                             \
+            if (t1_ >= T) ra1 = zero4;                                                            \
+        }                                                                                         \
+        _Pragma("unroll") for (int i = 0; i < 2 * EB; ++i) {                                      \
+            const int c_ = tid + i * 256;                                                         \
+            const int e_ = c_ >> 3;                                                               \
+            rb[i] = *reinterpret_cast<const float4*>(wr + (int64_t)min(e_, E - 1) * H + (k0) + (c_ & 7) * 4); \
+            if (e_ >= E) rb[i] = zero4;                                                           \
+        }                                                                                         \
+    } while (0)
+#define ROUTER_SSTORE(buf)                                                                        \
+    do {                                                                                          \
+        const int k4_ = (tid & 7) * 4, r0_ = tid >> 3, r1_ = (tid + 256) >> 3;                    \
+        As[buf][k4_ + 0][r0_] = ra0.x; As[buf][k4_ + 1][r0_] = ra0.y;                             \
+        As[buf][k4_ + 2][r0_] = ra0.z; As[buf][k4_ + 3][r0_] = ra0.w;                             \
+        As[buf][k4_ + 0][r1_] = ra1.x; As[buf][k4_ + 1][r1_] = ra1.y;                             \
+        As[buf][k4_ + 2][r1_] = ra1.z; As[buf][k4_ + 3][r1_] = ra1.w;                             \
+        _Pragma("unroll") for (int i = 0; i < 2 * EB; ++i) {                                      \
+            const int c_ = tid + i * 256;                                                         \
+            const int e_ = c_ >> 3;                                                               \
+            Bs[buf][k4_ + 0][e_] = rb[i].x; Bs[buf][k4_ + 1][e_] = rb[i].y;                       \
+            Bs[buf][k4_ + 2][e_] = rb[i].z; Bs[buf][k4_ + 3][e_] = rb[i].w;                       \
+        }                                                                                         \
+    } while (0)
 
-    v4f acc[2][2];
+    v4f acc[4][EB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < EB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    gload(kbeg);
-    sstore(0);
+    ROUTER_GLOAD(kbeg);
+    ROUTER_SSTORE(0);
     __syncthreads();
     for (int st = 0; st < nstage; ++st) {
         const int buf = st & 1;
-        if (st + 1 < nstage) gload(kbeg + (st + 1) * RBK);
+        if (st + 1 < nstage) ROUTER_GLOAD(kbeg + (st + 1) * RBK);
 #pragma unroll
         for (int kk = 0; kk < RBK / 4; ++kk) {
             const int kr = kk * 4 + (lane >> 4);
-            const float a0 = As[buf][kr][wm * 32 + (lane & 15)];
-            const float a1 = As[buf][kr][wm * 32 + 16 + (lane & 15)];
-            const float b0 = Bs[buf][kr][wn * 32 + (lane & 15)];
-            const float b1 = Bs[buf][kr][wn * 32 + 16 + (lane & 15)];
-            acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
-            acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
-            acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
-            acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
+            float a[4], bb[EB];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = As[buf][kr][i * 16 + (lane & 15)];
+#pragma unroll
+            for (int j = 0; j < EB; ++j) bb[j] = Bs[buf][kr][(w * EB + j) * 16 + (lane & 15)];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < EB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], bb[j], acc[i][j], 0, 0, 0);
         }
-        if (st + 1 < nstage) sstore(buf ^ 1);
+        if (st + 1 < nstage) ROUTER_SSTORE(buf ^ 1);
         __syncthreads();
     }
+#undef ROUTER_GLOAD
+#undef ROUTER_SSTORE
     float* out = partial + (int64_t)split * T * E;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < EB; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = m0 + wm * 32 + i * 16 + (lane >> 4) * 4 + r;
-                const int e = n0 + wn * 32 + j * 16 + (lane & 15);
-                if (t < T && e < E) out[(int64_t)t * E + e] = acc[i][j][r];
+                const int t = m0 + i * 16 + (lane >> 4) * 4 + r;
+                const int e = (w * EB + j) * 16 + (lane & 15);
+                // a single split writes the finished logits (bias added once)
+                if (t < T && e < E)
+                    out[(int64_t)t * E + e] = (bias && gridDim.y == 1) ? acc[i][j][r] + bias[e] : acc[i][j][r];
             }
 }
 
-__global__ __launch_bounds__(256) void topk_count(const float* __restrict__ partial, int S,
-                                                  const float* __restrict__ bias, int T, int E, int k,
-                                                  int nchunks, float* __restrict__ logits,
-                                                  int32_t* __restrict__ ids, float* __restrict__ wts,
-                                                  int32_t* __restrict__ rank,
-                                                  int32_t* __restrict__ chunk_counts) {
+// logits[t][e] = (sum of the S split partials, in split order) + bias[e]
+__global__ __launch_bounds__(256) void router_reduce(const float* __restrict__ partial, int S,
+                                                     const float* __restrict__ bias, int T, int E,
+                                                     float* __restrict__ logits) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t n = (int64_t)T * E;
+    if (i >= n) return;
+    float v = 0.0f;
+    for (int sp = 0; sp < S; ++sp) v += partial[(int64_t)sp * n + i];
+    if (bias) v += bias[i % E];
+    logits[i] = v;
+}
+
+// Block-wide exclusive scan of one int per thread (256 threads).
+__device__ int block_exclusive_scan(int v, int* total, int* lds /* >= 4 ints */);
+
+// Per 64-token chunk: top-k per token by wave arg-max rounds (ties to the
+// lower index), the renormalised softmax weights, and the rank of each
+// assignment among the chunk's tokens routed to the same expert (a 64-bit
+// token mask per expert in LDS).  With a single chunk (FUSED) the same
+// workgroup also produces the expert counts, segment offsets, m-tile
+// prefixes and the sorted assignment list, saving three launches.
+template <bool FUSED>
+__global__ __launch_bounds__(256) void topk_count(const float* __restrict__ logits, int T, int E,
+                                                  int k, int nchunks, int32_t* __restrict__ ids,
+                                                  float* __restrict__ wts, int32_t* __restrict__ rank,
+                                                  int32_t* __restrict__ chunk_counts,
+                                                  int32_t* __restrict__ expert_counts,
+                                                  int32_t* __restrict__ offsets, int bm_gu,
+                                                  int bm_dn, int32_t* __restrict__ mt_gu,
+                                                  int32_t* __restrict__ mt_dn,
+                                                  int32_t* __restrict__ sorted_assign) {
     __shared__ int ids_s[ROUTE_CHUNK * MAX_TOPK];
     __shared__ unsigned long long mask[MAX_EXPERTS];
+    __shared__ int off_s[MAX_EXPERTS];
+    __shared__ int scan_lds[4];
     const int c = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int t0 = c * ROUTE_CHUNK;
+    const int nt = min(ROUTE_CHUNK, T - t0);
     for (int e = tid; e < E; e += 256) mask[e] = 0ull;
 
-    for (int tl = w; tl < ROUTE_CHUNK; tl += 4) {
-        const int t = c * ROUTE_CHUNK + tl;
-        if (t >= T) break;
+    for (int tl = w; tl < nt; tl += 4) {
+        const int t = t0 + tl;
+        const float* lrow = logits + (int64_t)t * E;
         float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = lane + 64 * i;
-            if (e < E) {
-                float s = 0.0f;
-                for (int sp = 0; sp < S; ++sp) s += partial[((int64_t)sp * T + t) * E + e];
-                if (bias) s += bias[e];
-                v[i] = s;
-                logits[(int64_t)t * E + e] = s;
-            } else {
-                v[i] = -INFINITY;
-            }
+            v[i] = (e < E) ? lrow[min(e, E - 1)] : -INFINITY;
         }
         float sel_v[MAX_TOPK];
         int sel_i[MAX_TOPK];
@@ -172,35 +216,56 @@ __global__ __launch_bounds__(256) void topk_count(const float* __restrict__ part
         }
         if (lane == 0) {
             // softmax over the picked logits == full softmax renormalised over them
-            const float m = sel_v[0];
+            const float mx = sel_v[0];
             float ex[MAX_TOPK];
-            float sum = 0.0f;
+            float z = 0.0f;
             for (int j = 0; j < k; ++j) {
-                ex[j] = expf(sel_v[j] - m);
-                sum += ex[j];
+                ex[j] = expf(sel_v[j] - mx);
+                z += ex[j];
             }
             for (int j = 0; j < k; ++j) {
                 ids[(int64_t)t * k + j] = sel_i[j];
-                wts[(int64_t)t * k + j] = ex[j] / sum;
+                wts[(int64_t)t * k + j] = ex[j] / z;
                 ids_s[tl * k + j] = sel_i[j];
             }
         }
     }
     __syncthreads();
-    for (int al = tid; al < ROUTE_CHUNK * k; al += 256) {
-        const int tl = al / k;
-        if (c * ROUTE_CHUNK + tl < T) atomicOr(&mask[ids_s[al]], 1ull << tl);
-    }
+    for (int al = tid; al < nt * k; al += 256) atomicOr(&mask[ids_s[al]], 1ull << (al / k));
     __syncthreads();
-    for (int al = tid; al < ROUTE_CHUNK * k; al += 256) {
-        const int tl = al / k, j = al - tl * k;
-        const int t = c * ROUTE_CHUNK + tl;
-        if (t < T) {
+    if (!FUSED) {
+        for (int al = tid; al < nt * k; al += 256) {
+            const int tl = al / k;
+            rank[(int64_t)t0 * k + al] = __popcll(mask[ids_s[al]] & ((1ull << tl) - 1ull));
+        }
+        for (int e = tid; e < E; e += 256) chunk_counts[(int64_t)e * nchunks + c] = __popcll(mask[e]);
+    } else {
+        // single chunk: counts -> offsets -> m-tile prefixes -> sorted list
+        const int cnt = tid < E ? __popcll(mask[tid]) : 0;
+        int tot0, tot1, tot2;
+        const int off = block_exclusive_scan(cnt, &tot0, scan_lds);
+        const int m1 = block_exclusive_scan((cnt + bm_gu - 1) / bm_gu, &tot1, scan_lds);
+        const int m2 = block_exclusive_scan((cnt + bm_dn - 1) / bm_dn, &tot2, scan_lds);
+        if (tid < E) {
+            expert_counts[tid] = cnt;
+            offsets[tid] = off;
+            mt_gu[tid] = m1;
+            mt_dn[tid] = m2;
+            off_s[tid] = off;
+        }
+        if (tid == 0) {
+            offsets[E] = tot0;
+            mt_gu[E] = tot1;
+            mt_dn[E] = tot2;
+        }
+        __syncthreads();
+        for (int al = tid; al < nt * k; al += 256) {
+            const int tl = al / k;
             const int e = ids_s[al];
-            rank[(int64_t)t * k + j] = __popcll(mask[e] & ((1ull << tl) - 1ull));
+            const int pos = off_s[e] + __popcll(mask[e] & ((1ull << tl) - 1ull));
+            sorted_assign[pos] = (int32_t)al;  // t0 == 0
         }
     }
-    for (int e = tid; e < E; e += 256) chunk_counts[(int64_t)e * nchunks + c] = __popcll(mask[e]);
 }
 
 // Block-wide exclusive scan of one int per thread (256 threads).
@@ -288,10 +353,13 @@ __global__ __launch_bounds__(256) void scatter(const int32_t* __restrict__ ids, 
 }  // namespace
 
 int router_splits(int T, int E, int H) {
-    const int tiles = ((T + RBM - 1) / RBM) * ((E + RBN - 1) / RBN);
+    (void)E;
+    // enough workgroups to fill the GPU, at least 8 stages (256 of H) per split;
+    // the split count divides the stage count H/32
+    const int tiles = (T + RBM - 1) / RBM;
     const int stages = H / RBK;
     int s = 1;
-    while (tiles * s < 512 && (stages % (2 * s)) == 0 && stages / (2 * s) >= 2) s *= 2;
+    while (tiles * s < 256 && stages % (2 * s) == 0 && stages / (2 * s) >= 8) s *= 2;
     return s;
 }
 
@@ -299,11 +367,29 @@ hipError_t launch_route(const RouteInputs& in, const RouteBuffers& b, hipStream_
     const int T = in.T, E = in.E, k = in.k, H = in.H, S = in.splits;
     const int nchunks = (T + ROUTE_CHUNK - 1) / ROUTE_CHUNK;
     {
-        const dim3 grid((T + RBM - 1) / RBM, (E + RBN - 1) / RBN, S);
-        router_partial<<<grid, 256, 0, s>>>(in.x, in.router_w, T, H, E, H / S, b.partial);
+        const dim3 grid((T + RBM - 1) / RBM, S);
+        const int eb = (E + 63) / 64;
+        float* out = (S == 1) ? b.logits : b.partial;
+        if (eb == 1) router_partial<1><<<grid, 256, 0, s>>>(in.x, in.router_w, in.router_b, T, H, E, H / S, out);
+        else if (eb == 2) router_partial<2><<<grid, 256, 0, s>>>(in.x, in.router_w, in.router_b, T, H, E, H / S, out);
+        else if (eb == 3) router_partial<3><<<grid, 256, 0, s>>>(in.x, in.router_w, in.router_b, T, H, E, H / S, out);
+        else router_partial<4><<<grid, 256, 0, s>>>(in.x, in.router_w, in.router_b, T, H, E, H / S, out);
     }
-    topk_count<<<nchunks, 256, 0, s>>>(b.partial, S, in.router_b, T, E, k, nchunks, b.logits,
-                                       b.topk_ids, b.topk_w, b.rank, b.chunk_counts);
+    if (S > 1) {
+        const int64_t n = (int64_t)T * E;
+        router_reduce<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>(b.partial, S, in.router_b, T, E,
+                                                                          b.logits);
+    }
+    if (nchunks == 1) {
+        topk_count<true><<<1, 256, 0, s>>>(b.logits, T, E, k, nchunks, b.topk_ids, b.topk_w, b.rank,
+                                           b.chunk_counts, b.expert_counts, b.expert_offsets, in.bm_gu,
+                                           in.bm_dn, b.mt_prefix_gu, b.mt_prefix_dn, b.sorted_assign);
+        return hipGetLastError();
+    }
+    topk_count<false><<<nchunks, 256, 0, s>>>(b.logits, T, E, k, nchunks, b.topk_ids, b.topk_w, b.rank,
+                                              b.chunk_counts, b.expert_counts, b.expert_offsets,
+                                              in.bm_gu, in.bm_dn, b.mt_prefix_gu, b.mt_prefix_dn,
+                                              b.sorted_assign);
     chunk_scan<<<E, 256, 0, s>>>(b.chunk_counts, nchunks, b.chunk_base, b.expert_counts);
     finalize<<<1, 256, 0, s>>>(b.expert_counts, E, in.bm_gu, in.bm_dn, b.expert_offsets,
                                b.mt_prefix_gu, b.mt_prefix_dn);
