@@ -20,6 +20,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -68,6 +69,55 @@ class HipEvents:
     def destroy(self, arr):
         for ev in arr:
             self.hip.hipEventDestroy(ev)
+
+
+# HBM traffic per dispatch measured with rocprofv3 counters (FETCH_SIZE and
+# WRITE_SIZE, each in its own pass, scaled by what the same counters read for a
+# plain device copy of known size).  Valid only for the kernel sources it was
+# measured on: the hash below must match the sources as they are now.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["w8a8_quantized_moe_amd/csrc/gemm.hip", "w8a8_quantized_moe_amd/csrc/internal.h",
+                  "w8a8_quantized_moe_amd/csrc/route.hip", "w8a8_quantized_moe_amd/csrc/quant.hip",
+                  "w8a8_quantized_moe_amd/csrc/combine.hip"]
+
+
+def kernel_sources_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, stage):
+    """HBM bytes per launch of a stage from profiles/traffic.json, or None when
+    there is no measurement or the kernels changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != kernel_sources_hash():
+        return None
+    ent = rec.get("stages", {}).get(f"{workload}:{stage}")
+    if not ent:
+        return None
+    return int(ent["fetch_bytes"] + ent["write_bytes"])
+
+
+def copy_calibration(torch, nbytes=1 << 30, reps=5):
+    """A plain device-to-device copy of known size: what FETCH_SIZE and
+    WRITE_SIZE read for it converts the counters to bytes."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    print(json.dumps({"copy_bytes_each_way": nbytes, "reps": reps, "ms": round(dt * 1e3, 4),
+                      "gbps_read_plus_write": round(2 * nbytes / dt / 1e9, 1)}), flush=True)
 
 
 def stage_work(T, H, E, k, I):
@@ -160,7 +210,8 @@ def bench_dense(args, torch, synth, w8):
         "stage_ms": {"quant": round(q_ms, 4), "gemm": round(g_ms, 4)},
         "roofline": dict(kernel="gemm", bound="mfma", achieved=round(ops / (g_ms * 1e-3) / 1e12, 2),
                          peak=PEAK_INT8_OPS / 1e12, unit="TOP/s",
-                         frac=round(ops / (g_ms * 1e-3) / PEAK_INT8_OPS, 4), traffic=None,
+                         frac=round(ops / (g_ms * 1e-3) / PEAK_INT8_OPS, 4),
+                         traffic=measured_traffic("dense", "gemm"),
                          work_per_launch=ops),
         "quant_roofline": dict(bound="hbm", achieved=round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
                                peak=PEAK_HBM / 1e9, unit="GB/s",
@@ -180,6 +231,8 @@ def main():
                     choices=["large", "prefill", "decode", "tiny", "dense"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration for the traffic field)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -194,6 +247,8 @@ def main():
     import w8a8_quantized_moe_amd as w8
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        return copy_calibration(torch)
     if args.workload == "dense":
         return bench_dense(args, torch, synth, w8)
     log(f"[bench] generating workload '{args.workload}' on the GPU")
@@ -246,8 +301,8 @@ def main():
     scale = 1e9 if unit == "GB/s" else 1e12
     achieved = amount / (stage_ms[dom] * 1e-3)
     roofline = dict(kernel=dom, bound=bound, achieved=round(achieved / scale, 2),
-                    peak=peak / scale, unit=unit, frac=round(achieved / peak, 4), traffic=None,
-                    work_per_launch=amount)
+                    peak=peak / scale, unit=unit, frac=round(achieved / peak, 4),
+                    traffic=measured_traffic(args.workload, dom), work_per_launch=amount)
 
     step_s = ms_per_step * 1e-3
     int8_ops = 6 * A * H * I

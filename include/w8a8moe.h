@@ -102,7 +102,9 @@ W8A8_API w8a8_status w8a8_quantize_rows(const float* x, int64_t rows, int64_t co
  *
  * w       device, int8 [groups][n][k], dense
  * packed  device, int8, w8a8_pack_weights_size() bytes (= groups*n*k)
- * Limits: n % 32 == 0 (GATE_UP: n even and n/2 % 16 == 0), k % 64 == 0.
+ * Limits: groups, n, k >= 1; k % 64 == 0; PLAIN n % 16 == 0; GATE_UP n % 32
+ * (so each half holds whole 16-channel blocks).  An unknown kind is
+ * W8A8_ERR_INVALID_ARGUMENT; w and packed must not overlap.
  * ------------------------------------------------------------------------- */
 enum { W8A8_PACK_PLAIN = 0, W8A8_PACK_GATE_UP = 1 };
 

@@ -1,0 +1,189 @@
+"""Host-side checks of the C ABI (no GPU needed): the shared library loads,
+exports every function include/w8a8moe.h declares with the argument count the
+Python binding marshals, and rejects bad arguments on the host before any
+kernel is enqueued."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w8a8moe.h")
+LIB = os.path.join(ROOT, "w8a8_quantized_moe_amd", "libw8a8moe.so")
+
+
+def _ensure_built():
+    if not os.path.exists(LIB):
+        subprocess.run([sys.executable, os.path.join(ROOT, "w8a8_quantized_moe_amd", "build.py")],
+                       check=True)
+
+
+_ensure_built()
+from w8a8_quantized_moe_amd import _lib  # noqa: E402  (needs the library)
+
+lib = _lib.lib
+
+
+def header_functions():
+    """{name: number of parameters} of every W8A8_API function in the header."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = {}
+    for m in re.finditer(r"W8A8_API\s+[\w\s\*]+?\b(w8a8_\w+)\s*\(([^)]*)\)\s*;", text):
+        params = m.group(2).strip()
+        out[m.group(1)] = 0 if params in ("", "void") else len(params.split(","))
+    return out
+
+
+def exported_symbols():
+    res = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True)
+    return {line.split()[-1] for line in res.stdout.splitlines() if " T " in line}
+
+
+def test_header_parses():
+    fns = header_functions()
+    assert len(fns) == 11, sorted(fns)
+
+
+def test_every_declared_function_is_exported():
+    syms = exported_symbols()
+    missing = [f for f in header_functions() if f not in syms]
+    assert not missing, missing
+
+
+def test_only_declared_functions_are_exported():
+    extra = sorted(s for s in exported_symbols() if s.startswith("w8a8") and s not in header_functions())
+    assert not extra, extra
+
+
+def test_binding_matches_header():
+    fns = header_functions()
+    assert set(_lib.SIGNATURES) == set(fns)
+    for name, nparams in fns.items():
+        assert len(_lib.SIGNATURES[name][1]) == nparams, name
+
+
+def test_status_strings_and_version():
+    names = {0: "W8A8_OK", 1: "W8A8_ERR_INVALID_ARGUMENT", 2: "W8A8_ERR_UNSUPPORTED_SHAPE",
+             3: "W8A8_ERR_WORKSPACE_TOO_SMALL", 4: "W8A8_ERR_MISALIGNED", 5: "W8A8_ERR_HIP"}
+    for code, name in names.items():
+        assert lib.w8a8_status_string(code).decode() == name
+    assert lib.w8a8_status_string(99).decode() == "W8A8_UNKNOWN_STATUS"
+    assert lib.w8a8_abi_version() == 1
+
+
+def _shape(T, H, E, k, I):
+    return _lib.MoeShape(T, H, E, k, I)
+
+
+def _query(T, H, E, k, I):
+    lay = _lib.MoeLayout()
+    st = lib.w8a8_moe_workspace_query(ctypes.byref(_shape(T, H, E, k, I)), ctypes.byref(lay))
+    return st, lay
+
+
+@pytest.mark.parametrize("T,H,E,k,I", [(16, 128, 8, 2, 256), (64, 4096, 64, 2, 1536),
+                                       (16384, 7168, 256, 8, 2048), (0, 128, 1, 1, 128)])
+def test_workspace_layout(T, H, E, k, I):
+    st, lay = _query(T, H, E, k, I)
+    assert st == 0
+    A = T * k
+    sizes = dict(x_q=T * H, x_scale=4 * T, logits=4 * T * E, topk_ids=4 * A, topk_w=4 * A,
+                 expert_counts=4 * E, expert_offsets=4 * (E + 1), sorted_assign=4 * A,
+                 h=4 * A * I, h_q=A * I, h_scale=4 * A, o=4 * A * H)
+    spans = sorted((getattr(lay, f), getattr(lay, f) + n, f) for f, n in sizes.items())
+    for (a0, a1, fa), (b0, _, fb) in zip(spans, spans[1:]):
+        assert a1 <= b0, (fa, fb)          # no overlap
+    for f in sizes:
+        assert getattr(lay, f) % 256 == 0, f
+    assert spans[-1][1] <= lay.internal <= lay.total_bytes
+
+
+@pytest.mark.parametrize("T,H,E,k,I,status", [
+    (16, 100, 8, 2, 256, 2),      # H not a multiple of 128
+    (16, 128, 8, 2, 200, 2),      # I not a multiple of 128
+    (16, 32768, 8, 2, 256, 2),    # H too large
+    (16, 128, 257, 2, 256, 2),    # E > 256
+    (16, 128, 8, 9, 256, 2),      # k > 8
+    (16, 128, 4, 5, 256, 2),      # k > E
+    (16, 128, 8, 0, 256, 2),      # k = 0
+    (1 << 22, 128, 8, 8, 256, 2),  # T*k > 2^24
+    (-1, 128, 8, 2, 256, 1),      # negative size
+])
+def test_workspace_query_rejects(T, H, E, k, I, status):
+    st, _ = _query(T, H, E, k, I)
+    assert st == status
+    assert lib.w8a8_last_error().decode()
+
+
+def test_null_arguments_rejected_before_launch():
+    lay = _lib.MoeLayout()
+    assert lib.w8a8_moe_workspace_query(None, ctypes.byref(lay)) == 1
+    assert lib.w8a8_moe_workspace_query(ctypes.byref(_shape(16, 128, 8, 2, 256)), None) == 1
+    # forward with NULL tensors: host check, nothing enqueued
+    w = _lib.MoeWeights()
+    st = lib.w8a8_moe_forward(ctypes.byref(_shape(16, 128, 8, 2, 256)), ctypes.byref(w), None, None,
+                              None, 0, None)
+    assert st == 1 and "NULL" in lib.w8a8_last_error().decode()
+    # T = 0 is a no-op that touches nothing
+    assert lib.w8a8_moe_forward(ctypes.byref(_shape(0, 128, 8, 2, 256)), None, None, None, None, 0,
+                                None) == 0
+
+
+def test_forward_checks_workspace_and_alignment():
+    # fake, never dereferenced device addresses: the host checks fail first
+    base = 1 << 40
+    w = _lib.MoeWeights(base, None, base, base, base, base)
+    sh = ctypes.byref(_shape(16, 128, 8, 2, 256))
+    st = lib.w8a8_moe_forward(sh, ctypes.byref(w), base, base + 65536, base + 2 * 65536, 16, None)
+    assert st == 3 and "workspace" in lib.w8a8_last_error().decode()
+    st = lib.w8a8_moe_forward(sh, ctypes.byref(w), base + 4, base + 65536, base + 2 * 65536, 1 << 30,
+                              None)
+    assert st == 4
+    st = lib.w8a8_moe_forward(sh, ctypes.byref(w), base, base + 65536, base + 2 * 65536 + 16, 1 << 30,
+                              None)
+    assert st == 4
+    st = lib.w8a8_moe_forward(sh, ctypes.byref(w), base, base, base + 2 * 65536, 1 << 30, None)
+    assert st == 1  # y aliases x
+
+
+def test_gemm_and_quant_argument_checks():
+    base = 1 << 40
+    assert lib.w8a8_gemm(base, base, base, base, 256, 200, 256, base, None) == 2   # N % 128
+    assert lib.w8a8_gemm(base, base, base, base, 256, 256, 100, base, None) == 2   # K % 128
+    assert lib.w8a8_gemm(base, base, base, base, 256, 256, 1 << 18, base, None) == 2  # K > 2^17
+    assert lib.w8a8_gemm(base, base, base, base, -1, 256, 256, base, None) == 1
+    assert lib.w8a8_gemm(base + 1, base, base, base, 256, 256, 256, base, None) == 4
+    assert lib.w8a8_gemm(None, None, None, None, 0, 256, 256, None, None) == 0      # M = 0 no-op
+    assert lib.w8a8_gemm_i32(base, None, 256, 256, 256, base, None) == 1
+    assert lib.w8a8_quantize_rows(base, 4, 0, 0, base, base, None) == 2            # cols = 0
+    assert lib.w8a8_quantize_rows(base, 4, 16, 8, base, base, None) == 1           # ld < cols
+    assert lib.w8a8_quantize_rows(None, 0, 16, 16, None, None, None) == 0          # rows = 0
+    assert lib.w8a8_quantize_rows(base + 2, 4, 16, 16, base, base, None) == 4
+
+
+def test_pack_size():
+    n = ctypes.c_size_t()
+    assert lib.w8a8_pack_weights_size(3, 64, 128, _lib.PACK_PLAIN, ctypes.byref(n)) == 0
+    assert n.value == 3 * 64 * 128
+    assert lib.w8a8_pack_weights_size(1, 64, 100, _lib.PACK_PLAIN, ctypes.byref(n)) == 2
+    assert lib.w8a8_pack_weights_size(1, 48, 128, _lib.PACK_GATE_UP, ctypes.byref(n)) == 2
+    assert lib.w8a8_pack_weights_size(1, 48, 128, _lib.PACK_PLAIN, ctypes.byref(n)) == 0
+    assert lib.w8a8_pack_weights_size(1, 64, 128, 7, ctypes.byref(n)) == 1
+    assert lib.w8a8_pack_weights_size(1, 64, 128, 0, None) == 1
+    base = 1 << 40
+    assert lib.w8a8_pack_weights(base, 1, 64, 128, 0, base, None) == 1   # in place
+
+
+def test_binding_shares_one_hip_runtime():
+    # importing the binding first (before anything imports torch) must still map
+    # a single HIP runtime: the library binds to the copy PyTorch loads
+    code = ("import re, sys; sys.path.insert(0, %r); import w8a8_quantized_moe_amd; "
+            "m = open('/proc/self/maps').read(); "
+            "print(len(set(re.findall(r'\\S*libamdhip64\\S*', m))))" % ROOT)
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True)
+    assert res.stdout.strip() == "1", res.stdout + res.stderr

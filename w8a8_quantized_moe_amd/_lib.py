@@ -8,6 +8,13 @@ from __future__ import annotations
 import ctypes
 import os
 
+# PyTorch must be loaded first: it brings its own copy of the HIP runtime
+# (requested as libamdhip64.so), and the library's dependency on
+# libamdhip64.so.7 then resolves to that same copy by soname.  Loading the
+# library first would map the system runtime as well, and two runtimes in one
+# process do not share devices, streams or memory.
+import torch  # noqa: F401
+
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libw8a8moe.so")
 
