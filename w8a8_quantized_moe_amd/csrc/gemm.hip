@@ -124,8 +124,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
         }
         g = lo;
         const int64_t local = L - (int64_t)p.mt_prefix[g] * p.NTV;
-        const int mtl = (int)(local / p.NTV);
-        nt = (int)(local % p.NTV);
+        // inside an expert, m-tiles vary fastest: the m-tiles that share one
+        // weight tile run side by side and share its reads in L2
+        const int mcount = p.mt_prefix[g + 1] - p.mt_prefix[g];
+        const int mtl = (int)(local % mcount);
+        nt = (int)(local / mcount);
         row0 = p.seg_offsets[g] + (int64_t)mtl * BM;
         row_end = min(row0 + BM, (int64_t)p.seg_offsets[g + 1]);
     } else {
@@ -210,7 +213,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     if (nk - 1 >= NS - 2) wait_vmcnt<(NS - 2) * DPW>();
     else wait_vmcnt<0>();
     barrier_nofence();
-    v4i fa[FM], fb[FN], fbn[FN];
+    v4i fa[FM], fb[FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
         if (i < fm_active) fa[i] = frag_a(0, i);
@@ -310,8 +313,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     };
 
     // Stage ks's MFMAs run from registers while stage ks+1's fragments stream
-    // in from LDS: the B fragments into a second set, each A fragment right
-    // after its last use.  F = fragment rows this wave computes: FM for a full
+    // in from LDS: each A fragment right after its last use, the B fragments
+    // once the stage's MFMAs are issued.  F = fragment rows this wave computes: FM for a full
     // tile; in a segment's last, partial tile FM/2 or 0.
     auto mfma_and_refill = [&](auto f_tag, v4i (&acc)[FM][FN], int next_ks, bool refill) {
         constexpr int F = decltype(f_tag)::value;
@@ -340,28 +343,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
             wait_vmcnt<(NS - 3) * DPW>();
             barrier_nofence();
             issue(ks + NS - 1);
-            if (F > 0) {
-#pragma unroll
-                for (int j = 0; j < FN; ++j) fbn[j] = frag_b(ks + 1, j);
-            }
             mfma_and_refill(f_tag, acc, ks + 1, true);
             if (F > 0) {
 #pragma unroll
-                for (int j = 0; j < FN; ++j) fb[j] = fbn[j];
+                for (int j = 0; j < FN; ++j) fb[j] = frag_b(ks + 1, j);
             }
         }
         // drain: nothing left to issue
         for (; ks + 1 < nk; ++ks) {
             wait_vmcnt<0>();
             barrier_nofence();
-            if (F > 0) {
-#pragma unroll
-                for (int j = 0; j < FN; ++j) fbn[j] = frag_b(ks + 1, j);
-            }
             mfma_and_refill(f_tag, acc, ks + 1, true);
             if (F > 0) {
 #pragma unroll
-                for (int j = 0; j < FN; ++j) fb[j] = fbn[j];
+                for (int j = 0; j < FN; ++j) fb[j] = frag_b(ks + 1, j);
             }
         }
         mfma_and_refill(f_tag, acc, 0, false);

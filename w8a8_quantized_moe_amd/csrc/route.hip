@@ -32,6 +32,7 @@ namespace w8a8 {
 namespace {
 
 constexpr int RBM = 64, RBK = 32, RPAD = 4;
+constexpr int TOPK_THREADS = 1024;  // 16 waves: 4 tokens of a 64-token chunk each
 
 // partial[s][t][e] = sum over h in split s of x[t][h] * wr[e][h]   (fp32 MFMA);
 // with a single split the output is the logits themselves, bias included.
@@ -141,14 +142,44 @@ __global__ __launch_bounds__(256) void router_reduce(const float* __restrict__ p
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t n = (int64_t)T * E;
     if (i >= n) return;
+    // loads are issued sixteen at a time so their latencies overlap; the sum
+    // itself still runs in split order
     float v = 0.0f;
-    for (int sp = 0; sp < S; ++sp) v += partial[(int64_t)sp * n + i];
+    int sp = 0;
+    for (; sp + 16 <= S; sp += 16) {
+        float u[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) u[q] = partial[(int64_t)(sp + q) * n + i];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) v += u[q];
+    }
+    for (; sp < S; ++sp) v += partial[(int64_t)sp * n + i];
     if (bias) v += bias[i % E];
     logits[i] = v;
 }
 
-// Block-wide exclusive scan of one int per thread (256 threads).
-__device__ int block_exclusive_scan(int v, int* total, int* lds /* >= 4 ints */);
+// Block-wide exclusive scan of one int per thread (NW waves of 64).
+template <int NW>
+__device__ int block_exclusive_scan(int v, int* total, int* lds /* >= NW ints */) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += u;
+    }
+    if (lane == 63) lds[w] = incl;
+    __syncthreads();
+    int base = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        if (i < w) base += lds[i];
+        tot += lds[i];
+    }
+    __syncthreads();
+    *total = tot;
+    return base + incl - v;
+}
 
 // Per 64-token chunk: top-k per token by wave arg-max rounds (ties to the
 // lower index), the renormalised softmax weights, and the rank of each
@@ -157,48 +188,51 @@ __device__ int block_exclusive_scan(int v, int* total, int* lds /* >= 4 ints */)
 // workgroup also produces the expert counts, segment offsets, m-tile
 // prefixes and the sorted assignment list, saving three launches.
 template <bool FUSED>
-__global__ __launch_bounds__(256) void topk_count(const float* __restrict__ logits, int T, int E,
-                                                  int k, int nchunks, int32_t* __restrict__ ids,
-                                                  float* __restrict__ wts, int32_t* __restrict__ rank,
-                                                  int32_t* __restrict__ chunk_counts,
-                                                  int32_t* __restrict__ expert_counts,
-                                                  int32_t* __restrict__ offsets, int bm_gu,
-                                                  int bm_dn, int32_t* __restrict__ mt_gu,
-                                                  int32_t* __restrict__ mt_dn,
-                                                  int32_t* __restrict__ sorted_assign) {
+__global__ __launch_bounds__(TOPK_THREADS) void topk_count(
+    const float* __restrict__ logits, int T, int E, int k, int nchunks, int32_t* __restrict__ ids,
+    float* __restrict__ wts, int32_t* __restrict__ rank, int32_t* __restrict__ chunk_counts,
+    int32_t* __restrict__ expert_counts, int32_t* __restrict__ offsets, int bm_gu, int bm_dn,
+    int32_t* __restrict__ mt_gu, int32_t* __restrict__ mt_dn, int32_t* __restrict__ sorted_assign) {
+    constexpr int NWAVE = TOPK_THREADS / 64;
+    constexpr int TPW = ROUTE_CHUNK / NWAVE;  // tokens per wave
     __shared__ int ids_s[ROUTE_CHUNK * MAX_TOPK];
+    __shared__ float val_s[ROUTE_CHUNK * MAX_TOPK];
     __shared__ unsigned long long mask[MAX_EXPERTS];
     __shared__ int off_s[MAX_EXPERTS];
-    __shared__ int scan_lds[4];
+    __shared__ int scan_lds[NWAVE];
     const int c = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int t0 = c * ROUTE_CHUNK;
     const int nt = min(ROUTE_CHUNK, T - t0);
-    for (int e = tid; e < E; e += 256) mask[e] = 0ull;
+    for (int e = tid; e < E; e += TOPK_THREADS) mask[e] = 0ull;
 
-    for (int tl = w; tl < nt; tl += 4) {
-        const int t = t0 + tl;
+    // the wave's tokens w, w+NWAVE, ...: their logit rows are loaded together
+    // (lane l holds experts l, l+64, l+128, l+192)
+    float vall[TPW][4];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int t = t0 + min(w + NWAVE * u, nt - 1);
         const float* lrow = logits + (int64_t)t * E;
-        float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = lane + 64 * i;
-            v[i] = (e < E) ? lrow[min(e, E - 1)] : -INFINITY;
+            vall[u][i] = (e < E) ? lrow[min(e, E - 1)] : -INFINITY;
         }
-        float sel_v[MAX_TOPK];
-        int sel_i[MAX_TOPK];
-        for (int j = 0; j < k; ++j) {
-            float bv = -INFINITY;
-            int bi = 0x7fffffff;
+    }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int e = lane + 64 * i;
-                // lanes hold experts in ascending order: strict '>' keeps the lower index
-                if (e < E && (v[i] > bv || bi == 0x7fffffff)) {
-                    bv = v[i];
-                    bi = e;
-                }
-            }
+    for (int u = 0; u < TPW; ++u) {
+        const int tl = w + NWAVE * u;
+        if (tl >= nt) break;
+        float v0 = vall[u][0], v1 = vall[u][1], v2 = vall[u][2], v3 = vall[u][3];
+        // k rounds of a wave arg-max; ties go to the lower expert index
+#pragma unroll 1
+        for (int j = 0; j < k; ++j) {
+            float bv = v0;
+            int bi = lane;
+            if (v1 > bv) { bv = v1; bi = lane + 64; }
+            if (v2 > bv) { bv = v2; bi = lane + 128; }
+            if (v3 > bv) { bv = v3; bi = lane + 192; }
+            if (bi >= E) bi = 0x7fffffff;  // padding never wins a tie
 #pragma unroll
             for (int o = 32; o >= 1; o >>= 1) {
                 const float ov = __shfl_xor(bv, o, 64);
@@ -208,44 +242,44 @@ __global__ __launch_bounds__(256) void topk_count(const float* __restrict__ logi
                     bi = oi;
                 }
             }
-            sel_v[j] = bv;
-            sel_i[j] = bi;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (lane + 64 * i == bi) v[i] = -INFINITY;
-        }
-        if (lane == 0) {
-            // softmax over the picked logits == full softmax renormalised over them
-            const float mx = sel_v[0];
-            float ex[MAX_TOPK];
-            float z = 0.0f;
-            for (int j = 0; j < k; ++j) {
-                ex[j] = expf(sel_v[j] - mx);
-                z += ex[j];
+            if (lane == 0) {
+                ids_s[tl * k + j] = bi;
+                val_s[tl * k + j] = bv;
             }
-            for (int j = 0; j < k; ++j) {
-                ids[(int64_t)t * k + j] = sel_i[j];
-                wts[(int64_t)t * k + j] = ex[j] / z;
-                ids_s[tl * k + j] = sel_i[j];
-            }
+            if (bi == lane) v0 = -INFINITY;
+            if (bi == lane + 64) v1 = -INFINITY;
+            if (bi == lane + 128) v2 = -INFINITY;
+            if (bi == lane + 192) v3 = -INFINITY;
         }
     }
     __syncthreads();
-    for (int al = tid; al < nt * k; al += 256) atomicOr(&mask[ids_s[al]], 1ull << (al / k));
+    // softmax over the picked logits == full softmax renormalised over them;
+    // one thread per token, terms summed in pick order
+    for (int tl = tid; tl < nt; tl += TOPK_THREADS) {
+        const int t = t0 + tl;
+        const float mx = val_s[tl * k];
+        float z = 0.0f;
+        for (int j = 0; j < k; ++j) z += expf(val_s[tl * k + j] - mx);
+        for (int j = 0; j < k; ++j) {
+            ids[(int64_t)t * k + j] = ids_s[tl * k + j];
+            wts[(int64_t)t * k + j] = expf(val_s[tl * k + j] - mx) / z;
+        }
+    }
+    for (int al = tid; al < nt * k; al += TOPK_THREADS) atomicOr(&mask[ids_s[al]], 1ull << (al / k));
     __syncthreads();
     if (!FUSED) {
-        for (int al = tid; al < nt * k; al += 256) {
+        for (int al = tid; al < nt * k; al += TOPK_THREADS) {
             const int tl = al / k;
             rank[(int64_t)t0 * k + al] = __popcll(mask[ids_s[al]] & ((1ull << tl) - 1ull));
         }
-        for (int e = tid; e < E; e += 256) chunk_counts[(int64_t)e * nchunks + c] = __popcll(mask[e]);
+        for (int e = tid; e < E; e += TOPK_THREADS) chunk_counts[(int64_t)e * nchunks + c] = __popcll(mask[e]);
     } else {
         // single chunk: counts -> offsets -> m-tile prefixes -> sorted list
         const int cnt = tid < E ? __popcll(mask[tid]) : 0;
         int tot0, tot1, tot2;
-        const int off = block_exclusive_scan(cnt, &tot0, scan_lds);
-        const int m1 = block_exclusive_scan((cnt + bm_gu - 1) / bm_gu, &tot1, scan_lds);
-        const int m2 = block_exclusive_scan((cnt + bm_dn - 1) / bm_dn, &tot2, scan_lds);
+        const int off = block_exclusive_scan<NWAVE>(cnt, &tot0, scan_lds);
+        const int m1 = block_exclusive_scan<NWAVE>((cnt + bm_gu - 1) / bm_gu, &tot1, scan_lds);
+        const int m2 = block_exclusive_scan<NWAVE>((cnt + bm_dn - 1) / bm_dn, &tot2, scan_lds);
         if (tid < E) {
             expert_counts[tid] = cnt;
             offsets[tid] = off;
@@ -259,35 +293,13 @@ __global__ __launch_bounds__(256) void topk_count(const float* __restrict__ logi
             mt_dn[E] = tot2;
         }
         __syncthreads();
-        for (int al = tid; al < nt * k; al += 256) {
+        for (int al = tid; al < nt * k; al += TOPK_THREADS) {
             const int tl = al / k;
             const int e = ids_s[al];
             const int pos = off_s[e] + __popcll(mask[e] & ((1ull << tl) - 1ull));
             sorted_assign[pos] = (int32_t)al;  // t0 == 0
         }
     }
-}
-
-// Block-wide exclusive scan of one int per thread (256 threads).
-__device__ int block_exclusive_scan(int v, int* total, int* lds /* >= 4 ints */) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int u = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += u;
-    }
-    if (lane == 63) lds[w] = incl;
-    __syncthreads();
-    int base = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (i < w) base += lds[i];
-        tot += lds[i];
-    }
-    __syncthreads();
-    *total = tot;
-    return base + incl - v;
 }
 
 __global__ __launch_bounds__(256) void chunk_scan(const int32_t* __restrict__ chunk_counts,
@@ -302,7 +314,7 @@ __global__ __launch_bounds__(256) void chunk_scan(const int32_t* __restrict__ ch
     int local = 0;
     for (int c = beg; c < end; ++c) local += cc[c];
     int total;
-    int run = block_exclusive_scan(local, &total, lds);
+    int run = block_exclusive_scan<4>(local, &total, lds);
     for (int c = beg; c < end; ++c) {
         cb[c] = run;
         run += cc[c];
@@ -318,9 +330,9 @@ __global__ __launch_bounds__(256) void finalize(const int32_t* __restrict__ expe
     const int e = threadIdx.x;
     const int cnt = e < E ? expert_counts[e] : 0;
     int tot0, tot1, tot2;
-    const int off = block_exclusive_scan(cnt, &tot0, lds);
-    const int m1 = block_exclusive_scan((cnt + bm_gu - 1) / bm_gu, &tot1, lds);
-    const int m2 = block_exclusive_scan((cnt + bm_dn - 1) / bm_dn, &tot2, lds);
+    const int off = block_exclusive_scan<4>(cnt, &tot0, lds);
+    const int m1 = block_exclusive_scan<4>((cnt + bm_gu - 1) / bm_gu, &tot1, lds);
+    const int m2 = block_exclusive_scan<4>((cnt + bm_dn - 1) / bm_dn, &tot2, lds);
     if (e < E) {
         offsets[e] = off;
         mt_gu[e] = m1;
@@ -354,12 +366,14 @@ __global__ __launch_bounds__(256) void scatter(const int32_t* __restrict__ ids, 
 
 int router_splits(int T, int E, int H) {
     (void)E;
-    // enough workgroups to fill the GPU, at least 8 stages (256 of H) per split;
-    // the split count divides the stage count H/32
+    // enough workgroups to fill the GPU, at least 8 stages (256 of H) per split
+    // (4 when there are few token tiles: each stage of a split costs about one
+    // memory round trip); the split count divides the stage count H/32
     const int tiles = (T + RBM - 1) / RBM;
     const int stages = H / RBK;
     int s = 1;
-    while (tiles * s < 256 && stages % (2 * s) == 0 && stages / (2 * s) >= 8) s *= 2;
+    const int min_stages = tiles >= 16 ? 8 : 4;
+    while (tiles * s < 256 && stages % (2 * s) == 0 && stages / (2 * s) >= min_stages) s *= 2;
     return s;
 }
 
@@ -381,12 +395,12 @@ hipError_t launch_route(const RouteInputs& in, const RouteBuffers& b, hipStream_
                                                                           b.logits);
     }
     if (nchunks == 1) {
-        topk_count<true><<<1, 256, 0, s>>>(b.logits, T, E, k, nchunks, b.topk_ids, b.topk_w, b.rank,
+        topk_count<true><<<1, TOPK_THREADS, 0, s>>>(b.logits, T, E, k, nchunks, b.topk_ids, b.topk_w, b.rank,
                                            b.chunk_counts, b.expert_counts, b.expert_offsets, in.bm_gu,
                                            in.bm_dn, b.mt_prefix_gu, b.mt_prefix_dn, b.sorted_assign);
         return hipGetLastError();
     }
-    topk_count<false><<<nchunks, 256, 0, s>>>(b.logits, T, E, k, nchunks, b.topk_ids, b.topk_w, b.rank,
+    topk_count<false><<<nchunks, TOPK_THREADS, 0, s>>>(b.logits, T, E, k, nchunks, b.topk_ids, b.topk_w, b.rank,
                                               b.chunk_counts, b.expert_counts, b.expert_offsets,
                                               in.bm_gu, in.bm_dn, b.mt_prefix_gu, b.mt_prefix_dn,
                                               b.sorted_assign);
