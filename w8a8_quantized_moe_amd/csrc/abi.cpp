@@ -244,6 +244,10 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     const int T = (int)shape->T, H = (int)shape->H, E = (int)shape->E, k = (int)shape->top_k,
               I = (int)shape->I;
     const int64_t A = (int64_t)T * k;
+    // few rows per expert (decode): the weights are streamed once by the
+    // register-fed skinny kernel; otherwise the LDS-tiled MFMA kernel
+    const bool skinny = A <= 4 * (int64_t)E;
+    const int bm = skinny ? w8a8::SKINNY_BM : w8a8::GEMM_BM;
     hipStream_t s = (hipStream_t)stream;
     char* ws = (char*)workspace;
     const w8a8_moe_workspace_layout& L = plan.lay;
@@ -270,8 +274,7 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     if (st != W8A8_OK) return st;
 
     // 2-4. router, top-k, permutation
-    w8a8::RouteInputs ri{x, wts->router_w, wts->router_b, T, H, E, k, plan.splits, w8a8::GEMM_BM,
-                         w8a8::GEMM_BM};
+    w8a8::RouteInputs ri{x, wts->router_w, wts->router_b, T, H, E, k, plan.splits, bm, bm};
     w8a8::RouteBuffers rb{};
     rb.partial = (float*)(ws + plan.partial);
     rb.logits = (float*)(ws + L.logits);
@@ -308,7 +311,8 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     gu.I = I;
     gu.a_rows = T;
     if ((st = mark(2)) != W8A8_OK) return st;
-    st = check_hip(w8a8::launch_gemm(w8a8::EPI_GATE_UP, gu, max_m_tiles(A, E, w8a8::GEMM_BM), s),
+    st = check_hip(skinny ? w8a8::launch_gemm_skinny(w8a8::EPI_GATE_UP, gu, max_m_tiles(A, E, bm), s)
+                          : w8a8::launch_gemm(w8a8::EPI_GATE_UP, gu, max_m_tiles(A, E, bm), s),
                    "gate-up gemm");
     if (st != W8A8_OK) return st;
 
@@ -336,7 +340,8 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     dn.out_f32 = o;
     dn.a_rows = A;
     if ((st = mark(4)) != W8A8_OK) return st;
-    st = check_hip(w8a8::launch_gemm(w8a8::EPI_DOWN, dn, max_m_tiles(A, E, w8a8::GEMM_BM), s),
+    st = check_hip(skinny ? w8a8::launch_gemm_skinny(w8a8::EPI_DOWN, dn, max_m_tiles(A, E, bm), s)
+                          : w8a8::launch_gemm(w8a8::EPI_DOWN, dn, max_m_tiles(A, E, bm), s),
                    "down gemm");
     if (st != W8A8_OK) return st;
 

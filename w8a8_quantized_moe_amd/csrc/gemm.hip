@@ -28,9 +28,10 @@
 //
 // Workgroup -> tile order (XCD-aware).  Workgroups are dealt round-robin to the
 // 8 XCDs, so blockIdx % 8 names the XCD; each XCD takes one contiguous range
-// of the logical tile order (group, m-tile, n-tile; n-tile fastest).  Grouped
-// GEMMs thus give each XCD whole experts: an expert's gathered rows and its
-// weights are fetched into that XCD's L2 once.  The dense GEMM is split into
+// of the logical tile order (group, n-tile, m-tile; m-tile fastest).  Grouped
+// GEMMs thus give each XCD whole experts, and the m-tiles that share a weight
+// tile run side by side: an expert's gathered rows and its weights are
+// fetched into that XCD's L2 about once.  The dense GEMM is split into
 // 8 column stripes ("virtual groups" sharing the same rows), one per XCD, so
 // each weight tile is fetched once and the activations once per XCD.
 // Grouped tile counts are known only on the device (after routing): the grid
@@ -43,15 +44,6 @@ namespace w8a8 {
 namespace {
 
 #define LDS_AS __attribute__((address_space(3)))
-
-// SiLU(g) = g / (1 + exp(-g)); the exponential is computed in double and
-// rounded once to fp32 (correctly rounded fp32 exp but for vanishingly rare
-// double-rounding cases); the add and the divide are IEEE fp32.
-__device__ __forceinline__ float silu_f32(float g) {
-    const float e = (float)exp(-(double)g);
-    const float den = 1.0f + e;
-    return g / den;
-}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

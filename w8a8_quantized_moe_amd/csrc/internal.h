@@ -18,6 +18,16 @@ constexpr int ROUTE_CHUNK = 64;
 constexpr int MAX_EXPERTS = 256;
 constexpr int MAX_TOPK = 8;
 
+// SiLU(g) = g / (1 + exp(-g)); the exponential is computed in double and
+// rounded once to fp32 (correctly rounded fp32 exp but for vanishingly rare
+// double-rounding cases); the add and the divide are IEEE fp32.  Every GEMM
+// epilogue uses this one definition.
+__device__ __forceinline__ float silu_f32(float g) {
+    const float e = (float)exp(-(double)g);
+    const float den = 1.0f + e;
+    return g / den;
+}
+
 enum Epilogue : int {
     EPI_DENSE_F32 = 0,  // out[m][n] = ((float)acc * s_a[m]) * s_b[n]
     EPI_DENSE_I32 = 1,  // out[m][n] = acc
@@ -56,6 +66,13 @@ hipError_t launch_pack_weights(const int8_t* w, int64_t groups, int64_t n, int64
 // max_m_tiles: an upper bound of the number of BM-row tiles (grouped: over all
 // experts); surplus workgroups exit on the device.
 hipError_t launch_gemm(int epi, const GemmParams& p, int64_t max_m_tiles, hipStream_t s);
+
+// Grouped GEMM for segments of a few rows (decode): 16-row blocks, no LDS,
+// operands loaded straight into registers.  max_row_blocks bounds the number
+// of 16-row blocks over all groups; the routing's m-tile prefix must use
+// SKINNY_BM.  Gate-up and down epilogues only.
+constexpr int SKINNY_BM = 16;
+hipError_t launch_gemm_skinny(int epi, const GemmParams& p, int64_t max_row_blocks, hipStream_t s);
 
 // Number of partial sums the router GEMM splits H into (so a small token
 // count still yields enough workgroups); the workspace holds S*T*E floats.

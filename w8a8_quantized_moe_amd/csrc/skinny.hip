@@ -1,0 +1,167 @@
+// Grouped INT8 GEMM for expert segments of a few rows (the decode regime).
+//
+// Same computation and epilogues as the tiled grouped GEMM (gemm.hip): the
+// int32 accumulators of x_q . W^T per expert ("W8A8 quantisation of
+// MiniMax-M3 on K100AI", sec. 2.1 and 3.1), with the per-token x per-channel
+// scale product, SiLU(gate) * up ("DeepSeek V4 '950' unified FP8 dataflow",
+// sec. 2.3), or the routing-weighted scatter ("Tencent Hunyuan AI Infra ...
+// Hopper", sec. 1.3) fused into the epilogue.
+//
+// When a batch has only a handful of rows per expert the layer is bound by
+// streaming the experts' weights from HBM, and the tiled kernel's 256-row LDS
+// tiles mostly carry padding.  Here every wave works alone on a 16-row x
+// (16*FN)-column block:
+//  * no LDS and no barriers: the packed weight fragments (one contiguous
+//    1 KiB per wave instruction, already in MFMA register order) and the
+//    gathered activation fragment go straight from global memory into
+//    registers;
+//  * D stages of loads stay in flight per wave, and many waves per CU keep
+//    enough bytes in flight to cover the memory latency;
+//  * work items are (expert, 16-row block, column block) with the row blocks
+//    of an expert fastest, so the blocks that share a weight slice run side by
+//    side and share its reads in L2.
+#include "internal.h"
+
+namespace w8a8 {
+namespace {
+
+constexpr int SK_WAVES = 4;  // waves per workgroup (independent of each other)
+
+template <int EPI, int FN, int D>
+__global__ __launch_bounds__(SK_WAVES * 64) void gemm_skinny(GemmParams p) {
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * SK_WAVES + (threadIdx.x >> 6);
+    const int NC = p.N / (16 * FN);  // column blocks
+    const int64_t total = (int64_t)p.mt_prefix[p.G] * NC;
+    if (item >= total) return;  // wave-uniform
+
+    // expert of this item: the largest g with mt_prefix[g] <= item / NC
+    const int64_t mtL = item / NC;
+    int lo = 0, hi = p.G;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.mt_prefix[mid] <= mtL) lo = mid; else hi = mid;
+    }
+    const int g = lo;
+    const int mcount = p.mt_prefix[g + 1] - p.mt_prefix[g];
+    const int64_t local = item - (int64_t)p.mt_prefix[g] * NC;
+    const int rb = (int)(local % mcount);
+    const int cb = (int)(local / mcount);
+    const int64_t row0 = p.seg_offsets[g] + (int64_t)rb * SKINNY_BM;
+    const int64_t row_end = min(row0 + SKINNY_BM, (int64_t)p.seg_offsets[g + 1]);
+
+    // MFMA A operand: lane l holds row l%16 and the 16-byte k-chunk l/16 of
+    // each 64-byte k step; rows past the segment read a valid row (dropped)
+    const int K = p.K;
+    const int64_t KB = K / 64;
+    int64_t r = row0 + (lane & 15);
+    if (r >= row_end) r = row0;
+    int64_t src_row = r;
+    if (EPI == EPI_GATE_UP)
+        src_row = min(max((int64_t)(p.sorted_assign[r] / p.topk), (int64_t)0), p.a_rows - 1);
+    const int8_t* a_ptr = p.A + src_row * K + (lane >> 4) * 16;
+    // packed weights: fragment (channel block nb, k step kb) at
+    // g*b_group_bytes + (nb*KB + kb)*1024, lane l's 16 bytes at l*16
+    const int8_t* b_ptr = p.B + (int64_t)g * p.b_group_bytes + (int64_t)cb * FN * KB * 1024 + lane * 16;
+
+    const int nk = (int)KB;
+    v4i ra[D], rbf[D][FN];
+    auto load = [&](int slot, int ks) {
+        ra[slot] = *reinterpret_cast<const v4i*>(a_ptr + (int64_t)ks * 64);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            rbf[slot][j] = __builtin_nontemporal_load(
+                reinterpret_cast<const v4i*>(b_ptr + ((int64_t)j * KB + ks) * 1024));
+    };
+    // prologue without branches (a slot past the last stage reloads the last
+    // stage and is never multiplied), slot by slot as in the loop, so the
+    // compiler's wait counts stay exact at the loop entry
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        load(d, min(d, nk - 1));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    v4i acc[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[j] = v4i{0, 0, 0, 0};
+    auto mfma = [&](int slot) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[slot], rbf[slot][j], acc[j], 0, 0, 0);
+    };
+    // steady state without branches, so the compiler waits only for the
+    // oldest stage (D-1 stages of loads stay in flight)
+    int ks = 0;
+    for (; ks + 2 * D <= nk; ks += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            mfma(d);
+            load(d, ks + d + D);
+            // keep the loads in stage order (the scheduler would otherwise
+            // bunch them, and the waits would drain the whole pipeline)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // tail: the last D to 2D-1 stages
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        if (ks + d < nk) {
+            mfma(d);
+            if (ks + d + D < nk) load(d, ks + d + D);
+        }
+    }
+    ks += D;
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        if (ks + d < nk) mfma(d);
+
+    // epilogue: lane l, register q of block j holds row (l/16)*4 + q and
+    // channel-block column l%16
+    const int col_in_blk = lane & 15;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int64_t grow = row0 + (lane >> 4) * 4 + q;
+        if (grow >= row_end) continue;
+        if (EPI == EPI_GATE_UP) {
+            // column blocks alternate gate / up for the same 16 channels
+            const int64_t t = min(max((int64_t)(p.sorted_assign[grow] / p.topk), (int64_t)0), p.a_rows - 1);
+            const float sx = p.s_a[t];
+#pragma unroll
+            for (int jp = 0; jp < FN / 2; ++jp) {
+                const int ch = (cb * FN / 2 + jp) * 16 + col_in_blk;
+                const float gv = ((float)acc[2 * jp][q] * sx) * p.s_b[(int64_t)g * 2 * p.I + ch];
+                const float uv = ((float)acc[2 * jp + 1][q] * sx) * p.s_b[(int64_t)g * 2 * p.I + p.I + ch];
+                p.out_f32[grow * p.I + ch] = silu_f32(gv) * uv;
+            }
+        } else {  // EPI_DOWN
+            const int64_t a = min(max((int64_t)p.sorted_assign[grow], (int64_t)0), p.M - 1);
+            const float sh = p.s_a[grow];
+            const float w = p.route_w[a];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int col = (cb * FN + j) * 16 + col_in_blk;
+                const float dq = ((float)acc[j][q] * sh) * p.s_b[(int64_t)g * p.N + col];
+                p.out_f32[a * p.N + col] = w * dq;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_skinny(int epi, const GemmParams& p, int64_t max_row_blocks, hipStream_t s) {
+    constexpr int FN = 4, D = 4;
+    if (p.N % (16 * FN) != 0 || !p.seg_offsets) return hipErrorInvalidValue;
+    const int64_t items = max_row_blocks * (p.N / (16 * FN));
+    if (items == 0) return hipSuccess;
+    const dim3 grid((unsigned)((items + SK_WAVES - 1) / SK_WAVES)), block(SK_WAVES * 64);
+    switch (epi) {
+        case EPI_GATE_UP: gemm_skinny<EPI_GATE_UP, FN, D><<<grid, block, 0, s>>>(p); break;
+        case EPI_DOWN: gemm_skinny<EPI_DOWN, FN, D><<<grid, block, 0, s>>>(p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace w8a8
