@@ -120,15 +120,31 @@ def copy_calibration(torch, nbytes=1 << 30, reps=5):
                       "gbps_read_plus_write": round(2 * nbytes / dt / 1e9, 1)}), flush=True)
 
 
-def stage_work(T, H, E, k, I):
-    """Algorithmic work per launch of each stage: (bound, amount, unit, peak)."""
+def stage_work(T, H, E, k, I, touched):
+    """Algorithmic work per launch of each stage: (bound, amount, unit, peak).
+
+    The grouped GEMMs count both their int8 ops and their algorithmic bytes
+    (the touched experts' weights and scales once, the activation rows each
+    assignment reads, the output written); the bound is the one their
+    arithmetic intensity selects against the ridge point peak_ops/peak_bytes.
+    """
     A = T * k
+    gu_ops, dn_ops = 2 * A * H * 2 * I, 2 * A * I * H
+    gu_bytes = touched * (2 * I * H + 8 * I) + A * H + 4 * T + 4 * A * I
+    dn_bytes = touched * (H * I + 4 * H) + A * I + 8 * A + 4 * A * H
+    ridge = PEAK_INT8_OPS / PEAK_HBM
+
+    def gemm(ops, nbytes):
+        if ops / nbytes >= ridge:
+            return ("mfma", ops, "TOP/s", PEAK_INT8_OPS)
+        return ("hbm", nbytes, "GB/s", PEAK_HBM)
+
     return {
         "quant": ("hbm", 4 * T * H + T * H + 4 * T, "GB/s", PEAK_HBM),
         "route": ("mfma", 2 * T * H * E, "TFLOP/s", PEAK_FP32_MFMA),
-        "gate_up": ("mfma", 2 * A * H * 2 * I, "TOP/s", PEAK_INT8_OPS),
+        "gate_up": gemm(gu_ops, gu_bytes),
         "requant": ("hbm", 4 * A * I + A * I + 4 * A, "GB/s", PEAK_HBM),
-        "down": ("mfma", 2 * A * I * H, "TOP/s", PEAK_INT8_OPS),
+        "down": gemm(dn_ops, dn_bytes),
         "combine": ("hbm", 4 * A * H + 4 * T * H, "GB/s", PEAK_HBM),
     }
 
@@ -295,7 +311,7 @@ def main():
 
     counts = w8.workspace_views(ws, T, H, E, k, I)["expert_counts"].cpu()
     touched = int((counts > 0).sum())
-    work = stage_work(T, H, E, k, I)
+    work = stage_work(T, H, E, k, I, touched)
     dom = max(stages, key=lambda s: stage_ms[s])
     bound, amount, unit, peak = work[dom]
     scale = 1e9 if unit == "GB/s" else 1e12

@@ -282,6 +282,11 @@ EDGE = [
     dict(T=300, H=256, E=64, k=2, I=128, bias="zipf"),
     dict(T=129, H=384, E=5, k=3, I=384),
     dict(T=65, H=512, E=3, k=1, I=640, weights="fp32"),
+    # few rows per expert (register-fed skinny kernel): skewed routing puts
+    # several 16-row blocks on the hot experts; A = 4E exactly; K of 6 steps
+    dict(T=120, H=256, E=64, k=2, I=256, bias="zipf"),
+    dict(T=128, H=256, E=64, k=2, I=128, bias="zipf"),
+    dict(T=20, H=384, E=8, k=1, I=384),
 ]
 
 

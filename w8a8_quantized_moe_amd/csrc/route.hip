@@ -135,144 +135,6 @@ __global__ __launch_bounds__(256) void router_partial(const float* __restrict__ 
             }
 }
 
-// The same partial sums on the bf16 matrix cores.  Every fp32 operand is
-// split exactly into three bf16 terms, v = hi + mid + lo (hi = bf16(v),
-// mid = bf16(v - hi), lo = bf16(v - hi - mid); each difference is exact in
-// fp32), and x.w is formed from the six products down to the 2^-16 order:
-//   hi*hi + hi*mid + mid*hi + hi*lo + lo*hi + mid*mid,
-// dropping mid*lo, lo*mid and lo*lo (each below 2^-25 of |x*w|).  The bf16
-// products are exact and the MFMA accumulates in fp32, so the logits keep
-// fp32 accuracy at 16x the fp32 matrix rate per term ("Tencent Hunyuan AI
-// Infra ... Hopper", sec. 1.2, splits the router operands the same way, with
-// two terms for bf16 activations).
-// Tile: 64 tokens x all experts (E padded to 64*EB) per workgroup, K in
-// steps of 32; the three planes of both operands are split on the fly into
-// a double-buffered LDS tile (rows padded to 80 bytes: conflict-free reads).
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-constexpr int SROW = 80;  // bytes per LDS row: 32 bf16 + 16 padding
-
-__device__ __forceinline__ void split3(const float (&v)[8], bf16x8& hi, bf16x8& mid, bf16x8& lo) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const __bf16 h = (__bf16)v[q];
-        const float r1 = v[q] - (float)h;
-        const __bf16 m = (__bf16)r1;
-        const float r2 = r1 - (float)m;
-        hi[q] = h;
-        mid[q] = m;
-        lo[q] = (__bf16)r2;
-    }
-}
-
-template <int EB>
-__global__ __launch_bounds__(256) void router_split(const float* __restrict__ x,
-                                                    const float* __restrict__ wr,
-                                                    const float* __restrict__ bias, int T, int H,
-                                                    int E, int ksplit_len,
-                                                    float* __restrict__ partial) {
-    constexpr int EP = 64 * EB;
-    constexpr int APL = RBM * SROW, BPL = EP * SROW;  // plane bytes
-    constexpr int BUF = 3 * APL + 3 * BPL;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BUF];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int m0 = blockIdx.x * RBM;
-    const int kbeg = blockIdx.y * ksplit_len;
-    const int nstage = ksplit_len / RBK;
-
-    // global loads of one stage: thread t takes row t/4 (and t/4 + 64q of the
-    // weights), 8 consecutive k at (t%4)*8
-    const int lr = tid >> 2, lk = (tid & 3) * 8;
-    float xv[8], wv[EB][8];
-    auto gload = [&](int k0) {
-        const int t = m0 + lr;
-        const float* xs = x + (int64_t)min(t, T - 1) * H + k0 + lk;
-        const float4 a0 = *reinterpret_cast<const float4*>(xs);
-        const float4 a1 = *reinterpret_cast<const float4*>(xs + 4);
-        const bool tv = t < T;
-        xv[0] = tv ? a0.x : 0.f; xv[1] = tv ? a0.y : 0.f; xv[2] = tv ? a0.z : 0.f; xv[3] = tv ? a0.w : 0.f;
-        xv[4] = tv ? a1.x : 0.f; xv[5] = tv ? a1.y : 0.f; xv[6] = tv ? a1.z : 0.f; xv[7] = tv ? a1.w : 0.f;
-#pragma unroll
-        for (int q = 0; q < EB; ++q) {
-            const int e = lr + 64 * q;
-            const float* ws = wr + (int64_t)min(e, E - 1) * H + k0 + lk;
-            const float4 b0 = *reinterpret_cast<const float4*>(ws);
-            const float4 b1 = *reinterpret_cast<const float4*>(ws + 4);
-            const bool ev = e < E;
-            wv[q][0] = ev ? b0.x : 0.f; wv[q][1] = ev ? b0.y : 0.f; wv[q][2] = ev ? b0.z : 0.f; wv[q][3] = ev ? b0.w : 0.f;
-            wv[q][4] = ev ? b1.x : 0.f; wv[q][5] = ev ? b1.y : 0.f; wv[q][6] = ev ? b1.z : 0.f; wv[q][7] = ev ? b1.w : 0.f;
-        }
-    };
-    auto sstore = [&](int buf) {
-        uint8_t* base = lds + buf * BUF;
-        bf16x8 h, m, l;
-        split3(xv, h, m, l);
-        *reinterpret_cast<bf16x8*>(base + 0 * APL + lr * SROW + lk * 2) = h;
-        *reinterpret_cast<bf16x8*>(base + 1 * APL + lr * SROW + lk * 2) = m;
-        *reinterpret_cast<bf16x8*>(base + 2 * APL + lr * SROW + lk * 2) = l;
-#pragma unroll
-        for (int q = 0; q < EB; ++q) {
-            split3(wv[q], h, m, l);
-            const int r = lr + 64 * q;
-            *reinterpret_cast<bf16x8*>(base + 3 * APL + 0 * BPL + r * SROW + lk * 2) = h;
-            *reinterpret_cast<bf16x8*>(base + 3 * APL + 1 * BPL + r * SROW + lk * 2) = m;
-            *reinterpret_cast<bf16x8*>(base + 3 * APL + 2 * BPL + r * SROW + lk * 2) = l;
-        }
-    };
-
-    v4f acc[4][EB];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < EB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    gload(kbeg);
-    sstore(0);
-    __syncthreads();
-    // MFMA operands: lane l holds row l%16 and k elements (l/16)*8 .. +7
-    const int frow = lane & 15, fk = (lane >> 4) * 16;
-    for (int st = 0; st < nstage; ++st) {
-        const int buf = st & 1;
-        if (st + 1 < nstage) gload(kbeg + (st + 1) * RBK);
-        const uint8_t* base = lds + buf * BUF;
-        bf16x8 a[3][4], b[3][EB];
-#pragma unroll
-        for (int pl = 0; pl < 3; ++pl) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a[pl][i] = *reinterpret_cast<const bf16x8*>(base + pl * APL + (i * 16 + frow) * SROW + fk);
-#pragma unroll
-            for (int j = 0; j < EB; ++j)
-                b[pl][j] = *reinterpret_cast<const bf16x8*>(base + 3 * APL + pl * BPL +
-                                                            ((w * EB + j) * 16 + frow) * SROW + fk);
-        }
-        // term order: the small terms first, the hi*hi term last
-        constexpr int TA[6] = {1, 0, 2, 0, 1, 0};  // x plane of each term
-        constexpr int TB[6] = {1, 2, 0, 1, 0, 0};  // w plane of each term
-#pragma unroll
-        for (int tm = 0; tm < 6; ++tm)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < EB; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[TA[tm]][i], b[TB[tm]][j], acc[i][j], 0, 0, 0);
-        if (st + 1 < nstage) sstore(buf ^ 1);
-        __syncthreads();
-    }
-    float* out = partial + (int64_t)blockIdx.y * T * E;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < EB; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = m0 + i * 16 + (lane >> 4) * 4 + r;
-                const int e = (w * EB + j) * 16 + (lane & 15);
-                // a single split writes the finished logits (bias added once)
-                if (t < T && e < E)
-                    out[(int64_t)t * E + e] = (bias && gridDim.y == 1) ? acc[i][j][r] + bias[e] : acc[i][j][r];
-            }
-}
-
 // logits[t][e] = (sum of the S split partials, in split order) + bias[e]
 __global__ __launch_bounds__(256) void router_reduce(const float* __restrict__ partial, int S,
                                                      const float* __restrict__ bias, int T, int E,
