@@ -130,8 +130,10 @@ ORACLE_API void oracle_router_logits(const float* x, const float* wr, const floa
 /* ------------------------------------------------------------------------ */
 /* Gate -> top-k -> weights, [HUNYUAN] sec. 1.3 stage list.  Steps:          */
 /*  1. softmax over all E experts (fp64, max-subtracted);                   */
-/*  2. pick the k largest probabilities, in descending order, a tie going   */
-/*     to the lower expert index;                                           */
+/*  2. pick the k experts of largest logit (the order of the probabilities, */
+/*     which softmax preserves, but decided on the logits so that           */
+/*     probabilities that underflow to zero do not tie), in descending      */
+/*     order, a tie going to the lower expert index;                        */
 /*  3. renormalise the k picked probabilities to sum to one.                */
 /* ------------------------------------------------------------------------ */
 ORACLE_API void oracle_topk_softmax(const double* logits, int64_t T, int64_t E, int64_t k,
@@ -160,7 +162,7 @@ ORACLE_API void oracle_topk_softmax(const double* logits, int64_t T, int64_t E, 
                 int64_t best = -1;
                 for (int64_t e = 0; e < E; ++e) {
                     if (taken[e]) continue;
-                    if (best < 0 || p[e] > p[best]) best = e; /* strict: tie keeps lower index */
+                    if (best < 0 || l[e] > l[best]) best = e; /* strict: tie keeps lower index */
                 }
                 taken[best] = 1;
                 ids[t * k + j] = (int32_t)best;
