@@ -298,6 +298,22 @@ def test_moe_edge_cases(w8, case):
     check_moe(w8, inp)
 
 
+def test_moe_router_wide_dynamic_range(w8):
+    """Router operands whose values span 2^-20 .. 2^20: column h of x is scaled
+    by 2^s_h and column h of the router matrix by 2^-s_h, so every product
+    x*w (and the logits) keeps its size while each operand row crosses forty
+    binades.  The bf16 three-term split of the router GEMM must still give
+    logits within the fp32 error bound of the fp64 oracle, with exact routing
+    away from near ties (all checked in check_moe)."""
+    inp = synth.moe_inputs("edge", device="cuda", T=192, H=512, E=40, k=4, I=128, n_outlier=2,
+                           outlier_scale=20.0, bf16_x=False, bias="zero", weights="int8")
+    g = torch.Generator(device="cuda").manual_seed(11)
+    sh = torch.randint(-20, 21, (inp["H"],), generator=g, device="cuda").float()
+    inp["x"] = (inp["x"] * torch.exp2(sh)[None, :]).contiguous()
+    inp["wr"] = (inp["wr"] * torch.exp2(-sh)[None, :]).contiguous()
+    check_moe(w8, inp)
+
+
 def test_moe_zero_input_gives_zero(w8):
     inp = synth.moe_inputs("edge0", device="cuda", T=50, H=256, E=8, k=2, I=256, n_outlier=0,
                            outlier_scale=1.0, bf16_x=False, bias="zero", weights="int8")

@@ -28,6 +28,37 @@ __device__ __forceinline__ float silu_f32(float g) {
     return g / den;
 }
 
+// ---- copy-pipeline helpers shared by the LDS-staged kernels ----
+#define LDS_AS __attribute__((address_space(3)))
+
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without the implied memory fence of __syncthreads (which
+// would wait for every load in flight, i.e. drain the copy pipeline); the
+// "memory" clobber keeps the compiler from moving LDS accesses across it.
+// Visibility of a copied stage is established by the vmcnt wait before it.
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+
+// One wave-wide 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4):
+// lane l's 16 bytes land at lds_wave_base + 16*l; M0 carries the LDS base.
+// Issued through inline asm so that the compiler does not model the LDS write:
+// it would otherwise drain the whole copy pipeline (vmcnt(0)) before every
+// LDS read it cannot prove disjoint.  The ring's hazards are handled by hand
+// (explicit vmcnt waits before the workgroup barrier).  Nothing else in the
+// kernel uses M0 (no LDS DMA builtins, no dynamic register indexing).
+__device__ __forceinline__ void dma16(const int8_t* gsrc, const int8_t* lds_wave_base) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const LDS_AS int8_t*)lds_wave_base);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gsrc), "s"(lds)
+                 : "memory", "m0");
+}
+
 enum Epilogue : int {
     EPI_DENSE_F32 = 0,  // out[m][n] = ((float)acc * s_a[m]) * s_b[n]
     EPI_DENSE_I32 = 1,  // out[m][n] = acc

@@ -9,10 +9,11 @@
 // for the routing reorder).
 //
 // Kernels, all on the caller's stream, no host synchronisation:
-//   router_partial  fp32 MFMA GEMM (v_mfma_f32_16x16x4_f32), 64-token x
-//                   all-expert tiles (activations read once), optionally
-//                   split along H into S partial sums so small token counts
-//                   still fill the GPU;
+//   router_bf16x3   the fp32 router GEMM on the bf16 matrix cores at fp32
+//                   accuracy (each operand split exactly into three bf16
+//                   terms), 64-token x all-expert tiles (activations read
+//                   once), optionally split along H into S partial sums so
+//                   small token counts still fill the GPU;
 //   router_reduce   (split only) sums the S partials in split order (a fixed,
 //                   deterministic order) and adds the bias;
 //   topk_count      per 64-token chunk: picks the top-k by wave arg-max rounds
@@ -26,109 +27,207 @@
 //                   prefix of m-tiles per expert for the grouped GEMMs;
 //   scatter         sorted_assign[offset[e] + chunk_base + rank] = t*k + j.
 // The resulting order inside a segment is ascending token order.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace w8a8 {
 namespace {
 
-constexpr int RBM = 64, RBK = 32, RPAD = 4;
+constexpr int RBM = 64, RBK = 32;
 constexpr int TOPK_THREADS = 1024;  // 16 waves: 4 tokens of a 64-token chunk each
 
-// partial[s][t][e] = sum over h in split s of x[t][h] * wr[e][h]   (fp32 MFMA);
-// with a single split the output is the logits themselves, bias included.
-// One workgroup: 64 tokens x all experts (E padded to 64*EB), so the
-// activations are read once; wave w owns experts [16*EB*w, 16*EB*(w+1)).
-// K advances 32 per stage through a double-buffered, k-major LDS tile.
-template <int EB>
-__global__ __launch_bounds__(256) void router_partial(const float* __restrict__ x,
-                                                      const float* __restrict__ wr,
-                                                      const float* __restrict__ bias, int T, int H,
-                                                      int E, int ksplit_len,
-                                                      float* __restrict__ partial) {
-    constexpr int EP = 64 * EB;  // padded expert count
-    constexpr int AW = RBM + RPAD, BW = EP + RPAD;
-    __shared__ float As[2][RBK][AW];
-    __shared__ float Bs[2][RBK][BW];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int m0 = blockIdx.x * RBM;
-    const int split = blockIdx.y;
-    const int kbeg = split * ksplit_len;
-    const int nstage = ksplit_len / RBK;
+// partial[s][t][e] = sum over h in split s of x[t][h] * wr[e][h] on the bf16
+// matrix cores at fp32 accuracy; with a single split the output is the logits
+// themselves, bias included.
+//
+// "Tencent Hunyuan AI Infra ... Hopper", sec. 1.2, runs the router on tensor
+// cores by splitting each operand into a high bf16 part and a residual.  Here
+// both fp32 operands are split exactly into three bf16 terms,
+//   v = v0 + v1 + v2,  v0 = bf16(v), v1 = bf16(v - v0), v2 = bf16(v - v0 - v1)
+// (each difference is exact in fp32, and the three terms carry all 24 bits of
+// the significand), and x.w is the sum of the six products whose terms have
+// index sum <= 2:
+//   x0*w0 + x0*w1 + x1*w0 + x0*w2 + x1*w1 + x2*w0.
+// The three dropped products are each below 2^-25 |x*w|, bf16 x bf16 products
+// are exact, and the matrix cores accumulate in fp32, so the logits keep fp32
+// accuracy while the arithmetic runs at the bf16 rate (16x the fp32 rate, for
+// 6x the products).
+//
+// Workgroup: 64 tokens x 64*EB experts, 8 waves = 2 token halves x 4 expert
+// quarters; a wave owns 32 tokens x 16*EB experts (2 x EB blocks of
+// v_mfma_f32_16x16x32_bf16).  K advances 32 per stage.  Both fp32 tiles move
+// global -> LDS by direct copies (one wave instruction: 8 rows x 128 bytes),
+// NS stages deep; chunk c of a row r lands in slot c ^ (r % 8), so the
+// fragment reads (16 rows, one 16-byte chunk each per instruction) are
+// conflict-free.  The split into bf16 terms happens in registers right before
+// the MFMAs.  MFMA operand layout: lane l holds row (A) or column (B) l%16
+// and k elements (l/16)*8 .. +7.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-    // global tile loads: A 64x32 (2 float4 per thread), B EPx32 (2*EB float4 per thread)
-    float4 ra0, ra1, rb[2 * EB];
-    const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
-#define ROUTER_GLOAD(k0)                                                                          \
-    do {                                                                                          \
-        {                                                                                         \
-            const int t_ = m0 + (tid >> 3), t1_ = m0 + ((tid + 256) >> 3);                        \
-            ra0 = *reinterpret_cast<const float4*>(x + (int64_t)min(t_, T - 1) * H + (k0) + (tid & 7) * 4); \
-            ra1 = *reinterpret_cast<const float4*>(x + (int64_t)min(t1_, T - 1) * H + (k0) + (tid & 7) * 4); \
-            if (t_ >= T) ra0 = zero4;                                                             \
-            if (t1_ >= T) ra1 = zero4;                                                            \
-        }                                                                                         \
-        _Pragma("unroll") for (int i = 0; i < 2 * EB; ++i) {                                      \
-            const int c_ = tid + i * 256;                                                         \
-            const int e_ = c_ >> 3;                                                               \
-            rb[i] = *reinterpret_cast<const float4*>(wr + (int64_t)min(e_, E - 1) * H + (k0) + (c_ & 7) * 4); \
-            if (e_ >= E) rb[i] = zero4;                                                           \
-        }                                                                                         \
-    } while (0)
-#define ROUTER_SSTORE(buf)                                                                        \
-    do {                                                                                          \
-        const int k4_ = (tid & 7) * 4, r0_ = tid >> 3, r1_ = (tid + 256) >> 3;                    \
-        As[buf][k4_ + 0][r0_] = ra0.x; As[buf][k4_ + 1][r0_] = ra0.y;                             \
-        As[buf][k4_ + 2][r0_] = ra0.z; As[buf][k4_ + 3][r0_] = ra0.w;                             \
-        As[buf][k4_ + 0][r1_] = ra1.x; As[buf][k4_ + 1][r1_] = ra1.y;                             \
-        As[buf][k4_ + 2][r1_] = ra1.z; As[buf][k4_ + 3][r1_] = ra1.w;                             \
-        _Pragma("unroll") for (int i = 0; i < 2 * EB; ++i) {                                      \
-            const int c_ = tid + i * 256;                                                         \
-            const int e_ = c_ >> 3;                                                               \
-            Bs[buf][k4_ + 0][e_] = rb[i].x; Bs[buf][k4_ + 1][e_] = rb[i].y;                       \
-            Bs[buf][k4_ + 2][e_] = rb[i].z; Bs[buf][k4_ + 3][e_] = rb[i].w;                       \
-        }                                                                                         \
-    } while (0)
-
-    v4f acc[4][EB];
+__device__ __forceinline__ void split3(const float4& a, const float4& b, bf16x8 (&pl)[3]) {
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int q = 0; q < 8; ++q) {
+        float r = v[q];
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            const __bf16 h = (__bf16)r;
+            pl[t][q] = h;
+            r -= (float)h;
+        }
+    }
+}
+
+template <int EB>
+struct RouterBf16Cfg {
+    static constexpr int XBLK = RBM / 8;                    // 1 KiB copy blocks of x per stage
+    static constexpr int BBLK = 64 * EB / 8;                // ... of router rows
+    static constexpr int DPW = (XBLK + BBLK) / 8;           // copies per wave per stage
+    static constexpr int STAGE = (XBLK + BBLK) * 1024;      // bytes per stage
+    static constexpr int NS = (163840 / STAGE) < 6 ? (163840 / STAGE) : 6;
+};
+
+template <int EB>
+__global__ __launch_bounds__(512) void router_bf16x3(const float* __restrict__ x,
+                                                     const float* __restrict__ wr,
+                                                     const float* __restrict__ bias, int T, int H,
+                                                     int E, int ksplit_len,
+                                                     float* __restrict__ partial) {
+    using C = RouterBf16Cfg<EB>;
+    constexpr int NS = C::NS, DPW = C::DPW, STAGE = C::STAGE, XBLK = C::XBLK;
+    static_assert(NS >= 3, "at least one stage in flight beyond the pair being read");
+    __shared__ __attribute__((aligned(1024))) int8_t smem[NS * STAGE];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wt = w >> 2, we = w & 3;
+    const int m0 = blockIdx.x * RBM;
+    const int kbeg = blockIdx.y * ksplit_len;
+    const int nk = ksplit_len / RBK;
+
+    // copy sources: wave w moves blocks w, w+8, ... of every stage; block b < XBLK
+    // holds x rows 8b..8b+7, the rest router rows; lane l fetches chunk
+    // (l%8) ^ (l/8) of row l/8 of its block.  Rows past T or E repeat the last
+    // row (their sums are dropped).
+    const int8_t* src[DPW];
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) {
+        const int b = w + 8 * i;
+        const int chunk = (lane & 7) ^ (lane >> 3);
+        if (b < XBLK) {
+            const int t = min(m0 + b * 8 + (lane >> 3), T - 1);
+            src[i] = reinterpret_cast<const int8_t*>(x + (int64_t)t * H + kbeg + chunk * 4);
+        } else {
+            const int e = min((b - XBLK) * 8 + (lane >> 3), E - 1);
+            src[i] = reinterpret_cast<const int8_t*>(wr + (int64_t)e * H + kbeg + chunk * 4);
+        }
+    }
+    auto issue = [&](int ks) {
+        const int8_t* stage = smem + (ks % NS) * STAGE;
+#pragma unroll
+        for (int i = 0; i < DPW; ++i) dma16(src[i] + (int64_t)ks * RBK * 4, stage + (w + 8 * i) * 1024);
+    };
+    // Fragments: NF = 2 + EB per stage (A rows of this wave's two 16-token
+    // blocks, then B rows of its EB 16-expert blocks).  Fragment f reads row
+    // r's chunks 2*(l/16) and 2*(l/16)+1, at slots chunk ^ (r % 8).
+    constexpr int NF = 2 + EB;
+    const int frow = lane & 15, fc = (lane >> 4) * 2;
+    auto read_raw = [&](int ks, float4 (&raw)[NF][2]) {
+        const int8_t* stage = smem + (ks % NS) * STAGE;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            const int row = f < 2 ? wt * 32 + f * 16 + frow : (we * EB + (f - 2)) * 16 + frow;
+            const int8_t* rp = stage + (f < 2 ? 0 : XBLK * 1024) + row * 128;
+            raw[f][0] = *reinterpret_cast<const float4*>(rp + ((fc ^ (row & 7)) * 16));
+            raw[f][1] = *reinterpret_cast<const float4*>(rp + (((fc + 1) ^ (row & 7)) * 16));
+        }
+    };
+
+    v4f acc[2][EB];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < EB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    ROUTER_GLOAD(kbeg);
-    ROUTER_SSTORE(0);
-    __syncthreads();
-    for (int st = 0; st < nstage; ++st) {
-        const int buf = st & 1;
-        if (st + 1 < nstage) ROUTER_GLOAD(kbeg + (st + 1) * RBK);
+    // planes of the stage whose MFMAs run next: pa[i][term], pb[j][term]
+    bf16x8 pa[2][3], pb[EB][3];
+    // term order: the small products first, x0*w0 last
+    constexpr int TA[6] = {1, 0, 2, 0, 1, 0};
+    constexpr int TB[6] = {1, 2, 0, 1, 0, 0};
+    // Stage ks's MFMAs (six terms) run from pa/pb while stage ks+1's fragments
+    // (NEXT) come in from LDS and are split, one fragment after each term.
+    auto step = [&](int ks_next, auto next_tag) {
+        constexpr bool NEXT = decltype(next_tag)::value;
+        float4 raw[NF][2];
+        bf16x8 na[2][3], nb[EB][3];
+        if (NEXT) read_raw(ks_next, raw);
 #pragma unroll
-        for (int kk = 0; kk < RBK / 4; ++kk) {
-            const int kr = kk * 4 + (lane >> 4);
-            float a[4], bb[EB];
+        for (int tm = 0; tm < 6; ++tm) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = As[buf][kr][i * 16 + (lane & 15)];
-#pragma unroll
-            for (int j = 0; j < EB; ++j) bb[j] = Bs[buf][kr][(w * EB + j) * 16 + (lane & 15)];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < EB; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], bb[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[i][TA[tm]], pb[j][TB[tm]],
+                                                                        acc[i][j], 0, 0, 0);
+            if (NEXT && tm < NF) {
+                if (tm < 2) split3(raw[tm][0], raw[tm][1], na[tm]);
+                else split3(raw[tm][0], raw[tm][1], nb[tm < 2 ? 0 : tm - 2]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (st + 1 < nstage) ROUTER_SSTORE(buf ^ 1);
-        __syncthreads();
-    }
-#undef ROUTER_GLOAD
-#undef ROUTER_SSTORE
-    float* out = partial + (int64_t)split * T * E;
+        if (NEXT) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+            for (int t = 0; t < 3; ++t) {
+                pa[0][t] = na[0][t];
+                pa[1][t] = na[1][t];
+#pragma unroll
+                for (int j = 0; j < EB; ++j) pb[j][t] = nb[j][t];
+            }
+        }
+    };
+
+    // prologue: NS-1 stages in flight, stage 0 split into pa/pb
+    int issued = 0;
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < nk) {
+            issue(s);
+            ++issued;
+        }
+    if (issued == NS - 1) wait_vmcnt<(NS - 2) * DPW>();
+    else wait_vmcnt<0>();
+    barrier_nofence();
+    {
+        float4 raw[NF][2];
+        read_raw(0, raw);
+        split3(raw[0][0], raw[0][1], pa[0]);
+        split3(raw[1][0], raw[1][1], pa[1]);
+#pragma unroll
+        for (int j = 0; j < EB; ++j) split3(raw[2 + j][0], raw[2 + j][1], pb[j]);
+    }
+    int ks = 0;
+    // steady state: stage ks+1 landed (NS-3 newer stages may still fly); the
+    // barrier also retires every wave's reads of the slot refilled next
+    for (; ks + NS - 1 < nk; ++ks) {
+        wait_vmcnt<(NS - 3) * DPW>();
+        barrier_nofence();
+        issue(ks + NS - 1);
+        step(ks + 1, std::true_type{});
+    }
+    // drain: every stage is issued
+    wait_vmcnt<0>();
+    barrier_nofence();
+    for (; ks + 1 < nk; ++ks) step(ks + 1, std::true_type{});
+    step(0, std::false_type{});
+
+    float* out = partial + (int64_t)blockIdx.y * T * E;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < EB; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = m0 + i * 16 + (lane >> 4) * 4 + r;
-                const int e = (w * EB + j) * 16 + (lane & 15);
+                const int t = m0 + wt * 32 + i * 16 + (lane >> 4) * 4 + r;
+                const int e = (we * EB + j) * 16 + (lane & 15);
                 // a single split writes the finished logits (bias added once)
                 if (t < T && e < E)
                     out[(int64_t)t * E + e] = (bias && gridDim.y == 1) ? acc[i][j][r] + bias[e] : acc[i][j][r];
@@ -384,10 +483,11 @@ hipError_t launch_route(const RouteInputs& in, const RouteBuffers& b, hipStream_
         const dim3 grid((T + RBM - 1) / RBM, S);
         const int eb = (E + 63) / 64;
         float* out = (S == 1) ? b.logits : b.partial;
-        if (eb == 1) router_partial<1><<<grid, 256, 0, s>>>(in.x, in.router_w, in.router_b, T, H, E, H / S, out);
-        else if (eb == 2) router_partial<2><<<grid, 256, 0, s>>>(in.x, in.router_w, in.router_b, T, H, E, H / S, out);
-        else if (eb == 3) router_partial<3><<<grid, 256, 0, s>>>(in.x, in.router_w, in.router_b, T, H, E, H / S, out);
-        else router_partial<4><<<grid, 256, 0, s>>>(in.x, in.router_w, in.router_b, T, H, E, H / S, out);
+        const float *xx = in.x, *wr = in.router_w, *rb = in.router_b;
+        if (eb == 1) router_bf16x3<1><<<grid, 512, 0, s>>>(xx, wr, rb, T, H, E, H / S, out);
+        else if (eb == 2) router_bf16x3<2><<<grid, 512, 0, s>>>(xx, wr, rb, T, H, E, H / S, out);
+        else if (eb == 3) router_bf16x3<3><<<grid, 512, 0, s>>>(xx, wr, rb, T, H, E, H / S, out);
+        else router_bf16x3<4><<<grid, 512, 0, s>>>(xx, wr, rb, T, H, E, H / S, out);
     }
     if (S > 1) {
         const int64_t n = (int64_t)T * E;
