@@ -39,9 +39,14 @@ int64_t max_m_tiles(int64_t rows, int64_t groups, int64_t bm) {
     return bound < rows ? bound : rows;
 }
 
+// m-tile height of the grouped GEMMs: few rows per expert (decode) go to the
+// register-fed skinny kernel, which streams the weights once (16-row blocks);
+// otherwise the LDS-tiled MFMA kernel (256-row tiles)
+int moe_bm(int64_t A, int64_t E) { return A <= 4 * E ? w8a8::SKINNY_BM : w8a8::GEMM_BM; }
+
 struct MoePlan {
     w8a8_moe_workspace_layout lay;
-    size_t partial, rank, chunk_counts, chunk_base, mt_gu, mt_dn;
+    size_t partial, rank, chunk_counts, chunk_base, mt_prefix, mt_info, tile_ctr;
     int splits, nchunks;
 };
 
@@ -95,8 +100,9 @@ MoePlan plan_moe(const w8a8_moe_shape* sh) {
     p.rank = take(A * 4);
     p.chunk_counts = take((size_t)E * p.nchunks * 4);
     p.chunk_base = take((size_t)E * p.nchunks * 4);
-    p.mt_gu = take((E + 1) * 4);
-    p.mt_dn = take((E + 1) * 4);
+    p.mt_prefix = take((E + 1) * 4);
+    p.mt_info = take((size_t)max_m_tiles(A, E, moe_bm(A, E)) * sizeof(w8a8::MtInfo));
+    p.tile_ctr = take((size_t)w8a8::TILE_CTR_COUNT * w8a8::TILE_CTR_STRIDE * 4);
     L.total_bytes = off;
     return p;
 }
@@ -244,10 +250,8 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     const int T = (int)shape->T, H = (int)shape->H, E = (int)shape->E, k = (int)shape->top_k,
               I = (int)shape->I;
     const int64_t A = (int64_t)T * k;
-    // few rows per expert (decode): the weights are streamed once by the
-    // register-fed skinny kernel; otherwise the LDS-tiled MFMA kernel
-    const bool skinny = A <= 4 * (int64_t)E;
-    const int bm = skinny ? w8a8::SKINNY_BM : w8a8::GEMM_BM;
+    const int bm = moe_bm(A, E);
+    const bool skinny = bm == w8a8::SKINNY_BM;
     hipStream_t s = (hipStream_t)stream;
     char* ws = (char*)workspace;
     const w8a8_moe_workspace_layout& L = plan.lay;
@@ -260,8 +264,9 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     int8_t* h_q = (int8_t*)(ws + L.h_q);
     float* h_scale = (float*)(ws + L.h_scale);
     float* o = (float*)(ws + L.o);
-    int32_t* mt_gu = (int32_t*)(ws + plan.mt_gu);
-    int32_t* mt_dn = (int32_t*)(ws + plan.mt_dn);
+    int32_t* mt_prefix = (int32_t*)(ws + plan.mt_prefix);
+    int32_t* mt_info = (int32_t*)(ws + plan.mt_info);
+    int32_t* tile_ctr = (int32_t*)(ws + plan.tile_ctr);
 
     auto mark = [&](int i) -> w8a8_status {
         if (!events) return W8A8_OK;
@@ -274,7 +279,7 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     if (st != W8A8_OK) return st;
 
     // 2-4. router, top-k, permutation
-    w8a8::RouteInputs ri{x, wts->router_w, wts->router_b, T, H, E, k, plan.splits, bm, bm};
+    w8a8::RouteInputs ri{x, wts->router_w, wts->router_b, T, H, E, k, plan.splits, bm};
     w8a8::RouteBuffers rb{};
     rb.partial = (float*)(ws + plan.partial);
     rb.logits = (float*)(ws + L.logits);
@@ -285,8 +290,9 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     rb.rank = (int32_t*)(ws + plan.rank);
     rb.expert_counts = (int32_t*)(ws + L.expert_counts);
     rb.expert_offsets = offsets;
-    rb.mt_prefix_gu = mt_gu;
-    rb.mt_prefix_dn = mt_dn;
+    rb.mt_prefix = mt_prefix;
+    rb.mt_info = mt_info;
+    rb.tile_ctr = tile_ctr;
     rb.sorted_assign = sorted;
     if ((st = mark(1)) != W8A8_OK) return st;
     st = check_hip(w8a8::launch_route(ri, rb, s), "route");
@@ -301,7 +307,9 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     gu.N = 2 * I;
     gu.K = H;
     gu.seg_offsets = offsets;
-    gu.mt_prefix = mt_gu;
+    gu.mt_prefix = mt_prefix;
+    gu.mt_info = mt_info;
+    gu.tile_ctr = skinny ? nullptr : tile_ctr;
     gu.G = E;
     gu.sorted_assign = sorted;
     gu.topk = k;
@@ -330,7 +338,9 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     dn.N = H;
     dn.K = I;
     dn.seg_offsets = offsets;
-    dn.mt_prefix = mt_dn;
+    dn.mt_prefix = mt_prefix;
+    dn.mt_info = mt_info;
+    dn.tile_ctr = skinny ? nullptr : tile_ctr + 8 * w8a8::TILE_CTR_STRIDE;
     dn.G = E;
     dn.sorted_assign = sorted;
     dn.topk = k;

@@ -36,6 +36,7 @@
 // each weight tile is fetched once and the activations once per XCD.
 // Grouped tile counts are known only on the device (after routing): the grid
 // is sized for the worst case and surplus workgroups exit at once.
+#include <atomic>
 #include <type_traits>
 
 #include "internal.h"
@@ -59,41 +60,45 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     // (With several __shared__ objects the compiler can no longer tell the
     // copy target from other LDS data and drains the pipeline before every
     // LDS read.)
-    __shared__ __attribute__((aligned(1024))) int8_t smem[NS * STAGE + 3 * BM * 4];
+    __shared__ __attribute__((aligned(1024))) int8_t smem[NS * STAGE + 3 * BM * 4 + 16];
     float* row_scale = reinterpret_cast<float*>(smem + NS * STAGE);
     int* row_slot = reinterpret_cast<int*>(smem + NS * STAGE + BM * 4);
     float* row_w = reinterpret_cast<float*>(smem + NS * STAGE + 2 * BM * 4);
+    int* next_tile = reinterpret_cast<int*>(smem + NS * STAGE + 3 * BM * 4);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
+    const int tid0 = threadIdx.x;
 
-    // ---- logical tile of this workgroup ----
+    // ---- logical tiles: XCD x owns the contiguous range [x*per_xcd, (x+1)*per_xcd) ----
     const int64_t n_mt_dense = (p.M + BM - 1) / BM;
     const int64_t total = (p.seg_offsets ? (int64_t)p.mt_prefix[p.G] : n_mt_dense * p.VG) * p.NTV;
     const int64_t per_xcd = (total + 7) / 8;
-    const int64_t slot = blockIdx.x >> 3;
-    if (slot >= per_xcd) return;
-    const int64_t L = (int64_t)(blockIdx.x & 7) * per_xcd + slot;
-    if (L >= total) return;
 
+    // One output tile: L -> (group, m-tile, n-tile), K loop, epilogue.
+    auto process = [&](const int64_t L) {
+    // Thread indices pass through an opaque zero, so that the lane-dependent
+    // addresses below are recomputed per tile instead of being hoisted out of
+    // the tile loop (where they would stay live across the K loop and push
+    // the register count past the limit).
+    int opaque = 0;
+    asm volatile("" : "+v"(opaque));
+    const int tid = tid0 + opaque, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
+    const int wm = wave / WN, wn = wave % WN;
     int g = 0, nt;
     int64_t row0, row_end;
     if (p.seg_offsets) {
-        const int64_t mtL = L / p.NTV;  // index into the expert-major list of m-tiles
-        int lo = 0, hi = p.G;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (p.mt_prefix[mid] <= mtL) lo = mid; else hi = mid;
-        }
-        g = lo;
-        const int64_t local = L - (int64_t)p.mt_prefix[g] * p.NTV;
+        // the expert-major list of m-tiles: one table load names the expert
+        // (the routing built the table for this BM)
+        const MtInfo info = reinterpret_cast<const MtInfo*>(p.mt_info)[L / p.NTV];
+        g = info.group;
+        const int64_t local = L - (int64_t)info.first_tile * p.NTV;
         // inside an expert, m-tiles vary fastest: the m-tiles that share one
         // weight tile run side by side and share its reads in L2
-        const int mcount = p.mt_prefix[g + 1] - p.mt_prefix[g];
+        const int mcount = (info.seg_end - info.seg_start + BM - 1) / BM;
         const int mtl = (int)(local % mcount);
         nt = (int)(local / mcount);
-        row0 = p.seg_offsets[g] + (int64_t)mtl * BM;
-        row_end = min(row0 + BM, (int64_t)p.seg_offsets[g + 1]);
+        row0 = info.seg_start + (int64_t)mtl * BM;
+        row_end = min(row0 + BM, (int64_t)info.seg_end);
     } else {
         const int64_t per_vg = n_mt_dense * p.NTV;
         const int vg = (int)(L / per_vg);
@@ -328,6 +333,53 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     if (fm_active > FM / 2) run(std::integral_constant<int, FM>{});
     else if (fm_active > 0) run(std::integral_constant<int, FM / 2>{});
     else run(std::integral_constant<int, 0>{});
+    };
+
+    // Tile schedule.  Static (no counters): slot s of XCD x takes tiles s,
+    // s + slots, ... of the XCD's range (one tile per workgroup when the grid
+    // covers every tile).  Persistent (tile_ctr): each XCD's range is a queue
+    // (a counter the routing zeroed); a workgroup takes the next tile of its
+    // own XCD's queue and, once that is empty, helps drain the others, so
+    // every tile is taken exactly once whatever the number of workgroups per
+    // XCD.  The claim of the next tile is issued when a tile starts and read
+    // when it ends.
+    const int xcd = blockIdx.x & 7;
+    const int64_t slots = gridDim.x >> 3;
+    auto queue_len = [&](int xq) { return min(per_xcd, max((int64_t)0, total - (int64_t)xq * per_xcd)); };
+    auto next_after = [&](int got_own) -> int {
+        if (got_own < queue_len(xcd)) return (int)((int64_t)xcd * per_xcd + got_own);
+        for (int q = 1; q < 8; ++q) {
+            const int xq = (xcd + q) & 7;
+            if (queue_len(xq) == 0) continue;
+            const int got = atomicAdd(p.tile_ctr + TILE_CTR_STRIDE * xq, 1);
+            if (got < queue_len(xq)) return (int)((int64_t)xq * per_xcd + got);
+        }
+        return -1;
+    };
+    int64_t sl = blockIdx.x >> 3;  // static slot
+    int64_t L;
+    if (!p.tile_ctr) {
+        L = (sl < queue_len(xcd)) ? (int64_t)xcd * per_xcd + sl : -1;
+    } else {
+        if (tid0 == 0) next_tile[0] = next_after(atomicAdd(p.tile_ctr + TILE_CTR_STRIDE * xcd, 1));
+        __syncthreads();
+        // uniform: keeps every per-tile value in scalar registers
+        L = __builtin_amdgcn_readfirstlane(next_tile[0]);
+    }
+    while (L >= 0) {
+        int got = 0;
+        if (p.tile_ctr && tid0 == 0) got = atomicAdd(p.tile_ctr + TILE_CTR_STRIDE * xcd, 1);
+        process(L);
+        __syncthreads();  // every wave is done with the ring, the row metadata and next_tile
+        if (!p.tile_ctr) {
+            sl += slots;
+            L = (sl < queue_len(xcd)) ? (int64_t)xcd * per_xcd + sl : -1;
+        } else {
+            if (tid0 == 0) next_tile[0] = next_after(got);
+            __syncthreads();
+            L = __builtin_amdgcn_readfirstlane(next_tile[0]);
+        }
+    }
 }
 
 template <int BM, int BN, int WM, int WN, int NS>
@@ -347,6 +399,19 @@ hipError_t launch_tile(int epi, const GemmParams& p, int64_t blocks, hipStream_t
 
 int gemm_tile_n(int64_t N) { return (N % 256 == 0) ? 256 : 128; }
 
+int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 hipError_t launch_gemm(int epi, const GemmParams& p_in, int64_t max_m_tiles, hipStream_t s) {
     GemmParams p = p_in;
     const int bn = gemm_tile_n(p.N);
@@ -361,7 +426,13 @@ hipError_t launch_gemm(int epi, const GemmParams& p_in, int64_t max_m_tiles, hip
     }
     const int64_t max_tiles = max_m_tiles * nt_all;
     if (max_tiles == 0) return hipSuccess;
-    const int64_t blocks = 8 * ((max_tiles + 7) / 8);
+    // grouped: persistent, one workgroup per CU (the LDS ring allows one);
+    // dense: one workgroup per tile
+    int64_t blocks = 8 * ((max_tiles + 7) / 8);
+    if (p.tile_ctr) {
+        const int64_t cus = 8 * ((device_cu_count() + 7) / 8);
+        if (cus < blocks) blocks = cus;
+    }
     if (bn == 256) return launch_tile<GEMM_BM, 256, 2, 4, 4>(epi, p, blocks, s);
     return launch_tile<GEMM_BM, 128, 2, 4, 4>(epi, p, blocks, s);
 }

@@ -75,6 +75,8 @@ struct GemmParams {
     int VG, NTV;              // set by launch_gemm: column stripes and n-tiles per stripe
     const int32_t* seg_offsets;  // grouped: [G+1] segment starts, else nullptr
     const int32_t* mt_prefix;    // grouped: [G+1] prefix of m-tiles per group
+    const int32_t* mt_info;      // grouped: per m-tile {group, first m-tile of the group,
+                                 // segment start, segment end} (MtInfo)
     int G;
     const int32_t* sorted_assign;  // grouped: assignment a = t*k+j of each sorted row
     int topk;
@@ -85,7 +87,17 @@ struct GemmParams {
     int32_t* out_i32;
     int I;               // gate-up: intermediate size (N = 2I)
     int64_t a_rows;      // rows of the A operand (gate-up: T); indices are clamped to it
+    int32_t* tile_ctr;   // grouped: 8 zeroed tile counters (stride TILE_CTR_STRIDE), one
+                         // queue per XCD, for a persistent launch; nullptr: one tile
+                         // per workgroup
 };
+
+// Tile-queue counters sit 128 bytes apart; the routing zeroes TILE_CTR_COUNT of them.
+constexpr int TILE_CTR_STRIDE = 32;
+constexpr int TILE_CTR_COUNT = 16;  // gate-up queues 0..7, down queues 8..15
+
+// Compute units of the current device (queried once per device).
+int device_cu_count();
 
 // ---- launchers (each returns the launch status) ----
 hipError_t launch_quantize_rows(const float* x, int64_t rows, int64_t cols, int64_t ld, int8_t* q,
@@ -115,7 +127,7 @@ struct RouteInputs {
     const float* router_b;  // [E] or nullptr
     int T, H, E, k;
     int splits;             // router_splits(T, E, H)
-    int bm_gu, bm_dn;       // m-tile heights of the two grouped GEMMs
+    int bm;                 // m-tile height of the grouped GEMMs (GEMM_BM or SKINNY_BM)
 };
 
 struct RouteBuffers {
@@ -128,12 +140,23 @@ struct RouteBuffers {
     int32_t* rank;            // [T*k] rank of an assignment inside its chunk and expert
     int32_t* expert_counts;   // [E]
     int32_t* expert_offsets;  // [E+1]
-    int32_t* mt_prefix_gu;    // [E+1]
-    int32_t* mt_prefix_dn;    // [E+1]
+    int32_t* mt_prefix;       // [E+1] prefix of m-tiles per expert
+    int32_t* mt_info;         // [m-tiles][4] MtInfo of every m-tile
+    int32_t* tile_ctr;        // [TILE_CTR_COUNT * TILE_CTR_STRIDE] zeroed here for the GEMMs' queues
     int32_t* sorted_assign;   // [T*k]
 };
 
 hipError_t launch_route(const RouteInputs& in, const RouteBuffers& b, hipStream_t s);
+
+// One entry of the per-m-tile table the routing writes for the grouped GEMMs,
+// so that a workgroup finds its expert with one load instead of a search.
+struct MtInfo {
+    int32_t group;       // expert
+    int32_t first_tile;  // index of the expert's first m-tile
+    int32_t seg_start;   // first row of the expert's segment
+    int32_t seg_end;     // one past its last row
+};
+static_assert(sizeof(MtInfo) == 16, "one 16-byte load per m-tile");
 
 hipError_t launch_combine(const float* o, int T, int k, int H, float* y, hipStream_t s);
 

@@ -23,8 +23,9 @@
 //                   token mask per expert (a single chunk also finishes the
 //                   permutation below in the same workgroup);
 //   chunk_scan      per expert: exclusive scan of its per-chunk counts;
-//   finalize        exclusive scan over experts -> segment offsets, and the
-//                   prefix of m-tiles per expert for the grouped GEMMs;
+//   finalize        exclusive scan over experts -> segment offsets, the
+//                   prefix of m-tiles per expert and the per-m-tile table
+//                   (expert, first m-tile, segment) of the grouped GEMMs;
 //   scatter         sorted_assign[offset[e] + chunk_base + rank] = t*k + j.
 // The resulting order inside a segment is ascending token order.
 #include <type_traits>
@@ -280,6 +281,14 @@ __device__ int block_exclusive_scan(int v, int* total, int* lds /* >= NW ints */
     return base + incl - v;
 }
 
+// The m-tiles of expert e (first .. first + n - 1) all name e, its first
+// m-tile and its segment [seg_start, seg_end).
+__device__ __forceinline__ void write_mt_info(MtInfo* info, int e, int first, int n, int seg_start,
+                                              int seg_end) {
+    const MtInfo v{e, first, seg_start, seg_end};
+    for (int q = 0; q < n; ++q) info[first + q] = v;
+}
+
 // Per 64-token chunk: top-k per token by wave arg-max rounds (ties to the
 // lower index), the renormalised softmax weights, and the rank of each
 // assignment among the chunk's tokens routed to the same expert (a 64-bit
@@ -290,8 +299,9 @@ template <bool FUSED>
 __global__ __launch_bounds__(TOPK_THREADS) void topk_count(
     const float* __restrict__ logits, int T, int E, int k, int nchunks, int32_t* __restrict__ ids,
     float* __restrict__ wts, int32_t* __restrict__ rank, int32_t* __restrict__ chunk_counts,
-    int32_t* __restrict__ expert_counts, int32_t* __restrict__ offsets, int bm_gu, int bm_dn,
-    int32_t* __restrict__ mt_gu, int32_t* __restrict__ mt_dn, int32_t* __restrict__ sorted_assign) {
+    int32_t* __restrict__ expert_counts, int32_t* __restrict__ offsets, int bm,
+    int32_t* __restrict__ mt_prefix, MtInfo* __restrict__ mt_info, int32_t* __restrict__ tile_ctr,
+    int32_t* __restrict__ sorted_assign) {
     constexpr int NWAVE = TOPK_THREADS / 64;
     constexpr int TPW = ROUTE_CHUNK / NWAVE;  // tokens per wave
     __shared__ int ids_s[ROUTE_CHUNK * MAX_TOPK];
@@ -375,22 +385,21 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_count(
     } else {
         // single chunk: counts -> offsets -> m-tile prefixes -> sorted list
         const int cnt = tid < E ? __popcll(mask[tid]) : 0;
-        int tot0, tot1, tot2;
+        int tot0, tot1;
         const int off = block_exclusive_scan<NWAVE>(cnt, &tot0, scan_lds);
-        const int m1 = block_exclusive_scan<NWAVE>((cnt + bm_gu - 1) / bm_gu, &tot1, scan_lds);
-        const int m2 = block_exclusive_scan<NWAVE>((cnt + bm_dn - 1) / bm_dn, &tot2, scan_lds);
+        const int m1 = block_exclusive_scan<NWAVE>((cnt + bm - 1) / bm, &tot1, scan_lds);
         if (tid < E) {
             expert_counts[tid] = cnt;
             offsets[tid] = off;
-            mt_gu[tid] = m1;
-            mt_dn[tid] = m2;
+            mt_prefix[tid] = m1;
             off_s[tid] = off;
+            write_mt_info(mt_info, tid, m1, (cnt + bm - 1) / bm, off, off + cnt);
         }
         if (tid == 0) {
             offsets[E] = tot0;
-            mt_gu[E] = tot1;
-            mt_dn[E] = tot2;
+            mt_prefix[E] = tot1;
         }
+        if (tid < TILE_CTR_COUNT) tile_ctr[tid * TILE_CTR_STRIDE] = 0;
         __syncthreads();
         for (int al = tid; al < nt * k; al += TOPK_THREADS) {
             const int tl = al / k;
@@ -422,26 +431,26 @@ __global__ __launch_bounds__(256) void chunk_scan(const int32_t* __restrict__ ch
 }
 
 __global__ __launch_bounds__(256) void finalize(const int32_t* __restrict__ expert_counts, int E,
-                                                int bm_gu, int bm_dn, int32_t* __restrict__ offsets,
-                                                int32_t* __restrict__ mt_gu,
-                                                int32_t* __restrict__ mt_dn) {
+                                                int bm, int32_t* __restrict__ offsets,
+                                                int32_t* __restrict__ mt_prefix,
+                                                MtInfo* __restrict__ mt_info,
+                                                int32_t* __restrict__ tile_ctr) {
     __shared__ int lds[4];
     const int e = threadIdx.x;
     const int cnt = e < E ? expert_counts[e] : 0;
-    int tot0, tot1, tot2;
+    int tot0, tot1;
     const int off = block_exclusive_scan<4>(cnt, &tot0, lds);
-    const int m1 = block_exclusive_scan<4>((cnt + bm_gu - 1) / bm_gu, &tot1, lds);
-    const int m2 = block_exclusive_scan<4>((cnt + bm_dn - 1) / bm_dn, &tot2, lds);
+    const int m1 = block_exclusive_scan<4>((cnt + bm - 1) / bm, &tot1, lds);
     if (e < E) {
         offsets[e] = off;
-        mt_gu[e] = m1;
-        mt_dn[e] = m2;
+        mt_prefix[e] = m1;
+        write_mt_info(mt_info, e, m1, (cnt + bm - 1) / bm, off, off + cnt);
     }
     if (e == 0) {
         offsets[E] = tot0;
-        mt_gu[E] = tot1;
-        mt_dn[E] = tot2;
+        mt_prefix[E] = tot1;
     }
+    if (e < TILE_CTR_COUNT) tile_ctr[e * TILE_CTR_STRIDE] = 0;
 }
 
 __global__ __launch_bounds__(256) void scatter(const int32_t* __restrict__ ids, int T, int k,
@@ -479,6 +488,7 @@ int router_splits(int T, int E, int H) {
 hipError_t launch_route(const RouteInputs& in, const RouteBuffers& b, hipStream_t s) {
     const int T = in.T, E = in.E, k = in.k, H = in.H, S = in.splits;
     const int nchunks = (T + ROUTE_CHUNK - 1) / ROUTE_CHUNK;
+    MtInfo* mt_info = reinterpret_cast<MtInfo*>(b.mt_info);
     {
         const dim3 grid((T + RBM - 1) / RBM, S);
         const int eb = (E + 63) / 64;
@@ -496,17 +506,17 @@ hipError_t launch_route(const RouteInputs& in, const RouteBuffers& b, hipStream_
     }
     if (nchunks == 1) {
         topk_count<true><<<1, TOPK_THREADS, 0, s>>>(b.logits, T, E, k, nchunks, b.topk_ids, b.topk_w, b.rank,
-                                           b.chunk_counts, b.expert_counts, b.expert_offsets, in.bm_gu,
-                                           in.bm_dn, b.mt_prefix_gu, b.mt_prefix_dn, b.sorted_assign);
+                                                    b.chunk_counts, b.expert_counts, b.expert_offsets, in.bm,
+                                                    b.mt_prefix, mt_info, b.tile_ctr, b.sorted_assign);
         return hipGetLastError();
     }
-    topk_count<false><<<nchunks, TOPK_THREADS, 0, s>>>(b.logits, T, E, k, nchunks, b.topk_ids, b.topk_w, b.rank,
-                                              b.chunk_counts, b.expert_counts, b.expert_offsets,
-                                              in.bm_gu, in.bm_dn, b.mt_prefix_gu, b.mt_prefix_dn,
-                                              b.sorted_assign);
+    topk_count<false><<<nchunks, TOPK_THREADS, 0, s>>>(b.logits, T, E, k, nchunks, b.topk_ids, b.topk_w,
+                                                       b.rank, b.chunk_counts, b.expert_counts,
+                                                       b.expert_offsets, in.bm, b.mt_prefix, mt_info,
+                                                       b.tile_ctr, b.sorted_assign);
     chunk_scan<<<E, 256, 0, s>>>(b.chunk_counts, nchunks, b.chunk_base, b.expert_counts);
-    finalize<<<1, 256, 0, s>>>(b.expert_counts, E, in.bm_gu, in.bm_dn, b.expert_offsets,
-                               b.mt_prefix_gu, b.mt_prefix_dn);
+    finalize<<<1, 256, 0, s>>>(b.expert_counts, E, in.bm, b.expert_offsets, b.mt_prefix, mt_info,
+                               b.tile_ctr);
     scatter<<<nchunks, 256, 0, s>>>(b.topk_ids, T, k, nchunks, b.expert_offsets, b.chunk_base,
                                     b.rank, b.sorted_assign);
     return hipGetLastError();

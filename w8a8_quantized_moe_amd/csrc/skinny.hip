@@ -35,20 +35,15 @@ __global__ __launch_bounds__(SK_WAVES * 64) void gemm_skinny(GemmParams p) {
     const int64_t total = (int64_t)p.mt_prefix[p.G] * NC;
     if (item >= total) return;  // wave-uniform
 
-    // expert of this item: the largest g with mt_prefix[g] <= item / NC
-    const int64_t mtL = item / NC;
-    int lo = 0, hi = p.G;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (p.mt_prefix[mid] <= mtL) lo = mid; else hi = mid;
-    }
-    const int g = lo;
-    const int mcount = p.mt_prefix[g + 1] - p.mt_prefix[g];
-    const int64_t local = item - (int64_t)p.mt_prefix[g] * NC;
+    // expert of this item: one load from the routing's per-row-block table
+    const MtInfo info = reinterpret_cast<const MtInfo*>(p.mt_info)[item / NC];
+    const int g = info.group;
+    const int mcount = (info.seg_end - info.seg_start + SKINNY_BM - 1) / SKINNY_BM;
+    const int64_t local = item - (int64_t)info.first_tile * NC;
     const int rb = (int)(local % mcount);
     const int cb = (int)(local / mcount);
-    const int64_t row0 = p.seg_offsets[g] + (int64_t)rb * SKINNY_BM;
-    const int64_t row_end = min(row0 + SKINNY_BM, (int64_t)p.seg_offsets[g + 1]);
+    const int64_t row0 = info.seg_start + (int64_t)rb * SKINNY_BM;
+    const int64_t row_end = min(row0 + SKINNY_BM, (int64_t)info.seg_end);
 
     // MFMA A operand: lane l holds row l%16 and the 16-byte k-chunk l/16 of
     // each 64-byte k step; rows past the segment read a valid row (dropped)
