@@ -78,7 +78,8 @@ class HipEvents:
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["w8a8_quantized_moe_amd/csrc/gemm.hip", "w8a8_quantized_moe_amd/csrc/internal.h",
                   "w8a8_quantized_moe_amd/csrc/route.hip", "w8a8_quantized_moe_amd/csrc/quant.hip",
-                  "w8a8_quantized_moe_amd/csrc/combine.hip"]
+                  "w8a8_quantized_moe_amd/csrc/combine.hip", "w8a8_quantized_moe_amd/csrc/skinny.hip",
+                  "w8a8_quantized_moe_amd/csrc/abi.cpp"]
 
 
 def kernel_sources_hash():
