@@ -77,6 +77,7 @@ class HipEvents:
 # measured on: the hash below must match the sources as they are now.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["w8a8_quantized_moe_amd/csrc/gemm.hip", "w8a8_quantized_moe_amd/csrc/internal.h",
+                  "w8a8_quantized_moe_amd/csrc/device_common.h", "w8a8_quantized_moe_amd/csrc/skinny_item.h",
                   "w8a8_quantized_moe_amd/csrc/route.hip", "w8a8_quantized_moe_amd/csrc/quant.hip",
                   "w8a8_quantized_moe_amd/csrc/combine.hip", "w8a8_quantized_moe_amd/csrc/skinny.hip",
                   "w8a8_quantized_moe_amd/csrc/abi.cpp"]

@@ -1,0 +1,126 @@
+// Device building blocks of the routing and quantisation kernels: block
+// scans, the per-m-tile table, wave top-k and routing weights, and the per-row
+// quantisation arithmetic.
+#pragma once
+
+#include "internal.h"
+
+namespace w8a8 {
+
+// Block-wide exclusive scan of one int per thread (NW waves of 64).
+template <int NW>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* lds /* >= NW ints */) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += u;
+    }
+    if (lane == 63) lds[w] = incl;
+    __syncthreads();
+    int base = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        if (i < w) base += lds[i];
+        tot += lds[i];
+    }
+    __syncthreads();
+    *total = tot;
+    return base + incl - v;
+}
+
+// The m-tiles of expert e (first .. first + n - 1) all name e, its first
+// m-tile and its segment [seg_start, seg_end).
+__device__ __forceinline__ void write_mt_info(MtInfo* info, int e, int first, int n, int seg_start,
+                                              int seg_end) {
+    const MtInfo v{e, first, seg_start, seg_end};
+    for (int q = 0; q < n; ++q) info[first + q] = v;
+}
+
+// k rounds of a wave-wide arg-max over one token's logits (lane l holds
+// experts l, l+64, l+128, l+192 in v[0..3], -inf past E); ties go to the lower
+// expert index.  Lane 0 writes the picks in descending order to ids/vals.
+__device__ __forceinline__ void wave_topk(const float (&vin)[4], int lane, int E, int k, int* ids,
+                                          float* vals) {
+    float v0 = vin[0], v1 = vin[1], v2 = vin[2], v3 = vin[3];
+#pragma unroll 1
+    for (int j = 0; j < k; ++j) {
+        float bv = v0;
+        int bi = lane;
+        if (v1 > bv) { bv = v1; bi = lane + 64; }
+        if (v2 > bv) { bv = v2; bi = lane + 128; }
+        if (v3 > bv) { bv = v3; bi = lane + 192; }
+        if (bi >= E) bi = 0x7fffffff;  // padding never wins a tie
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            const float ov = __shfl_xor(bv, o, 64);
+            const int oi = __shfl_xor(bi, o, 64);
+            if (ov > bv || (ov == bv && oi < bi)) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        if (lane == 0) {
+            ids[j] = bi;
+            vals[j] = bv;
+        }
+        if (bi == lane) v0 = -INFINITY;
+        if (bi == lane + 64) v1 = -INFINITY;
+        if (bi == lane + 128) v2 = -INFINITY;
+        if (bi == lane + 192) v3 = -INFINITY;
+    }
+}
+
+// Routing weights of one token from its k picked logits (descending): the
+// softmax over the picks, which equals the full softmax renormalised over
+// them; terms summed in pick order, fp32.
+__device__ __forceinline__ void topk_weights(const float* vals, int k, float* w) {
+    const float mx = vals[0];
+    float z = 0.0f;
+    for (int j = 0; j < k; ++j) z += expf(vals[j] - mx);
+    for (int j = 0; j < k; ++j) w[j] = expf(vals[j] - mx) / z;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ int quant_one(float v, float s) {
+    if (s == 0.0f) return 0;
+    float r = __builtin_rintf(v / s);
+    r = fminf(fmaxf(r, -128.0f), 127.0f);
+    return (int)r;
+}
+
+// Same result as quant_one, cheaper: y = v * (1/s) differs from the IEEE
+// quotient fl(v/s) by less than 2.5 ulp, i.e. by less than 2^-15 for
+// |v/s| <= 127.  Rounding y and fl(v/s) to the nearest integer can then only
+// disagree if y lies within 2^-15 of a half-integer; those (rare) elements
+// take the exact division.
+__device__ __forceinline__ int quant_fast(float v, float s, float rs) {
+    if (s == 0.0f) return 0;
+    const float y = v * rs;
+    const float fy = fabsf(y);
+    const float frac = fy - __builtin_floorf(fy);
+    float r;
+    // the comparisons are written so that a non-finite y (1/s overflowing for
+    // a subnormal scale) also takes the exact path
+    if (fy <= 128.0f && fabsf(frac - 0.5f) >= 0x1p-15f) r = __builtin_rintf(y);
+    else r = __builtin_rintf(v / s);
+    r = fminf(fmaxf(r, -128.0f), 127.0f);
+    return (int)r;
+}
+
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
+    return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+           ((uint32_t)(d & 0xff) << 24);
+}
+
+__device__ __forceinline__ float amax4(float4 v) {
+    return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+}  // namespace w8a8

@@ -160,4 +160,5 @@ static_assert(sizeof(MtInfo) == 16, "one 16-byte load per m-tile");
 
 hipError_t launch_combine(const float* o, int T, int k, int H, float* y, hipStream_t s);
 
+
 }  // namespace w8a8

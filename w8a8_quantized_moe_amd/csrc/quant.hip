@@ -10,51 +10,10 @@
 // reduced: one wave per row up to 1024 columns, one 256-thread workgroup per
 // row above), and its codes and scale written once.  Loads and stores are
 // 16-byte (read) / 4-byte (write) per lane and contiguous across the wave.
-#include "internal.h"
+#include "device_common.h"
 
 namespace w8a8 {
 namespace {
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
-
-__device__ __forceinline__ int quant_one(float v, float s) {
-    if (s == 0.0f) return 0;
-    float r = __builtin_rintf(v / s);
-    r = fminf(fmaxf(r, -128.0f), 127.0f);
-    return (int)r;
-}
-
-// Same result as quant_one, cheaper: y = v * (1/s) differs from the IEEE
-// quotient fl(v/s) by less than 2.5 ulp, i.e. by less than 2^-15 for
-// |v/s| <= 127.  Rounding y and fl(v/s) to the nearest integer can then only
-// disagree if y lies within 2^-15 of a half-integer; those (rare) elements
-// take the exact division.
-__device__ __forceinline__ int quant_fast(float v, float s, float rs) {
-    if (s == 0.0f) return 0;
-    const float y = v * rs;
-    const float fy = fabsf(y);
-    const float frac = fy - __builtin_floorf(fy);
-    float r;
-    // the comparisons are written so that a non-finite y (1/s overflowing for
-    // a subnormal scale) also takes the exact path
-    if (fy <= 128.0f && fabsf(frac - 0.5f) >= 0x1p-15f) r = __builtin_rintf(y);
-    else r = __builtin_rintf(v / s);
-    r = fminf(fmaxf(r, -128.0f), 127.0f);
-    return (int)r;
-}
-
-__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
-    return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
-           ((uint32_t)(d & 0xff) << 24);
-}
-
-__device__ __forceinline__ float amax4(float4 v) {
-    return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-}
 
 // Vector path: cols % 4 == 0, ld % 4 == 0, x 16-byte aligned.  VPL float4 per
 // lane stay in registers (rows up to VPL*256 elements).

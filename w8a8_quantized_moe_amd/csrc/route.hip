@@ -30,7 +30,7 @@
 // The resulting order inside a segment is ascending token order.
 #include <type_traits>
 
-#include "internal.h"
+#include "device_common.h"
 
 namespace w8a8 {
 namespace {
@@ -258,37 +258,6 @@ __global__ __launch_bounds__(256) void router_reduce(const float* __restrict__ p
     logits[i] = v;
 }
 
-// Block-wide exclusive scan of one int per thread (NW waves of 64).
-template <int NW>
-__device__ int block_exclusive_scan(int v, int* total, int* lds /* >= NW ints */) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int u = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += u;
-    }
-    if (lane == 63) lds[w] = incl;
-    __syncthreads();
-    int base = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        if (i < w) base += lds[i];
-        tot += lds[i];
-    }
-    __syncthreads();
-    *total = tot;
-    return base + incl - v;
-}
-
-// The m-tiles of expert e (first .. first + n - 1) all name e, its first
-// m-tile and its segment [seg_start, seg_end).
-__device__ __forceinline__ void write_mt_info(MtInfo* info, int e, int first, int n, int seg_start,
-                                              int seg_end) {
-    const MtInfo v{e, first, seg_start, seg_end};
-    for (int q = 0; q < n; ++q) info[first + q] = v;
-}
-
 // Per 64-token chunk: top-k per token by wave arg-max rounds (ties to the
 // lower index), the renormalised softmax weights, and the rank of each
 // assignment among the chunk's tokens routed to the same expert (a 64-bit
@@ -332,46 +301,16 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_count(
     for (int u = 0; u < TPW; ++u) {
         const int tl = w + NWAVE * u;
         if (tl >= nt) break;
-        float v0 = vall[u][0], v1 = vall[u][1], v2 = vall[u][2], v3 = vall[u][3];
-        // k rounds of a wave arg-max; ties go to the lower expert index
-#pragma unroll 1
-        for (int j = 0; j < k; ++j) {
-            float bv = v0;
-            int bi = lane;
-            if (v1 > bv) { bv = v1; bi = lane + 64; }
-            if (v2 > bv) { bv = v2; bi = lane + 128; }
-            if (v3 > bv) { bv = v3; bi = lane + 192; }
-            if (bi >= E) bi = 0x7fffffff;  // padding never wins a tie
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                const float ov = __shfl_xor(bv, o, 64);
-                const int oi = __shfl_xor(bi, o, 64);
-                if (ov > bv || (ov == bv && oi < bi)) {
-                    bv = ov;
-                    bi = oi;
-                }
-            }
-            if (lane == 0) {
-                ids_s[tl * k + j] = bi;
-                val_s[tl * k + j] = bv;
-            }
-            if (bi == lane) v0 = -INFINITY;
-            if (bi == lane + 64) v1 = -INFINITY;
-            if (bi == lane + 128) v2 = -INFINITY;
-            if (bi == lane + 192) v3 = -INFINITY;
-        }
+        wave_topk(vall[u], lane, E, k, ids_s + tl * k, val_s + tl * k);
     }
     __syncthreads();
-    // softmax over the picked logits == full softmax renormalised over them;
-    // one thread per token, terms summed in pick order
     for (int tl = tid; tl < nt; tl += TOPK_THREADS) {
         const int t = t0 + tl;
-        const float mx = val_s[tl * k];
-        float z = 0.0f;
-        for (int j = 0; j < k; ++j) z += expf(val_s[tl * k + j] - mx);
+        float wj[MAX_TOPK];
+        topk_weights(val_s + tl * k, k, wj);
         for (int j = 0; j < k; ++j) {
             ids[(int64_t)t * k + j] = ids_s[tl * k + j];
-            wts[(int64_t)t * k + j] = expf(val_s[tl * k + j] - mx) / z;
+            wts[(int64_t)t * k + j] = wj[j];
         }
     }
     for (int al = tid; al < nt * k; al += TOPK_THREADS) atomicOr(&mask[ids_s[al]], 1ull << (al / k));
