@@ -13,6 +13,9 @@ together in the order the pages give them:
   per-expert segments -> gate-up GEMM + dequant + SiLU*up + requant -> down
   GEMM + dequant * routing weight -> combine.
 
+With FP8 codes (DeepSeek V4 page, sec. 2.1 and 2.3) the codes are E4M3 and
+the accumulators exact (fp64), rounded once to fp32 before the epilogue.
+
 Sources: "W8A8 quantisation of MiniMax-M3 on K100AI" sec. 2.1 (quant maths,
 scale outer product in the GEMM epilogue); "Tencent Hunyuan AI Infra ...
 Hopper" sec. 1.3 (FusedMoE stage list, weighted aggregation at the end);
@@ -68,6 +71,14 @@ def _load():
     lib.oracle_expert_ffn.argtypes = [I64, P, P, P, P, P, I64, I64, P, P, P, P, P, P, P, P, P, P]
     lib.oracle_combine.argtypes = [P, I64, I64, I64, P]
     lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_decode.restype = ctypes.c_double
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_quantize_rows_fp8.argtypes = [P, I64, I64, I64, P, P]
+    lib.oracle_gemm_fp8.argtypes = [P, P, I64, I64, I64, P]
+    lib.oracle_dense_fp8.argtypes = [P, P, P, P, I64, I64, I64, P]
+    lib.oracle_expert_ffn_fp8.argtypes = [I64, P, P, P, P, P, I64, I64, P, P, P, P, P, P, P, P, P, P]
     _lib = lib
     return lib
 
@@ -218,16 +229,112 @@ def combine(o, T, k):
 
 
 # --------------------------------------------------------------------------
+# FP8 E4M3 codes (DeepSeek V4 page, sec. 2.1 and 2.3)
+# --------------------------------------------------------------------------
+def e4m3_decode(codes):
+    """Values of E4M3 codes (uint8 array) as float64."""
+    lib = _load()
+    c = np.asarray(codes, np.uint8)
+    table = np.array([lib.oracle_e4m3_decode(i) for i in range(256)], np.float64)
+    return table[c]
+
+
+def e4m3_encode(v):
+    """Nearest E4M3 codes of float32 values (ties to even, saturating)."""
+    lib = _load()
+    v = np.asarray(v, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    fi, fo = v.reshape(-1), out.reshape(-1)
+    for i in range(fi.size):
+        fo[i] = lib.oracle_e4m3_encode(float(fi[i]))
+    return out
+
+
+def quantize_rows_fp8(x):
+    """Per-row FP8 E4M3 quantisation: s = max|x|/448, code = E4M3(x/s).
+    x: [rows, cols] float32 -> (q uint8 [rows, cols], s float32 [rows])."""
+    x = _c(x, np.float32)
+    if x.ndim == 1:
+        x = x[None, :]
+    rows, cols = x.shape
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((rows,), np.float32)
+    _load().oracle_quantize_rows_fp8(_p(x), rows, cols, cols, _p(q), _p(s))
+    return q, s
+
+
+def gemm_fp8(a, b):
+    """Exact accumulator sum_k E4M3(a) * E4M3(b) in float64; a [M, K], b [N, K] uint8 codes."""
+    a = _c(a, np.uint8)
+    b = _c(b, np.uint8)
+    M, K = a.shape
+    N, K2 = b.shape
+    assert K == K2
+    acc = np.empty((M, N), np.float64)
+    _load().oracle_gemm_fp8(_p(a), _p(b), M, N, K, _p(acc))
+    return acc
+
+
+def dense_fp8(a_q, s_a, b_q, s_b):
+    """Dense GEMM with FP8 codes: ((float)acc * s_a) * s_b."""
+    a_q = _c(a_q, np.uint8)
+    b_q = _c(b_q, np.uint8)
+    s_a = _c(s_a, np.float32)
+    s_b = _c(s_b, np.float32)
+    M, K = a_q.shape
+    N = b_q.shape[0]
+    out = np.empty((M, N), np.float32)
+    _load().oracle_dense_fp8(_p(a_q), _p(s_a), _p(b_q), _p(s_b), M, N, K, _p(out))
+    return out
+
+
+def expert_ffn_fp8(a_token, a_expert, a_weight, x_q, s_x, w_gu, s_gu, w_d, s_d, want_acc=False,
+                   want_h=False):
+    """Expert SwiGLU FFN with FP8 codes (see oracle.c)."""
+    a_token = _c(a_token, np.int64)
+    a_expert = _c(a_expert, np.int32)
+    a_weight = _c(a_weight, np.float32)
+    x_q = _c(x_q, np.uint8)
+    s_x = _c(s_x, np.float32)
+    w_gu = _c(w_gu, np.uint8)
+    s_gu = _c(s_gu, np.float32)
+    w_d = _c(w_d, np.uint8)
+    s_d = _c(s_d, np.float32)
+    n = a_token.shape[0]
+    E, twoI, H = w_gu.shape
+    I = twoI // 2
+    assert w_d.shape == (E, H, I)
+    acc_gu = np.empty((n, 2 * I), np.float64) if want_acc else None
+    acc_d = np.empty((n, H), np.float64) if want_acc else None
+    h = np.empty((n, I), np.float32) if want_h else None
+    h_q = np.empty((n, I), np.uint8)
+    s_h = np.empty((n,), np.float32)
+    o = np.empty((n, H), np.float32)
+    _load().oracle_expert_ffn_fp8(n, _p(a_token), _p(a_expert), _p(a_weight), _p(x_q), _p(s_x), H, I,
+                                  _p(w_gu), _p(s_gu), _p(w_d), _p(s_d), _p(acc_gu), _p(h), _p(h_q),
+                                  _p(s_h), _p(acc_d), _p(o))
+    out = dict(h_q=h_q, s_h=s_h, o=o)
+    if want_acc:
+        out["acc_gu"] = acc_gu
+        out["acc_d"] = acc_d
+    if want_h:
+        out["h"] = h
+    return out
+
+
+# --------------------------------------------------------------------------
 # the whole layer
 # --------------------------------------------------------------------------
 def moe_forward(x, wr, bias, w_gu_q, s_gu, w_d_q, s_d, k, tokens=None, want_acc=False,
-                want_h=False, route_tokens=None):
+                want_h=False, route_tokens=None, code="int8"):
     """The W8A8 MoE expert layer, step by step.
 
     x      [T, H]   float32 activations
     wr     [E, H]   float32 router weight, bias [E] float32 or None
     w_gu_q [E, 2I, H] int8 (rows 0..I-1 gate, I..2I-1 up), s_gu [E, 2I] f32
     w_d_q  [E, H, I]  int8, s_d [E, H] f32
+    code   "int8" (the codes above are int8) or "fp8" (uint8 E4M3 codes; the
+           activations and h are then quantised to E4M3 as well)
 
     ``tokens``: optional sorted subset of token indices for which the expert
     FFN, the outputs o and y are computed (tokens are independent, so a
@@ -242,7 +349,8 @@ def moe_forward(x, wr, bias, w_gu_q, s_gu, w_d_q, s_d, k, tokens=None, want_acc=
         x = x[np.asarray(route_tokens)]
     T, H = x.shape
     E = wr.shape[0]
-    x_q, s_x = quantize_rows(x)
+    assert code in ("int8", "fp8")
+    x_q, s_x = quantize_rows(x) if code == "int8" else quantize_rows_fp8(x)
     logits = router_logits(x, wr, bias)
     ids, w = topk_softmax(logits, k)
     counts, offsets, sorted_assign = permute(ids, E)
@@ -253,8 +361,9 @@ def moe_forward(x, wr, bias, w_gu_q, s_gu, w_d_q, s_d, k, tokens=None, want_acc=
     a_token = np.repeat(tok, k)
     a_expert = ids[tok].reshape(-1)
     a_weight = w[tok].reshape(-1)
-    ffn = expert_ffn(a_token, a_expert, a_weight, x_q, s_x, w_gu_q, s_gu, w_d_q, s_d,
-                     want_acc=want_acc, want_h=want_h)
+    ffn = (expert_ffn if code == "int8" else expert_ffn_fp8)(
+        a_token, a_expert, a_weight, x_q, s_x, w_gu_q, s_gu, w_d_q, s_d, want_acc=want_acc,
+        want_h=want_h)
     y = combine(ffn["o"], tok.shape[0], k)
     res = dict(x_q=x_q, s_x=s_x, logits=logits, ids=ids, w=w, counts=counts, offsets=offsets,
                sorted_assign=sorted_assign, tokens=tok, y=y)

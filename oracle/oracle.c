@@ -31,6 +31,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -277,6 +278,143 @@ ORACLE_API void oracle_combine(const float* o, int64_t T, int64_t k, int64_t H, 
             for (int64_t j = 0; j < k; ++j) sum += o[(t * k + j) * H + n];
             y[t * H + n] = sum;
         }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* FP8 E4M3 codes, [DSV4] sec. 2.1: the forward weights and activations use  */
+/* E4M3 (4 exponent bits, 3 mantissa bits, range about +-448); sec. 2.3:     */
+/* fp8 inputs, an fp32 (here: exact) accumulator, the output requantised.   */
+/* Layout (the OCP "E4M3FN" format that the +-448 range implies): sign bit,  */
+/* 4-bit exponent with bias 7, 3-bit mantissa; exponent 0 holds subnormals   */
+/* m * 2^-9; there are no infinities and S.1111.111 is NaN, so the largest   */
+/* finite magnitude is 1.75 * 2^8 = 448.                                     */
+/* Reading adopted (the pages give no rounding rule): round to the nearest   */
+/* finite value, a tie going to the even mantissa; magnitudes beyond 448     */
+/* therefore map to 448 (saturation).                                        */
+/* ------------------------------------------------------------------------ */
+ORACLE_API double oracle_e4m3_decode(uint8_t c) {
+    const int e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double mag = (e == 0) ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return (c & 0x80) ? -mag : mag;
+}
+
+/* Nearest finite E4M3 value by a walk over the 127 non-negative finite codes
+ * in increasing order (codes 0x00 .. 0x7E increase with the value): the
+ * magnitude lies between two consecutive values, and the midpoint decides. */
+ORACLE_API uint8_t oracle_e4m3_encode(float v) {
+    if (isnan(v)) return 0x7F;
+    const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    const double a = fabs((double)v);
+    uint8_t best = 0x7E; /* beyond the largest value: saturate */
+    for (int c = 0; c < 0x7E; ++c) {
+        const double lo = oracle_e4m3_decode((uint8_t)c), hi = oracle_e4m3_decode((uint8_t)(c + 1));
+        if (a > hi) continue;
+        const double mid = 0.5 * (lo + hi); /* exact: both have at most 4 significant bits */
+        if (a < mid) best = (uint8_t)c;
+        else if (a > mid) best = (uint8_t)(c + 1);
+        else best = (c % 2 == 0) ? (uint8_t)c : (uint8_t)(c + 1); /* tie: even mantissa */
+        break;
+    }
+    return (uint8_t)(sign | best);
+}
+
+/* Per-row FP8 quantisation, the same scheme as the INT8 one with the E4M3
+ * range: s = max|x| / 448 (fp32 division), code = E4M3(x / s) (the quotient
+ * an IEEE fp32 division, then rounded as above); an all-zero row gives s = 0
+ * and code 0x00. */
+ORACLE_API void oracle_quantize_rows_fp8(const float* x, int64_t rows, int64_t cols, int64_t ld,
+                                         uint8_t* q, float* scale) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* xr = x + r * ld;
+        float amax = 0.0f;
+        for (int64_t c = 0; c < cols; ++c)
+            if (fabsf(xr[c]) > amax) amax = fabsf(xr[c]);
+        const float s = amax / 448.0f;
+        scale[r] = s;
+        for (int64_t c = 0; c < cols; ++c) q[r * cols + c] = (s == 0.0f) ? 0x00 : oracle_e4m3_encode(xr[c] / s);
+    }
+}
+
+/* FP8 GEMM accumulator: acc[m][n] = sum_k E4M3(a[m][k]) * E4M3(b[n][k]) in
+ * fp64.  Products of two E4M3 values have at most 8 significant bits and
+ * magnitudes in [2^-18, 448^2]; a sum of up to 2^13 of them needs at most 49
+ * bits, so this fp64 sum is exact for K <= 8192. */
+ORACLE_API void oracle_gemm_fp8(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
+                                double* acc) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double sum = 0.0;
+            for (int64_t k = 0; k < K; ++k) sum += oracle_e4m3_decode(a[m * K + k]) * oracle_e4m3_decode(b[n * K + k]);
+            acc[m * N + n] = sum;
+        }
+}
+
+/* Dense W8A8 GEMM with FP8 codes: out = ((float)acc * s_a[m]) * s_b[n], the
+ * exact accumulator rounded once to fp32, then the scale outer product. */
+ORACLE_API void oracle_dense_fp8(const uint8_t* a, const float* s_a, const uint8_t* b, const float* s_b,
+                                 int64_t M, int64_t N, int64_t K, float* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double sum = 0.0;
+            for (int64_t k = 0; k < K; ++k) sum += oracle_e4m3_decode(a[m * K + k]) * oracle_e4m3_decode(b[n * K + k]);
+            const float v = (float)sum * s_a[m];
+            out[m * N + n] = v * s_b[n];
+        }
+}
+
+/* Expert FFN with FP8 codes: the INT8 definition above with E4M3 codes, the
+ * exact accumulators rounded once to fp32, and h requantised per row to E4M3
+ * (s_h = max|h| / 448). */
+ORACLE_API void oracle_expert_ffn_fp8(int64_t n_assign, const int64_t* a_token, const int32_t* a_expert,
+                                      const float* a_weight, const uint8_t* x_q, const float* s_x,
+                                      int64_t H, int64_t I, const uint8_t* w_gu, const float* s_gu,
+                                      const uint8_t* w_d, const float* s_d, double* acc_gu, float* h_out,
+                                      uint8_t* h_q, float* s_h, double* acc_d, float* o) {
+#pragma omp parallel
+    {
+        double* acc = (double*)malloc((size_t)(2 * I) * sizeof(double));
+        float* h = (float*)malloc((size_t)I * sizeof(float));
+        uint8_t* hq = (uint8_t*)malloc((size_t)I);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t a = 0; a < n_assign; ++a) {
+            const int64_t t = a_token[a];
+            const int64_t e = a_expert[a];
+            const uint8_t* xr = x_q + t * H;
+            const uint8_t* wg = w_gu + e * (2 * I) * H;
+            for (int64_t i = 0; i < 2 * I; ++i) {
+                double sum = 0.0;
+                for (int64_t hh = 0; hh < H; ++hh)
+                    sum += oracle_e4m3_decode(xr[hh]) * oracle_e4m3_decode(wg[i * H + hh]);
+                acc[i] = sum;
+            }
+            if (acc_gu) memcpy(acc_gu + a * 2 * I, acc, (size_t)(2 * I) * sizeof(double));
+            for (int64_t i = 0; i < I; ++i) {
+                float g = ((float)acc[i] * s_x[t]) * s_gu[e * 2 * I + i];
+                float u = ((float)acc[I + i] * s_x[t]) * s_gu[e * 2 * I + I + i];
+                h[i] = oracle_silu(g) * u;
+            }
+            if (h_out) memcpy(h_out + a * I, h, (size_t)I * sizeof(float));
+            float sh;
+            oracle_quantize_rows_fp8(h, 1, I, I, hq, &sh);
+            s_h[a] = sh;
+            memcpy(h_q + a * I, hq, (size_t)I);
+            const uint8_t* wdn = w_d + e * H * I;
+            for (int64_t n = 0; n < H; ++n) {
+                double sum = 0.0;
+                for (int64_t i = 0; i < I; ++i) sum += oracle_e4m3_decode(hq[i]) * oracle_e4m3_decode(wdn[n * I + i]);
+                if (acc_d) acc_d[a * H + n] = sum;
+                float v = ((float)sum * sh) * s_d[e * H + n];
+                o[a * H + n] = a_weight[a] * v;
+            }
+        }
+        free(acc);
+        free(h);
+        free(hq);
     }
 }
 

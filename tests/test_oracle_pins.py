@@ -330,3 +330,115 @@ def test_combine_order_and_k1():
     ref = (o[0::3].astype(np.float32) + o[1::3]) + o[2::3]
     assert np.array_equal(y, ref)
     assert np.array_equal(oracle.combine(o, 12, 1), o)
+
+
+# ---------------------------------------------------------------- FP8 E4M3 codes
+def test_e4m3_hand_worked():
+    g = _gold("fp8_pins.json")
+    for c in g["encode"]:
+        assert int(oracle.e4m3_encode(np.float32(c["v"]))) == c["code"], c
+    for c in g["quant"]:
+        q, s = oracle.quantize_rows_fp8(np.array(c["x"], np.float32))
+        assert s[0] == np.float32(c["s"]), c
+        assert q[0].tolist() == c["q"], c
+    d = g["dense"]
+    a = oracle.e4m3_encode(np.array(d["a"], np.float32))
+    b = oracle.e4m3_encode(np.array(d["b"], np.float32))
+    out = oracle.dense_fp8(a, np.array(d["s_a"], np.float32), b, np.array(d["s_b"], np.float32))
+    assert out.tolist() == d["out"]
+
+
+def test_e4m3_format_closed_forms():
+    codes = np.arange(256, dtype=np.uint8)
+    v = oracle.e4m3_decode(codes)
+    finite = ~np.isnan(v)
+    # exactly two NaN codes (S.1111.111), no infinities, largest finite 448
+    assert np.count_nonzero(~finite) == 2 and not np.isinf(v[finite]).any()
+    assert np.nanmax(v) == 448.0 and np.nanmin(v) == -448.0
+    # codes 0x00..0x7E increase strictly; the negative half mirrors them
+    assert np.all(np.diff(v[:127]) > 0)
+    assert np.array_equal(v[128:255], -v[:127])
+    # the value formula: subnormals m*2^-9, normals (1 + m/8) * 2^(e-7)
+    for c in range(127):
+        e, m = c >> 3, c & 7
+        ref = m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        assert v[c] == ref
+    # round trip of every finite code (negative zero included)
+    back = oracle.e4m3_encode(v[finite].astype(np.float32))
+    assert np.array_equal(back, codes[finite])
+
+
+def test_e4m3_encoder_is_nearest_ties_even_by_brute_force():
+    rng = np.random.default_rng(5)
+    vals = oracle.e4m3_decode(np.arange(127, dtype=np.uint8))
+    mids = 0.5 * (vals[:-1] + vals[1:])
+    x = np.concatenate([rng.standard_normal(3000) * 40, rng.standard_normal(500) * 0.01,
+                        mids, -mids, np.nextafter(mids.astype(np.float32), np.float32(0)),
+                        np.nextafter(mids.astype(np.float32), np.float32(1e9))]).astype(np.float32)
+    got = oracle.e4m3_encode(x)
+    mag = np.abs(x.astype(np.float64))
+    for xi, gi, ai in zip(x, got, mag):
+        d = np.abs(vals - min(ai, 448.0))
+        best = np.flatnonzero(d == d.min())
+        want = best[0] if best.size == 1 else best[best % 2 == 0][0]  # tie: even mantissa
+        assert (gi & 0x7F) == want, (xi, gi, want)
+        assert (gi >> 7) == (1 if np.signbit(xi) else 0)
+
+
+def test_fp8_quant_invariants():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((23, 301)).astype(np.float32)
+    x[:, 7] *= 50.0
+    q, s = oracle.quantize_rows_fp8(x)
+    v = oracle.e4m3_decode(q)
+    # the row maximum maps to +-448 and nothing exceeds it
+    am = np.argmax(np.abs(x), axis=1)
+    assert np.all(np.abs(v[np.arange(23), am]) == 448.0)
+    assert np.abs(v).max() <= 448.0
+    # sign symmetry and power-of-two scaling invariance
+    qn, sn = oracle.quantize_rows_fp8(-x)
+    assert np.array_equal(qn, q ^ 0x80) and np.array_equal(sn, s)
+    qp, sp = oracle.quantize_rows_fp8(x * np.float32(2.0 ** 9))
+    assert np.array_equal(qp, q) and np.array_equal(sp, s * np.float32(2.0 ** 9))
+    # relative error of round-to-nearest with 3 mantissa bits: |x - v*s| <= 2^-4 |x| for normals
+    xs = x.astype(np.float64) / s[:, None]
+    norm = np.abs(xs) >= 2.0 ** -6
+    err = np.abs(xs - v)
+    assert np.all(err[norm] <= np.abs(xs[norm]) * 2.0 ** -4 * (1 + 1e-6))
+    assert np.all(err[~norm] <= 2.0 ** -10 * (1 + 1e-6))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 7), (17, 9, 130), (8, 33, 512)])
+def test_fp8_gemm_exact_against_numpy(M, N, K):
+    rng = np.random.default_rng(M * 100 + N)
+    a = rng.integers(0, 256, (M, K), dtype=np.uint8)
+    b = rng.integers(0, 256, (N, K), dtype=np.uint8)
+    a[(a & 0x7F) == 0x7F] = 0x7E  # no NaN codes
+    b[(b & 0x7F) == 0x7F] = 0x7E
+    acc = oracle.gemm_fp8(a, b)
+    ref = oracle.e4m3_decode(a) @ oracle.e4m3_decode(b).T  # exact: the sum needs < 53 bits
+    assert np.array_equal(acc, ref)
+    out = oracle.dense_fp8(a, np.full(M, 0.5, np.float32), b, np.full(N, 4.0, np.float32))
+    assert np.array_equal(out, (ref.astype(np.float32) * np.float32(0.5)) * np.float32(4.0))
+
+
+def test_fp8_single_expert_reduces_to_dense_chain():
+    """E = 1, k = 1: the FP8 expert FFN equals two dense FP8 GEMMs around the
+    SwiGLU and the E4M3 requantisation, written out here step by step."""
+    rng = np.random.default_rng(8)
+    T, H, I = 5, 64, 32
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    wgu = (rng.standard_normal((1, 2 * I, H)) * 0.05).astype(np.float32)
+    wd = (rng.standard_normal((1, H, I)) * 0.05).astype(np.float32)
+    qgu, sgu = oracle.quantize_rows_fp8(wgu[0])
+    qd, sd = oracle.quantize_rows_fp8(wd[0])
+    xq, sx = oracle.quantize_rows_fp8(x)
+    gu = oracle.dense_fp8(xq, sx, qgu, sgu)
+    h = oracle.silu(gu[:, :I]) * gu[:, I:]
+    hq, sh = oracle.quantize_rows_fp8(h)
+    o = oracle.dense_fp8(hq, sh, qd, sd)
+    r = oracle.moe_forward(x, np.zeros((1, H), np.float32), None, qgu[None], sgu[None], qd[None],
+                           sd[None], 1, code="fp8", want_h=True)
+    assert np.array_equal(r["x_q"], xq) and np.array_equal(r["h"], h)
+    assert np.array_equal(r["h_q"], hq) and np.array_equal(r["s_h"], sh)
+    assert np.array_equal(r["y"], o)
