@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 # MI355X published peaks (dense)
 PEAK_INT8_OPS = 5.0e15      # int8 MFMA, ops/s
+PEAK_FP8_OPS = 5.0e15       # fp8 MFMA, flop/s (the same as int8 on this chip)
 PEAK_FP32_MFMA = 157.3e12   # fp32 matrix, flop/s
 PEAK_HBM = 8.0e12           # bytes/s
 
@@ -91,7 +92,7 @@ def kernel_sources_hash():
     return h.hexdigest()
 
 
-def measured_traffic(workload, stage):
+def measured_traffic(workload, stage, code="int8"):
     """HBM bytes per launch of a stage from profiles/traffic.json, or None when
     there is no measurement or the kernels changed since it was taken."""
     try:
@@ -101,7 +102,8 @@ def measured_traffic(workload, stage):
         return None
     if rec.get("sources_sha256") != kernel_sources_hash():
         return None
-    ent = rec.get("stages", {}).get(f"{workload}:{stage}")
+    key = f"{workload}:{stage}" if code == "int8" else f"{workload}/{code}:{stage}"
+    ent = rec.get("stages", {}).get(key)
     if not ent:
         return None
     return int(ent["fetch_bytes"] + ent["write_bytes"])
@@ -151,7 +153,7 @@ def stage_work(T, H, E, k, I, touched):
     }
 
 
-def cpu_baseline(inp, target_s):
+def cpu_baseline(inp, target_s, code="int8"):
     """The CPU oracle, as it stands, on the first n tokens of the same batch
     (whole layer for those tokens), n sized for about target_s seconds."""
     import numpy as np
@@ -168,7 +170,7 @@ def cpu_baseline(inp, target_s):
 
     def run(n):
         t0 = time.perf_counter()
-        oracle.moe_forward(x, wr, b, w_gu, s_gu, w_d, s_d, k, route_tokens=np.arange(n))
+        oracle.moe_forward(x, wr, b, w_gu, s_gu, w_d, s_d, k, route_tokens=np.arange(n), code=code)
         return time.perf_counter() - t0
 
     probe_n = min(8, T)
@@ -247,6 +249,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large",
                     choices=["large", "prefill", "decode", "tiny", "dense"])
+    ap.add_argument("--code", default="int8", choices=["int8", "fp8"],
+                    help="code type of the expert weights and activations (fp8: E4M3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -270,12 +274,14 @@ def main():
     if args.workload == "dense":
         return bench_dense(args, torch, synth, w8)
     log(f"[bench] generating workload '{args.workload}' on the GPU")
-    inp = synth.moe_inputs(args.workload, device="cuda")
+    over = {} if args.code == "int8" else {"weights": "fp8"}
+    inp = synth.moe_inputs(args.workload, device="cuda", **over)
     T, H, E, k, I = inp["T"], inp["H"], inp["E"], inp["k"], inp["I"]
     A = T * k
     if "w_gu_f32" in inp:
         wts, codes = w8.MoEWeights.from_fp32(inp["wr"], inp["b"], inp["w_gu_f32"], inp["w_d_f32"],
-                                             keep_codes=True)
+                                             keep_codes=True,
+                                             code=w8.CODE_FP8 if args.code == "fp8" else w8.CODE_INT8)
         inp.update(codes)
     else:
         wts = w8.MoEWeights.from_int8(inp["wr"], inp["b"], inp["w_gu"], inp["s_gu"], inp["w_d"],
@@ -320,7 +326,7 @@ def main():
     achieved = amount / (stage_ms[dom] * 1e-3)
     roofline = dict(kernel=dom, bound=bound, achieved=round(achieved / scale, 2),
                     peak=peak / scale, unit=unit, frac=round(achieved / peak, 4),
-                    traffic=measured_traffic(args.workload, dom), work_per_launch=amount)
+                    traffic=measured_traffic(args.workload, dom, args.code), work_per_launch=amount)
 
     step_s = ms_per_step * 1e-3
     int8_ops = 6 * A * H * I
@@ -337,12 +343,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8",
-        "data": "synthetic (seeded; random int8 expert weights of the layer's shape)",
-        "config": {"workload": f"{args.workload} MoE layer T={T} H={H} E={E} top-{k} I={I}",
-                   "T": T, "H": H, "E": E, "top_k": k, "I": I, "parallelism": "none (1 GPU)"},
-        "int8_tops": round(int8_ops / step_s / 1e12, 2),
-        "int8_frac_of_peak": round(int8_ops / step_s / PEAK_INT8_OPS, 4),
+        "dtype": "int8" if args.code == "int8" else "fp8_e4m3",
+        "data": f"synthetic (seeded; random {'int8' if args.code == 'int8' else 'FP8 E4M3'} expert "
+                "weights of the layer's shape)",
+        "config": {"workload": f"{args.workload} MoE layer T={T} H={H} E={E} top-{k} I={I}"
+                               + ("" if args.code == "int8" else ", FP8 E4M3 codes"),
+                   "T": T, "H": H, "E": E, "top_k": k, "I": I, "code": args.code,
+                   "parallelism": "none (1 GPU)"},
+        f"{args.code}_tops": round(int8_ops / step_s / 1e12, 2),
+        f"{args.code}_frac_of_peak": round(int8_ops / step_s / PEAK_INT8_OPS, 4),
         "alg_hbm_gbps": round(alg_bytes / step_s / 1e9, 1),
         "hbm_frac_of_peak": round(alg_bytes / step_s / PEAK_HBM, 4),
         "experts_touched": touched,
@@ -352,7 +361,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a token sample")
-        cb = cpu_baseline(inp, args.cpu_seconds)
+        cb = cpu_baseline(inp, args.cpu_seconds, args.code)
         out["cpu_baseline"] = {kk: (round(v, 3) if isinstance(v, float) else v)
                                for kk, v in cb.items() if kk in ("value", "unit", "cores", "kind",
                                                                  "sample")}

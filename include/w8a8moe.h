@@ -67,7 +67,7 @@ W8A8_API const char* w8a8_status_string(int status);
 /* Thread-local detail of the last non-OK status returned on this thread. */
 W8A8_API const char* w8a8_last_error(void);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2. */
 W8A8_API int w8a8_abi_version(void);
 
 /* -------------------------------------------------------------------------
@@ -86,6 +86,26 @@ W8A8_API int w8a8_abi_version(void);
  * ------------------------------------------------------------------------- */
 W8A8_API w8a8_status w8a8_quantize_rows(const float* x, int64_t rows, int64_t cols, int64_t ld, int8_t* q,
                                float* scale, w8a8_stream stream);
+
+/* -------------------------------------------------------------------------
+ * Codes of the quantised operands.  [DSV4] sec. 2.1 uses FP8 E4M3 (4
+ * exponent bits, 3 mantissa bits, range +-448) for the forward weights and
+ * activations; sec. 2.3 accumulates fp8 products in fp32.  E4M3 here is the
+ * OCP E4M3FN format: sign | exponent (bias 7) | mantissa, exponent 0 for
+ * subnormals m * 2^-9, no infinities, S.1111.111 = NaN, largest value 448.
+ * ------------------------------------------------------------------------- */
+enum { W8A8_CODE_INT8 = 0, W8A8_CODE_FP8_E4M3 = 1 };
+
+/* Per-row dynamic FP8 quantisation: the scheme of w8a8_quantize_rows with the
+ * E4M3 range ([DSV4] sec. 2.1):
+ *   s[r] = max_c |x[r][c]| / 448          (fp32, IEEE division)
+ *   q[r][c] = E4M3(x[r][c] / s[r])        (fp32 quotient, rounded to the
+ *                                          nearest E4M3 value, ties to the
+ *                                          even mantissa)
+ * An all-zero row gives s = 0 and codes 0x00.  Arguments, limits and errors
+ * as for w8a8_quantize_rows; q holds uint8 E4M3 codes. */
+W8A8_API w8a8_status w8a8_quantize_rows_fp8(const float* x, int64_t rows, int64_t cols, int64_t ld,
+                                            uint8_t* q, float* scale, w8a8_stream stream);
 
 /* -------------------------------------------------------------------------
  * Weight packing.  The GEMM kernels read the int8 weight operand in a
@@ -131,6 +151,19 @@ W8A8_API w8a8_status w8a8_gemm(const int8_t* a_q, const float* s_a, const int8_t
 W8A8_API w8a8_status w8a8_gemm_i32(const int8_t* a_q, const int8_t* b_packed, int64_t M, int64_t N,
                           int64_t K, int32_t* acc, w8a8_stream stream);
 
+/* The same GEMM with FP8 E4M3 codes ([DSV4] sec. 2.3: fp8 inputs, fp32
+ * accumulator): acc[m][n] = sum_k E4M3(a_q[m][k]) * E4M3(b[n][k]) on the FP8
+ * matrix cores, out = ((float)acc * s_a[m]) * s_b[n].  Not exact: the
+ * accumulator between matrix instructions is fp32, but inside one instruction
+ * (128 k) the hardware aligns the products to the largest one and drops bits
+ * below about 2^-16 of it; on Gaussian-like codes the error stays below
+ * 2^-16 * sum_k |a_k b_k|.  b_packed is the uint8 codes packed like int8
+ * weights (w8a8_pack_weights moves bytes).  Limits and errors as for
+ * w8a8_gemm. */
+W8A8_API w8a8_status w8a8_gemm_fp8(const uint8_t* a_q, const float* s_a, const uint8_t* b_packed,
+                                   const float* s_b, int64_t M, int64_t N, int64_t K, float* out,
+                                   w8a8_stream stream);
+
 /* -------------------------------------------------------------------------
  * The MoE expert layer.
  *
@@ -174,6 +207,8 @@ typedef struct {
     const float* s_gate_up;
     const int8_t* w_down;
     const float* s_down;
+    int32_t code;  /* W8A8_CODE_INT8 or W8A8_CODE_FP8_E4M3: the code of w_gate_up
+                      and w_down, and the code the layer quantises x and h to */
 } w8a8_moe_weights;
 
 /* Byte offsets of the intermediates inside the workspace. */

@@ -133,12 +133,30 @@ def int8_expert_weights(E, H, I, seed, workload, device):
     return w_gu, s_gu.float().contiguous(), w_d, s_d.float().contiguous()
 
 
+def fp8_expert_weights(E, H, I, seed, workload, device):
+    """E4M3 codes (uint8) of weights with std ~0.02: code values ~N(0, 64),
+    clipped to the E4M3 range, times per-channel scales ~U(0.9, 1.1)*0.02/64.
+    The codes are random inputs; their conversion is torch's, not the method's."""
+    def codes(shape, name):
+        g = _gen(device, seed, workload, name)
+        v = (torch.randn(shape, generator=g, device=device) * 64.0).clamp(-448.0, 448.0)
+        return v.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+    w_gu = codes((E, 2 * I, H), "w_gate_up_fp8")
+    w_d = codes((E, H, I), "w_down_fp8")
+    g = _gen(device, seed, workload, "s_gate_up")
+    s_gu = (torch.rand(E, 2 * I, generator=g, device=device) * 0.2 + 0.9) * (0.02 / 64.0)
+    g = _gen(device, seed, workload, "s_down")
+    s_d = (torch.rand(E, H, generator=g, device=device) * 0.2 + 0.9) * (0.02 / 64.0)
+    return w_gu, s_gu.float().contiguous(), w_d, s_d.float().contiguous()
+
+
 def moe_inputs(workload="tiny", seed=0, device="cpu", **override):
     """Inputs of one MoE workload.  ``override`` replaces shape/recipe fields
     (T, H, E, k, I, n_outlier, outlier_scale, bf16_x, bias, weights, beta).
 
     Returns a dict with x, wr, b and either (w_gu_f32, w_d_f32) for fp32
-    weights or (w_gu, s_gu, w_d, s_d) for int8 weights, plus the shape."""
+    weights or (w_gu, s_gu, w_d, s_d) for int8 (or, weights="fp8", uint8 E4M3)
+    codes, plus the shape."""
     cfg = dict(CONFIGS[workload]) if workload in CONFIGS else dict(CONFIGS["tiny"])
     cfg.update(override)
     assert cfg["kind"] == "moe"
@@ -149,6 +167,9 @@ def moe_inputs(workload="tiny", seed=0, device="cpu", **override):
     out["wr"], out["b"] = router(E, H, cfg["bias"], seed, workload, device, cfg.get("beta"))
     if cfg["weights"] == "fp32":
         out["w_gu_f32"], out["w_d_f32"] = fp32_expert_weights(E, H, I, seed, workload, device)
+    elif cfg["weights"] == "fp8":
+        out["w_gu"], out["s_gu"], out["w_d"], out["s_d"] = fp8_expert_weights(
+            E, H, I, seed, workload, device)
     else:
         out["w_gu"], out["s_gu"], out["w_d"], out["s_d"] = int8_expert_weights(
             E, H, I, seed, workload, device)

@@ -46,7 +46,7 @@ def exported_symbols():
 
 def test_header_parses():
     fns = header_functions()
-    assert len(fns) == 11, sorted(fns)
+    assert len(fns) == 13, sorted(fns)
 
 
 def test_every_declared_function_is_exported():
@@ -73,7 +73,7 @@ def test_status_strings_and_version():
     for code, name in names.items():
         assert lib.w8a8_status_string(code).decode() == name
     assert lib.w8a8_status_string(99).decode() == "W8A8_UNKNOWN_STATUS"
-    assert lib.w8a8_abi_version() == 1
+    assert lib.w8a8_abi_version() == 2
 
 
 def _shape(T, H, E, k, I):
@@ -149,6 +149,10 @@ def test_forward_checks_workspace_and_alignment():
     assert st == 4
     st = lib.w8a8_moe_forward(sh, ctypes.byref(w), base, base, base + 2 * 65536, 1 << 30, None)
     assert st == 1  # y aliases x
+    bad = _lib.MoeWeights(base, None, base, base, base, base, 7)
+    st = lib.w8a8_moe_forward(sh, ctypes.byref(bad), base, base + 65536, base + 2 * 65536, 1 << 30,
+                              None)
+    assert st == 1 and "code" in lib.w8a8_last_error().decode()  # unknown weight code
 
 
 def test_gemm_and_quant_argument_checks():

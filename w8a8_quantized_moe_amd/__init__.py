@@ -4,6 +4,7 @@ The computation lives in libw8a8moe.so (hand-written HIP kernels behind the C
 ABI of include/w8a8moe.h); this package is its thin Python binding.  Importing
 it fails if the library has not been built: there is no CPU fallback.
 """
-from ._lib import (LIB_PATH, PACK_GATE_UP, PACK_PLAIN, W8A8Error, check, lib)  # noqa: F401
+from ._lib import (CODE_FP8, CODE_INT8, LIB_PATH, PACK_GATE_UP, PACK_PLAIN, W8A8Error, check,  # noqa: F401
+                   lib)
 from .api import (MoEWeights, gemm, gemm_i32, moe_forward, moe_workspace_layout,  # noqa: F401
                   pack_weights, quantize_rows, workspace_views)

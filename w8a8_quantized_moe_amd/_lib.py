@@ -25,6 +25,8 @@ W8A8_ERR_WORKSPACE_TOO_SMALL = 3
 W8A8_ERR_MISALIGNED = 4
 W8A8_ERR_HIP = 5
 
+CODE_INT8 = 0
+CODE_FP8 = 1
 PACK_PLAIN = 0
 PACK_GATE_UP = 1
 
@@ -43,7 +45,7 @@ class MoeShape(ctypes.Structure):
 class MoeWeights(ctypes.Structure):
     _fields_ = [("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
                 ("w_gate_up", ctypes.c_void_p), ("s_gate_up", ctypes.c_void_p),
-                ("w_down", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+                ("w_down", ctypes.c_void_p), ("s_down", ctypes.c_void_p), ("code", ctypes.c_int32)]
 
 
 LAYOUT_FIELDS = ["total_bytes", "x_q", "x_scale", "logits", "topk_ids", "topk_w", "expert_counts",
@@ -62,6 +64,8 @@ SIGNATURES = {
     "w8a8_last_error": (ctypes.c_char_p, []),
     "w8a8_abi_version": (ctypes.c_int, []),
     "w8a8_quantize_rows": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "w8a8_quantize_rows_fp8": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "w8a8_gemm_fp8": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]),
     "w8a8_pack_weights_size": (ctypes.c_int, [_I64, _I64, _I64, ctypes.c_int,
                                               ctypes.POINTER(ctypes.c_size_t)]),
     "w8a8_pack_weights": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.c_int, _P, _P]),

@@ -36,17 +36,20 @@ def _dev(t: torch.Tensor, dtype, name):
 
 
 def quantize_rows(x: torch.Tensor, q: Optional[torch.Tensor] = None,
-                  scale: Optional[torch.Tensor] = None):
-    """Per-row int8 quantisation of a [rows, cols] fp32 matrix (any leading
-    dimension via stride(0)).  Returns (q int8 [rows, cols], scale fp32 [rows])."""
+                  scale: Optional[torch.Tensor] = None, code: int = _lib.CODE_INT8):
+    """Per-row quantisation of a [rows, cols] fp32 matrix (any leading
+    dimension via stride(0)) to int8 codes or (code=CODE_FP8) uint8 E4M3 codes.
+    Returns (q [rows, cols], scale fp32 [rows])."""
     if not x.is_cuda or x.dtype != torch.float32 or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a 2-D fp32 GPU tensor with unit column stride")
     rows, cols = x.shape
+    fp8 = code == _lib.CODE_FP8
     if q is None:
-        q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+        q = torch.empty((rows, cols), dtype=torch.uint8 if fp8 else torch.int8, device=x.device)
     if scale is None:
         scale = torch.empty((rows,), dtype=torch.float32, device=x.device)
-    check(lib.w8a8_quantize_rows(_ptr(x), rows, cols, x.stride(0), _ptr(q), _ptr(scale), _stream()))
+    fn = lib.w8a8_quantize_rows_fp8 if fp8 else lib.w8a8_quantize_rows
+    check(fn(_ptr(x), rows, cols, x.stride(0), _ptr(q), _ptr(scale), _stream()))
     return q, scale
 
 
@@ -54,6 +57,8 @@ def pack_weights(w: torch.Tensor, kind: int = _lib.PACK_PLAIN) -> torch.Tensor:
     """Re-lay int8 weights [groups, n, k] (or [n, k]) into the GEMM tile order."""
     if w.dim() == 2:
         w = w.unsqueeze(0)
+    if w.dtype == torch.uint8:  # FP8 codes: the packing moves bytes
+        w = w.view(torch.int8)
     _dev(w, torch.int8, "w")
     g, n, k = w.shape
     nbytes = ctypes.c_size_t()
@@ -64,13 +69,16 @@ def pack_weights(w: torch.Tensor, kind: int = _lib.PACK_PLAIN) -> torch.Tensor:
 
 
 def gemm(a_q, s_a, b_packed, s_b, N: int, K: int, out=None) -> torch.Tensor:
-    """Dense W8A8 GEMM: out = ((float)(a_q @ b^T) * s_a[:, None]) * s_b[None, :]."""
-    _dev(a_q, torch.int8, "a_q")
+    """Dense W8A8 GEMM: out = ((float)(a_q @ b^T) * s_a[:, None]) * s_b[None, :].
+    int8 a_q: int8 codes (exact int32 accumulation); uint8 a_q: FP8 E4M3 codes
+    (fp32 accumulation), with b packed from codes of the same kind."""
     M = a_q.shape[0]
+    fp8 = a_q.dtype == torch.uint8
+    _dev(a_q, torch.uint8 if fp8 else torch.int8, "a_q")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=a_q.device)
-    check(lib.w8a8_gemm(_ptr(a_q), _ptr(s_a), _ptr(b_packed), _ptr(s_b), M, N, K, _ptr(out),
-                        _stream()))
+    fn = lib.w8a8_gemm_fp8 if fp8 else lib.w8a8_gemm
+    check(fn(_ptr(a_q), _ptr(s_a), _ptr(b_packed), _ptr(s_b), M, N, K, _ptr(out), _stream()))
     return out
 
 
@@ -96,25 +104,29 @@ class MoEWeights:
     s_gate_up: torch.Tensor           # [E, 2I] fp32
     w_down: torch.Tensor              # packed int8 (PLAIN) of [E, H, I]
     s_down: torch.Tensor              # [E, H] fp32
+    code: int = _lib.CODE_INT8        # CODE_INT8 or CODE_FP8 (E4M3 codes)
 
     @classmethod
     def from_int8(cls, router_w, router_b, w_gu, s_gu, w_d, s_d):
-        """From int8 codes [E, 2I, H] / [E, H, I] with per-output-channel scales."""
+        """From int8 codes [E, 2I, H] / [E, H, I] with per-output-channel scales
+        (uint8 tensors: FP8 E4M3 codes, and the layer runs with FP8 codes)."""
         E, twoI, H = w_gu.shape
+        code = _lib.CODE_FP8 if w_gu.dtype == torch.uint8 else _lib.CODE_INT8
         return cls(E, H, twoI // 2, router_w.contiguous(),
                    None if router_b is None else router_b.contiguous(),
                    pack_weights(w_gu.contiguous(), _lib.PACK_GATE_UP), s_gu.contiguous(),
-                   pack_weights(w_d.contiguous(), _lib.PACK_PLAIN), s_d.contiguous())
+                   pack_weights(w_d.contiguous(), _lib.PACK_PLAIN), s_d.contiguous(), code)
 
     @classmethod
-    def from_fp32(cls, router_w, router_b, w_gu_f32, w_d_f32, keep_codes=False):
+    def from_fp32(cls, router_w, router_b, w_gu_f32, w_d_f32, keep_codes=False,
+                  code: int = _lib.CODE_INT8):
         """Quantise fp32 expert weights per output channel with the library's
         row quantiser (offline step), then pack.  With keep_codes the unpacked
-        int8 codes and scales are returned as well."""
+        codes and scales are returned as well."""
         E, twoI, H = w_gu_f32.shape
         I = twoI // 2
-        q_gu, s_gu = quantize_rows(w_gu_f32.reshape(E * twoI, H).contiguous())
-        q_d, s_d = quantize_rows(w_d_f32.reshape(E * H, I).contiguous())
+        q_gu, s_gu = quantize_rows(w_gu_f32.reshape(E * twoI, H).contiguous(), code=code)
+        q_d, s_d = quantize_rows(w_d_f32.reshape(E * H, I).contiguous(), code=code)
         q_gu = q_gu.view(E, twoI, H)
         q_d = q_d.view(E, H, I)
         w = cls.from_int8(router_w, router_b, q_gu, s_gu.view(E, twoI), q_d, s_d.view(E, H))
@@ -126,7 +138,7 @@ class MoEWeights:
         return _lib.MoeWeights(self.router_w.data_ptr(),
                                None if self.router_b is None else self.router_b.data_ptr(),
                                self.w_gate_up.data_ptr(), self.s_gate_up.data_ptr(),
-                               self.w_down.data_ptr(), self.s_down.data_ptr())
+                               self.w_down.data_ptr(), self.s_down.data_ptr(), self.code)
 
 
 def _shape(T, H, E, k, I):

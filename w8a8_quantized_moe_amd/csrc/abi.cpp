@@ -125,10 +125,10 @@ const char* w8a8_status_string(int status) {
 
 const char* w8a8_last_error(void) { return g_last_error.c_str(); }
 
-int w8a8_abi_version(void) { return 1; }
+int w8a8_abi_version(void) { return 2; }
 
-w8a8_status w8a8_quantize_rows(const float* x, int64_t rows, int64_t cols, int64_t ld, int8_t* q,
-                               float* scale, w8a8_stream stream) {
+static w8a8_status quantize_rows_code(const float* x, int64_t rows, int64_t cols, int64_t ld, int8_t* q,
+                                      float* scale, int code, w8a8_stream stream) {
     if (rows < 0 || cols < 0 || ld < 0) return fail(W8A8_ERR_INVALID_ARGUMENT, "negative size");
     if (cols < 1 || cols > (int64_t(1) << 24))
         return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "cols=%lld: need 1 <= cols <= 2^24", (long long)cols);
@@ -137,8 +137,18 @@ w8a8_status w8a8_quantize_rows(const float* x, int64_t rows, int64_t cols, int64
     if (rows == 0) return W8A8_OK;
     if (!x || !q || !scale) return fail(W8A8_ERR_INVALID_ARGUMENT, "NULL pointer");
     if (!aligned(x, 4) || !aligned(scale, 4)) return fail(W8A8_ERR_MISALIGNED, "x/scale not 4-byte aligned");
-    return check_hip(w8a8::launch_quantize_rows(x, rows, cols, ld, q, scale, (hipStream_t)stream),
+    return check_hip(w8a8::launch_quantize_rows(x, rows, cols, ld, q, scale, code, (hipStream_t)stream),
                      "quantize_rows launch");
+}
+
+w8a8_status w8a8_quantize_rows(const float* x, int64_t rows, int64_t cols, int64_t ld, int8_t* q,
+                               float* scale, w8a8_stream stream) {
+    return quantize_rows_code(x, rows, cols, ld, q, scale, w8a8::CODE_INT8, stream);
+}
+
+w8a8_status w8a8_quantize_rows_fp8(const float* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* q,
+                                   float* scale, w8a8_stream stream) {
+    return quantize_rows_code(x, rows, cols, ld, (int8_t*)q, scale, w8a8::CODE_FP8, stream);
 }
 
 w8a8_status w8a8_pack_weights_size(int64_t groups, int64_t n, int64_t k, int kind, size_t* bytes) {
@@ -168,9 +178,9 @@ w8a8_status w8a8_pack_weights(const int8_t* w, int64_t groups, int64_t n, int64_
                      "pack_weights launch");
 }
 
-static w8a8_status dense_gemm(int epi, const int8_t* a_q, const float* s_a, const int8_t* b_packed,
-                              const float* s_b, int64_t M, int64_t N, int64_t K, float* out,
-                              int32_t* out_i32, w8a8_stream stream) {
+static w8a8_status dense_gemm(int epi, int code, const int8_t* a_q, const float* s_a,
+                              const int8_t* b_packed, const float* s_b, int64_t M, int64_t N,
+                              int64_t K, float* out, int32_t* out_i32, w8a8_stream stream) {
     if (M < 0 || N < 0 || K < 0) return fail(W8A8_ERR_INVALID_ARGUMENT, "negative size");
     if (N % 128 != 0 || N < 128 || N > (int64_t(1) << 24))
         return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "N=%lld: need N %% 128 == 0, N >= 128", (long long)N);
@@ -197,19 +207,27 @@ static w8a8_status dense_gemm(int epi, const int8_t* a_q, const float* s_a, cons
     p.out_f32 = out;
     p.out_i32 = out_i32;
     p.a_rows = M;
+    p.code = code;
     const int64_t mt = (M + w8a8::GEMM_BM - 1) / w8a8::GEMM_BM;
     return check_hip(w8a8::launch_gemm(epi, p, mt, (hipStream_t)stream), "gemm launch");
 }
 
 w8a8_status w8a8_gemm(const int8_t* a_q, const float* s_a, const int8_t* b_packed, const float* s_b,
                       int64_t M, int64_t N, int64_t K, float* out, w8a8_stream stream) {
-    return dense_gemm(w8a8::EPI_DENSE_F32, a_q, s_a, b_packed, s_b, M, N, K, out, nullptr, stream);
+    return dense_gemm(w8a8::EPI_DENSE_F32, w8a8::CODE_INT8, a_q, s_a, b_packed, s_b, M, N, K, out,
+                      nullptr, stream);
+}
+
+w8a8_status w8a8_gemm_fp8(const uint8_t* a_q, const float* s_a, const uint8_t* b_packed, const float* s_b,
+                          int64_t M, int64_t N, int64_t K, float* out, w8a8_stream stream) {
+    return dense_gemm(w8a8::EPI_DENSE_F32, w8a8::CODE_FP8, (const int8_t*)a_q, s_a, (const int8_t*)b_packed,
+                      s_b, M, N, K, out, nullptr, stream);
 }
 
 w8a8_status w8a8_gemm_i32(const int8_t* a_q, const int8_t* b_packed, int64_t M, int64_t N,
                           int64_t K, int32_t* acc, w8a8_stream stream) {
-    return dense_gemm(w8a8::EPI_DENSE_I32, a_q, nullptr, b_packed, nullptr, M, N, K, nullptr, acc,
-                      stream);
+    return dense_gemm(w8a8::EPI_DENSE_I32, w8a8::CODE_INT8, a_q, nullptr, b_packed, nullptr, M, N, K,
+                      nullptr, acc, stream);
 }
 
 w8a8_status w8a8_moe_workspace_query(const w8a8_moe_shape* shape, w8a8_moe_workspace_layout* layout) {
@@ -241,6 +259,9 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
         !aligned(wts->s_down, 4) || (wts->router_b && !aligned(wts->router_b, 4)))
         return fail(W8A8_ERR_MISALIGNED, "x, y, router_w and weights must be 16-byte aligned");
     if (!aligned(workspace, 256)) return fail(W8A8_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+    if (wts->code != W8A8_CODE_INT8 && wts->code != W8A8_CODE_FP8_E4M3)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "unknown weight code %d", (int)wts->code);
+    const int code = wts->code == W8A8_CODE_FP8_E4M3 ? w8a8::CODE_FP8 : w8a8::CODE_INT8;
     if (x == y) return fail(W8A8_ERR_INVALID_ARGUMENT, "y must not alias x");
     const MoePlan plan = plan_moe(shape);
     if (workspace_bytes < plan.lay.total_bytes)
@@ -275,7 +296,7 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
 
     // 1. per-token quantisation
     if ((st = mark(0)) != W8A8_OK) return st;
-    st = check_hip(w8a8::launch_quantize_rows(x, T, H, H, x_q, x_scale, s), "quantize x");
+    st = check_hip(w8a8::launch_quantize_rows(x, T, H, H, x_q, x_scale, code, s), "quantize x");
     if (st != W8A8_OK) return st;
 
     // 2-4. router, top-k, permutation
@@ -318,6 +339,7 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     gu.out_f32 = h;
     gu.I = I;
     gu.a_rows = T;
+    gu.code = code;
     if ((st = mark(2)) != W8A8_OK) return st;
     st = check_hip(skinny ? w8a8::launch_gemm_skinny(w8a8::EPI_GATE_UP, gu, max_m_tiles(A, E, bm), s)
                           : w8a8::launch_gemm(w8a8::EPI_GATE_UP, gu, max_m_tiles(A, E, bm), s),
@@ -326,7 +348,7 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
 
     // requantise h per assignment row
     if ((st = mark(3)) != W8A8_OK) return st;
-    st = check_hip(w8a8::launch_quantize_rows(h, A, I, I, h_q, h_scale, s), "requantize h");
+    st = check_hip(w8a8::launch_quantize_rows(h, A, I, I, h_q, h_scale, code, s), "requantize h");
     if (st != W8A8_OK) return st;
 
     // 6. grouped down GEMM, epilogue dequant * routing weight -> o[t*k+j]
@@ -349,6 +371,7 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     dn.route_w = topk_w;
     dn.out_f32 = o;
     dn.a_rows = A;
+    dn.code = code;
     if ((st = mark(4)) != W8A8_OK) return st;
     st = check_hip(skinny ? w8a8::launch_gemm_skinny(w8a8::EPI_DOWN, dn, max_m_tiles(A, E, bm), s)
                           : w8a8::launch_gemm(w8a8::EPI_DOWN, dn, max_m_tiles(A, E, bm), s),

@@ -123,4 +123,36 @@ __device__ __forceinline__ float amax4(float4 v) {
     return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 }
 
+// ---- code types of the quantised operands ----
+// INT8: s = max|x| / 127, q = clamp(rne(x / s), -128, 127)  ([K100AI] 2.1).
+// FP8 E4M3 ([DSV4] 2.1: 4 exponent and 3 mantissa bits, range +-448): s =
+// max|x| / 448, q = E4M3(x / s), the quotient an IEEE fp32 division and the
+// conversion gfx950's v_cvt_pk_fp8_f32 (OCP E4M3FN, round to nearest even).
+// An all-zero row gives s = 0 and code 0 in both.
+template <int CODE>
+__device__ __forceinline__ float code_range() {
+    return CODE == CODE_FP8 ? 448.0f : 127.0f;
+}
+
+// Four codes of one row packed into a 32-bit word (element 0 in the low byte).
+template <int CODE>
+__device__ __forceinline__ uint32_t encode4(const float4& v, float s, float rs) {
+    if (CODE == CODE_INT8)
+        return pack4(quant_fast(v.x, s, rs), quant_fast(v.y, s, rs), quant_fast(v.z, s, rs),
+                     quant_fast(v.w, s, rs));
+    const bool z = (s == 0.0f);
+    const float a = z ? 0.0f : v.x / s, b = z ? 0.0f : v.y / s;
+    const float c = z ? 0.0f : v.z / s, d = z ? 0.0f : v.w / s;
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+template <int CODE>
+__device__ __forceinline__ uint8_t encode1(float v, float s) {
+    if (CODE == CODE_INT8) return (uint8_t)(int8_t)quant_one(v, s);
+    const float a = (s == 0.0f) ? 0.0f : v / s;
+    return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(a, 0.0f, 0, false) & 0xff);
+}
+
 }  // namespace w8a8

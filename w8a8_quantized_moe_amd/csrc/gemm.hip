@@ -1,5 +1,6 @@
-// INT8 x INT8 -> INT32 GEMM on gfx950 matrix cores, dense or grouped by expert,
-// with the scale handling fused into the epilogue.
+// INT8 x INT8 -> INT32 (or FP8 E4M3 x E4M3 -> FP32) GEMM on gfx950 matrix
+// cores, dense or grouped by expert, with the scale handling fused into the
+// epilogue.
 //
 // "W8A8 quantisation of MiniMax-M3 on K100AI", sec. 2.1: the per-token [A,1] x
 // per-channel [1,N] scale outer product is applied inside the GEMM epilogue,
@@ -44,8 +45,9 @@
 namespace w8a8 {
 namespace {
 
-template <int BM, int BN, int WM, int WN, int NS, int EPI>
+template <int BM, int BN, int WM, int WN, int NS, int EPI, int CODE>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
+    typedef typename AccOf<CODE>::type AccT;
     constexpr int NW = WM * WN;                  // waves per workgroup
     constexpr int FM = BM / WM / 16;             // fragment rows per wave
     constexpr int FN = BN / WN / 16;             // fragment cols per wave
@@ -61,6 +63,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     // copy target from other LDS data and drains the pipeline before every
     // LDS read.)
     __shared__ __attribute__((aligned(1024))) int8_t smem[NS * STAGE + 3 * BM * 4 + 16];
+    // the ring through an LDS-typed pointer: copies and fragment reads address
+    // LDS directly, also where the compiler cannot infer the address space
+    // through the stage select
+    const LDS_AS int8_t* lds = (const LDS_AS int8_t*)smem;
     float* row_scale = reinterpret_cast<float*>(smem + NS * STAGE);
     int* row_slot = reinterpret_cast<int*>(smem + NS * STAGE + BM * 4);
     float* row_w = reinterpret_cast<float*>(smem + NS * STAGE + 2 * BM * 4);
@@ -158,7 +164,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
         }
     }
     auto issue = [&](int ks) {
-        const int8_t* stage = smem + (ks % NS) * STAGE;
+        const LDS_AS int8_t* stage = lds + (ks % NS) * STAGE;
 #pragma unroll
         for (int i = 0; i < DPW; ++i)
             dma16(src[i] + (int64_t)ks * stride[i], stage + (wave + NW * i) * 1024);
@@ -166,27 +172,56 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     // MFMA A operand: lane l holds row l%16, 16-byte k-chunk l/16 of the block
     const int a_slot = 4 * (lane & 15) + ((lane >> 4) ^ ((lane >> 2) & 3));
     auto frag_a = [&](int ks, int i) {
-        return *reinterpret_cast<const v4i*>(smem + (ks % NS) * STAGE + (wm * FM + i) * 1024 + a_slot * 16);
+        return *reinterpret_cast<const LDS_AS v4i*>(lds + (ks % NS) * STAGE + (wm * FM + i) * 1024 + a_slot * 16);
     };
     auto frag_b = [&](int ks, int j) {
-        return *reinterpret_cast<const v4i*>(smem + (ks % NS) * STAGE + (NBA + wn * FN + j) * 1024 +
+        return *reinterpret_cast<const LDS_AS v4i*>(lds + (ks % NS) * STAGE + (NBA + wn * FN + j) * 1024 +
                                              lane * 16);
     };
 
     const int nk = K / 64;
-    // prologue: NS-1 stages in flight, stage 0's fragments in registers
+    // FP8 codes run on the 16x16x128 FP8 MFMA (the 16x16x32 one issues at a
+    // quarter of its rate): one instruction takes lane l's 16-byte chunk of two
+    // consecutive stages, so the FP8 variant consumes the ring in stage pairs.
+    constexpr bool PAIRS = (CODE == CODE_FP8);
+    static_assert(!PAIRS || NS == 4, "the FP8 stage pairs need a ring of exactly two pairs");
+    v4i fa[PAIRS ? 1 : FM], fb[PAIRS ? 1 : FN];
+    // FP8: a pair's fragments, the first stage in the low and the second in
+    // the high 16 bytes of the 32-byte MFMA operand
+    v8i fa8[PAIRS ? FM : 1], fb8[PAIRS ? FN : 1];
+    if constexpr (PAIRS) {
+        // prologue: both pairs of the ring in flight, pair 0's fragments in registers
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-        if (s < nk) issue(s);
-    if (nk - 1 >= NS - 2) wait_vmcnt<(NS - 2) * DPW>();
-    else wait_vmcnt<0>();
-    barrier_nofence();
-    v4i fa[FM], fb[FN];
+        for (int s = 0; s < NS; ++s)
+            if (s < nk) issue(s);
+        if (nk >= 4) wait_vmcnt<2 * DPW>();
+        else wait_vmcnt<0>();
+        barrier_nofence();
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-        if (i < fm_active) fa[i] = frag_a(0, i);
+        for (int i = 0; i < FM; ++i)
+            if (i < fm_active) {
+                fa8[i].lo = frag_a(0, i);
+                fa8[i].hi = frag_a(1, i);
+            }
 #pragma unroll
-    for (int j = 0; j < FN; ++j) fb[j] = frag_b(0, j);
+        for (int j = 0; j < FN; ++j) {
+            fb8[j].lo = frag_b(0, j);
+            fb8[j].hi = frag_b(1, j);
+        }
+    } else {
+        // prologue: NS-1 stages in flight, stage 0's fragments in registers
+#pragma unroll
+        for (int s = 0; s < NS - 1; ++s)
+            if (s < nk) issue(s);
+        if (nk - 1 >= NS - 2) wait_vmcnt<(NS - 2) * DPW>();
+        else wait_vmcnt<0>();
+        barrier_nofence();
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            if (i < fm_active) fa[i] = frag_a(0, i);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[j] = frag_b(0, j);
+    }
 
     // ---- epilogue.  Lane l, register r of accumulator block (i, j) holds
     //      row (wm*FM+i)*16 + (l/16)*4 + r, column (wn*FN+j)*16 + l%16.  The
@@ -198,7 +233,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     constexpr int OCOLS = (EPI == EPI_GATE_UP) ? FN * 8 : FN * 16;  // output columns per wave
     constexpr int SROW = OCOLS + 4;                                 // padded staging stride (words)
     static_assert(NW * 32 * SROW * 4 <= NS * STAGE, "epilogue staging fits in the LDS ring");
-    auto epilogue = [&](v4i (&acc)[FM][FN]) {
+    auto epilogue = [&](AccT (&acc)[FM][FN]) {
         __syncthreads();  // the ring is idle; row metadata written before the loop is visible
         uint32_t* stg = reinterpret_cast<uint32_t*>(smem) + wave * (32 * SROW);
         const int col_in_blk = lane & 15;
@@ -244,7 +279,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
                         for (int j = 0; j < FN; ++j) {
                             uint32_t v;
                             if (EPI == EPI_DENSE_I32) {
-                                v = (uint32_t)acc[i][j][r];
+                                v = (uint32_t)(int)acc[i][j][r];
                             } else if (EPI == EPI_DENSE_F32) {
                                 v = __float_as_uint(((float)acc[i][j][r] * row_scale[row]) * s_col[j]);
                             } else {  // EPI_DOWN
@@ -284,13 +319,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     // in from LDS: each A fragment right after its last use, the B fragments
     // once the stage's MFMAs are issued.  F = fragment rows this wave computes: FM for a full
     // tile; in a segment's last, partial tile FM/2 or 0.
-    auto mfma_and_refill = [&](auto f_tag, v4i (&acc)[FM][FN], int next_ks, bool refill) {
+    auto mfma_and_refill = [&](auto f_tag, AccT (&acc)[FM][FN], int next_ks, bool refill) {
         constexpr int F = decltype(f_tag)::value;
 #pragma unroll
         for (int i = 0; i < F; ++i) {
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = mma16<CODE>(fa[i], fb[j], acc[i][j]);
             if (refill) fa[i] = frag_a(next_ks, i);
             // keep each refill next to the MFMAs it follows (hoisting them all
             // would need a second set of A registers)
@@ -299,11 +334,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     };
     auto run = [&](auto f_tag) {
         constexpr int F = decltype(f_tag)::value;
-        v4i acc[FM][FN];
+        AccT acc[FM][FN];
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+            for (int j = 0; j < FN; ++j) acc[i][j] = AccT{};
         int ks = 0;
         // steady state: stage ks+1 landed (NS-3 newer stages may still fly),
         // refill the ring with stage ks+NS-1
@@ -330,9 +365,56 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
         mfma_and_refill(f_tag, acc, 0, false);
         epilogue(acc);
     };
-    if (fm_active > FM / 2) run(std::integral_constant<int, FM>{});
-    else if (fm_active > 0) run(std::integral_constant<int, FM / 2>{});
-    else run(std::integral_constant<int, 0>{});
+    if constexpr (PAIRS) {
+        // FP8: pair q's MFMAs run from registers while pair q+1's fragments
+        // stream in from LDS (each A fragment row right after its MFMAs, the B
+        // fragments after the last row); the copies of pair q+2 go to the two
+        // ring slots pair q left.  The reads ahead are unconditional: past the
+        // last pair they read stale ring slots whose values are never used
+        // (conditional reads would cost register copies at every join).
+        auto run_pairs = [&](auto f_tag) {
+            constexpr int F = decltype(f_tag)::value;
+            AccT acc[FM][FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = AccT{};
+            const int np = nk / 2;
+            for (int q = 0; q < np; ++q) {
+                if (q + 1 < np) {
+                    wait_vmcnt<0>();    // pair q+1 landed (nothing newer is in flight)
+                    barrier_nofence();  // ... for every wave, and every wave holds pair q
+                    if (2 * q + 4 < nk) {
+                        issue(2 * q + 4);
+                        issue(2 * q + 5);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < F; ++i) {
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) acc[i][j] = mma128_fp8(fa8[i], fb8[j], acc[i][j]);
+                    fa8[i].lo = frag_a(2 * q + 2, i);
+                    fa8[i].hi = frag_a(2 * q + 3, i);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (F > 0) {
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        fb8[j].lo = frag_b(2 * q + 2, j);
+                        fb8[j].hi = frag_b(2 * q + 3, j);
+                    }
+                }
+            }
+            epilogue(acc);
+        };
+        if (fm_active > FM / 2) run_pairs(std::integral_constant<int, FM>{});
+        else if (fm_active > 0) run_pairs(std::integral_constant<int, FM / 2>{});
+        else run_pairs(std::integral_constant<int, 0>{});
+    } else {
+        if (fm_active > FM / 2) run(std::integral_constant<int, FM>{});
+        else if (fm_active > 0) run(std::integral_constant<int, FM / 2>{});
+        else run(std::integral_constant<int, 0>{});
+    }
     };
 
     // Tile schedule.  Static (no counters): slot s of XCD x takes tiles s,
@@ -385,11 +467,24 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
 template <int BM, int BN, int WM, int WN, int NS>
 hipError_t launch_tile(int epi, const GemmParams& p, int64_t blocks, hipStream_t s) {
     const dim3 grid((unsigned)blocks), block(WM * WN * 64);
+    if (p.code == CODE_FP8) {
+        if constexpr (BN == 128) {  // the only FP8 tile (gemm_tile_n)
+            switch (epi) {
+                case EPI_DENSE_F32: gemm_i8<BM, BN, WM, WN, NS, EPI_DENSE_F32, CODE_FP8><<<grid, block, 0, s>>>(p); break;
+                case EPI_GATE_UP: gemm_i8<BM, BN, WM, WN, NS, EPI_GATE_UP, CODE_FP8><<<grid, block, 0, s>>>(p); break;
+                case EPI_DOWN: gemm_i8<BM, BN, WM, WN, NS, EPI_DOWN, CODE_FP8><<<grid, block, 0, s>>>(p); break;
+                default: return hipErrorInvalidValue;
+            }
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
+    if (p.code != CODE_INT8) return hipErrorInvalidValue;
     switch (epi) {
-        case EPI_DENSE_F32: gemm_i8<BM, BN, WM, WN, NS, EPI_DENSE_F32><<<grid, block, 0, s>>>(p); break;
-        case EPI_DENSE_I32: gemm_i8<BM, BN, WM, WN, NS, EPI_DENSE_I32><<<grid, block, 0, s>>>(p); break;
-        case EPI_GATE_UP: gemm_i8<BM, BN, WM, WN, NS, EPI_GATE_UP><<<grid, block, 0, s>>>(p); break;
-        case EPI_DOWN: gemm_i8<BM, BN, WM, WN, NS, EPI_DOWN><<<grid, block, 0, s>>>(p); break;
+        case EPI_DENSE_F32: gemm_i8<BM, BN, WM, WN, NS, EPI_DENSE_F32, CODE_INT8><<<grid, block, 0, s>>>(p); break;
+        case EPI_DENSE_I32: gemm_i8<BM, BN, WM, WN, NS, EPI_DENSE_I32, CODE_INT8><<<grid, block, 0, s>>>(p); break;
+        case EPI_GATE_UP: gemm_i8<BM, BN, WM, WN, NS, EPI_GATE_UP, CODE_INT8><<<grid, block, 0, s>>>(p); break;
+        case EPI_DOWN: gemm_i8<BM, BN, WM, WN, NS, EPI_DOWN, CODE_INT8><<<grid, block, 0, s>>>(p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -397,7 +492,10 @@ hipError_t launch_tile(int epi, const GemmParams& p, int64_t blocks, hipStream_t
 
 }  // namespace
 
-int gemm_tile_n(int64_t N) { return (N % 256 == 0) ? 256 : 128; }
+int gemm_tile_n(int64_t N, int code) {
+    // FP8 keeps two stages of fragments in registers: 256x128 tiles
+    return (code == CODE_INT8 && N % 256 == 0) ? 256 : 128;
+}
 
 int device_cu_count() {
     static std::atomic<int> cache[64];
@@ -414,7 +512,7 @@ int device_cu_count() {
 
 hipError_t launch_gemm(int epi, const GemmParams& p_in, int64_t max_m_tiles, hipStream_t s) {
     GemmParams p = p_in;
-    const int bn = gemm_tile_n(p.N);
+    const int bn = gemm_tile_n(p.N, p.code);
     const int nt_all = (int)(p.N / bn);
     if (p.seg_offsets) {
         p.VG = 1;

@@ -8,6 +8,7 @@ namespace w8a8 {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 
 // Row-tile height of the int8 MFMA GEMM (the m-tile unit of the routing's
 // per-expert tile prefix).
@@ -50,13 +51,56 @@ __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" :::
 // LDS read it cannot prove disjoint.  The ring's hazards are handled by hand
 // (explicit vmcnt waits before the workgroup barrier).  Nothing else in the
 // kernel uses M0 (no LDS DMA builtins, no dynamic register indexing).
-__device__ __forceinline__ void dma16(const int8_t* gsrc, const int8_t* lds_wave_base) {
-    const uint32_t lds = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(const LDS_AS int8_t*)lds_wave_base);
+__device__ __forceinline__ void dma16(const int8_t* gsrc, const LDS_AS int8_t* lds_wave_base) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                  :
                  : "v"(gsrc), "s"(lds)
                  : "memory", "m0");
+}
+__device__ __forceinline__ void dma16(const int8_t* gsrc, const int8_t* lds_wave_base) {
+    dma16(gsrc, (const LDS_AS int8_t*)lds_wave_base);
+}
+
+// Code type of the quantised operands.
+enum Code : int {
+    CODE_INT8 = 0,  // int8, int32 accumulation (exact)
+    CODE_FP8 = 1,   // FP8 E4M3 (OCP E4M3FN), fp32 accumulation
+};
+
+// One 16x16 output block += A fragment (16 rows x 64 k) . B fragment (16
+// columns x 64 k), lane l holding row/column l%16 and the 16 k-bytes
+// (l/16)*16 .. +15.  INT8: v_mfma_i32_16x16x64_i8 (int32, exact).  FP8: the
+// 16 bytes of a lane are two 8-byte k groups; one v_mfma_f32_16x16x32_fp8_fp8
+// per group (lane l then holds k-bytes (l/16)*8 .. +7 of its group, the same
+// grouping in both operands), so the two products together cover all 64 k,
+// accumulated in fp32.
+typedef long v2l __attribute__((ext_vector_type(2)));
+template <int CODE>
+struct AccOf {
+    typedef v4i type;
+};
+template <>
+struct AccOf<1> {
+    typedef v4f type;
+};
+template <int CODE>
+__device__ __forceinline__ typename AccOf<CODE>::type mma16(const v4i& a, const v4i& b,
+                                                            const typename AccOf<CODE>::type& c) {
+    if constexpr (CODE == 0) {
+        return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+    } else {
+        const v2l a2 = __builtin_bit_cast(v2l, a), b2 = __builtin_bit_cast(v2l, b);
+        const v4f c1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[0], b2[0], c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[1], b2[1], c1, 0, 0, 0);
+    }
+}
+
+// 16x16x128 FP8 E4M3 x E4M3 MFMA, fp32 accumulator (block scales fixed at 2^0:
+// E8M0 exponent 127).  A and B lanes pair the same byte positions, so the
+// product sums the 128 k of both operands whatever k each byte stands for.
+__device__ __forceinline__ v4f mma128_fp8(const v8i& a, const v8i& b, const v4f& c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
 enum Epilogue : int {
@@ -87,6 +131,7 @@ struct GemmParams {
     int32_t* out_i32;
     int I;               // gate-up: intermediate size (N = 2I)
     int64_t a_rows;      // rows of the A operand (gate-up: T); indices are clamped to it
+    int code;            // CODE_INT8 or CODE_FP8 (both operands)
     int32_t* tile_ctr;   // grouped: 8 zeroed tile counters (stride TILE_CTR_STRIDE), one
                          // queue per XCD, for a persistent launch; nullptr: one tile
                          // per workgroup
@@ -101,7 +146,7 @@ int device_cu_count();
 
 // ---- launchers (each returns the launch status) ----
 hipError_t launch_quantize_rows(const float* x, int64_t rows, int64_t cols, int64_t ld, int8_t* q,
-                                float* scale, hipStream_t s);
+                                float* scale, int code, hipStream_t s);
 
 hipError_t launch_pack_weights(const int8_t* w, int64_t groups, int64_t n, int64_t k, int kind,
                                int8_t* packed, hipStream_t s);

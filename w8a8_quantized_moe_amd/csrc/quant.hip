@@ -1,10 +1,12 @@
-// Per-row dynamic INT8 quantisation (one wave64 per row).
+// Per-row dynamic quantisation to INT8 or FP8 E4M3 codes.
 //
 // "W8A8 quantisation of MiniMax-M3 on K100AI", sec. 2.1: q = clamp(round(x/s),
 // -128, 127) with a per-token scale computed at run time from one extra
 // reduction over the row.  Here s = max|x| / 127 (IEEE fp32 division), the
 // quotient x/s is an IEEE fp32 division and round() is round-half-to-even
-// (v_rndne).  An all-zero row gives s = 0 and all-zero codes.
+// (v_rndne).  An all-zero row gives s = 0 and all-zero codes.  With FP8 codes
+// ("DeepSeek V4 '950' unified FP8 dataflow", sec. 2.1: E4M3, range +-448)
+// s = max|x| / 448 and the code is E4M3(x / s), rounded to nearest even.
 //
 // HBM-bound: each row is read once (cached in VGPRs while its maximum is
 // reduced: one wave per row up to 1024 columns, one 256-thread workgroup per
@@ -17,7 +19,7 @@ namespace {
 
 // Vector path: cols % 4 == 0, ld % 4 == 0, x 16-byte aligned.  VPL float4 per
 // lane stay in registers (rows up to VPL*256 elements).
-template <int VPL>
+template <int CODE, int VPL>
 __global__ __launch_bounds__(256) void quant_rows_cached(const float* __restrict__ x, int64_t rows,
                                                          int cols, int64_t ld, int8_t* __restrict__ q,
                                                          float* __restrict__ scale) {
@@ -39,7 +41,7 @@ __global__ __launch_bounds__(256) void quant_rows_cached(const float* __restrict
         }
     }
     amax = wave_max(amax);
-    const float s = amax / 127.0f;
+    const float s = amax / code_range<CODE>();
     const float rs = 1.0f / s;
     if (lane == 0) scale[row] = s;
     uint32_t* qr = reinterpret_cast<uint32_t*>(q + row * (int64_t)cols);
@@ -47,15 +49,14 @@ __global__ __launch_bounds__(256) void quant_rows_cached(const float* __restrict
     for (int i = 0; i < VPL; ++i) {
         const int c = i * 64 + lane;
         if (c < nv)
-            qr[c] = pack4(quant_fast(v[i].x, s, rs), quant_fast(v[i].y, s, rs),
-                          quant_fast(v[i].z, s, rs), quant_fast(v[i].w, s, rs));
+            qr[c] = encode4<CODE>(v[i], s, rs);
     }
 }
 
 // Long rows (vector path): one 256-thread workgroup per row, VPT float4 per
 // thread held in registers; the row maximum goes through a wave reduction and
 // four LDS slots.
-template <int VPT>
+template <int CODE, int VPT>
 __global__ __launch_bounds__(256) void quant_rows_block(const float* __restrict__ x, int64_t rows,
                                                         int cols, int64_t ld, int8_t* __restrict__ q,
                                                         float* __restrict__ scale) {
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(256) void quant_rows_block(const float* __restrict_
     if (lane == 0) wmax[wv] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-    const float s = amax / 127.0f;
+    const float s = amax / code_range<CODE>();
     const float rs = 1.0f / s;
     if (tid == 0) scale[row] = s;
     uint32_t* qr = reinterpret_cast<uint32_t*>(q + row * (int64_t)cols);
@@ -88,13 +89,13 @@ __global__ __launch_bounds__(256) void quant_rows_block(const float* __restrict_
     for (int i = 0; i < VPT; ++i) {
         const int c = i * 256 + tid;
         if (c < nv)
-            qr[c] = pack4(quant_fast(v[i].x, s, rs), quant_fast(v[i].y, s, rs),
-                          quant_fast(v[i].z, s, rs), quant_fast(v[i].w, s, rs));
+            qr[c] = encode4<CODE>(v[i], s, rs);
     }
 }
 
 // General path: any cols / ld / alignment; the row is read twice (the second
 // read normally hits L2).
+template <int CODE>
 __global__ __launch_bounds__(256) void quant_rows_twopass(const float* __restrict__ x, int64_t rows,
                                                           int64_t cols, int64_t ld,
                                                           int8_t* __restrict__ q,
@@ -106,17 +107,15 @@ __global__ __launch_bounds__(256) void quant_rows_twopass(const float* __restric
     float amax = 0.0f;
     for (int64_t c = lane; c < cols; c += 64) amax = fmaxf(amax, fabsf(xr[c]));
     amax = wave_max(amax);
-    const float s = amax / 127.0f;
+    const float s = amax / code_range<CODE>();
     if (lane == 0) scale[row] = s;
     int8_t* qr = q + row * cols;
-    for (int64_t c = lane; c < cols; c += 64) qr[c] = (int8_t)quant_one(xr[c], s);
+    for (int64_t c = lane; c < cols; c += 64) qr[c] = (int8_t)encode1<CODE>(xr[c], s);
 }
 
-}  // namespace
-
-hipError_t launch_quantize_rows(const float* x, int64_t rows, int64_t cols, int64_t ld, int8_t* q,
-                                float* scale, hipStream_t s) {
-    if (rows == 0) return hipSuccess;
+template <int CODE>
+hipError_t launch_quant(const float* x, int64_t rows, int64_t cols, int64_t ld, int8_t* q,
+                        float* scale, hipStream_t s) {
     const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
     const bool vec = (cols % 4 == 0) && (ld % 4 == 0) && ((uintptr_t)x % 16 == 0) &&
                      ((uintptr_t)q % 4 == 0) && cols <= 8 * 1024;
@@ -125,26 +124,34 @@ hipError_t launch_quantize_rows(const float* x, int64_t rows, int64_t cols, int6
         const int need = (nv + 255) / 256;
         const dim3 g1((unsigned)rows);
         if (need <= 2)
-            quant_rows_block<2><<<g1, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
+            quant_rows_block<CODE, 2><<<g1, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
         else if (need <= 4)
-            quant_rows_block<4><<<g1, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
+            quant_rows_block<CODE, 4><<<g1, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
         else
-            quant_rows_block<8><<<g1, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
+            quant_rows_block<CODE, 8><<<g1, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
     } else if (vec) {
         const int nv = (int)(cols / 4);
         const int need = (nv + 63) / 64;
         if (need <= 1)
-            quant_rows_cached<1><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
+            quant_rows_cached<CODE, 1><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
         else if (need <= 2)
-            quant_rows_cached<2><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
-        else if (need <= 4)
-            quant_rows_cached<4><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
+            quant_rows_cached<CODE, 2><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
         else
-            quant_rows_cached<4><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
+            quant_rows_cached<CODE, 4><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
     } else {
-        quant_rows_twopass<<<grid, block, 0, s>>>(x, rows, cols, ld, q, scale);
+        quant_rows_twopass<CODE><<<grid, block, 0, s>>>(x, rows, cols, ld, q, scale);
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rows(const float* x, int64_t rows, int64_t cols, int64_t ld, int8_t* q,
+                                float* scale, int code, hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    if (code == CODE_FP8) return launch_quant<CODE_FP8>(x, rows, cols, ld, q, scale, s);
+    if (code == CODE_INT8) return launch_quant<CODE_INT8>(x, rows, cols, ld, q, scale, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace w8a8

@@ -27,7 +27,7 @@ namespace {
 
 constexpr int SK_WAVES = 4;  // waves per workgroup (independent of each other)
 
-template <int EPI, int FN, int D>
+template <int EPI, int FN, int D, int CODE>
 __global__ __launch_bounds__(SK_WAVES * 64) void gemm_skinny(GemmParams p) {
     const int lane = threadIdx.x & 63;
     const int64_t item = (int64_t)blockIdx.x * SK_WAVES + (threadIdx.x >> 6);
@@ -35,7 +35,7 @@ __global__ __launch_bounds__(SK_WAVES * 64) void gemm_skinny(GemmParams p) {
     const int64_t total = (int64_t)p.mt_prefix[p.G] * NC;
     if (item >= total) return;  // wave-uniform
 
-    skinny_item<EPI, FN, D>(p, item, NC, lane);
+    skinny_item<EPI, FN, D, CODE>(p, item, NC, lane);
 }
 
 }  // namespace
@@ -46,10 +46,20 @@ hipError_t launch_gemm_skinny(int epi, const GemmParams& p, int64_t max_row_bloc
     const int64_t items = max_row_blocks * (p.N / (16 * FN));
     if (items == 0) return hipSuccess;
     const dim3 grid((unsigned)((items + SK_WAVES - 1) / SK_WAVES)), block(SK_WAVES * 64);
-    switch (epi) {
-        case EPI_GATE_UP: gemm_skinny<EPI_GATE_UP, FN, D><<<grid, block, 0, s>>>(p); break;
-        case EPI_DOWN: gemm_skinny<EPI_DOWN, FN, D><<<grid, block, 0, s>>>(p); break;
-        default: return hipErrorInvalidValue;
+    if (p.code == CODE_FP8) {
+        switch (epi) {
+            case EPI_GATE_UP: gemm_skinny<EPI_GATE_UP, FN, D, CODE_FP8><<<grid, block, 0, s>>>(p); break;
+            case EPI_DOWN: gemm_skinny<EPI_DOWN, FN, D, CODE_FP8><<<grid, block, 0, s>>>(p); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else if (p.code == CODE_INT8) {
+        switch (epi) {
+            case EPI_GATE_UP: gemm_skinny<EPI_GATE_UP, FN, D, CODE_INT8><<<grid, block, 0, s>>>(p); break;
+            case EPI_DOWN: gemm_skinny<EPI_DOWN, FN, D, CODE_INT8><<<grid, block, 0, s>>>(p); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }

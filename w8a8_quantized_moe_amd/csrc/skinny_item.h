@@ -17,7 +17,7 @@ namespace w8a8 {
 // item: (row block, column block) index in the expert-major order of the
 // routing's per-row-block table, row blocks of an expert fastest; NC: column
 // blocks (N / (16 * FN)).  The caller guarantees item < row blocks * NC.
-template <int EPI, int FN, int D>
+template <int EPI, int FN, int D, int CODE>
 __device__ __forceinline__ void skinny_item(const GemmParams& p, const int64_t item, const int NC,
                                             const int lane) {
     // expert of this item: one load from the routing's per-row-block table
@@ -62,13 +62,13 @@ __device__ __forceinline__ void skinny_item(const GemmParams& p, const int64_t i
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    v4i acc[FN];
+    typename AccOf<CODE>::type acc[FN];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[j] = v4i{0, 0, 0, 0};
+    for (int j = 0; j < FN; ++j) acc[j] = typename AccOf<CODE>::type{};
     auto mfma = [&](int slot) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-            acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[slot], rbf[slot][j], acc[j], 0, 0, 0);
+            acc[j] = mma16<CODE>(ra[slot], rbf[slot][j], acc[j]);
     };
     // steady state without branches, so the compiler waits only for the
     // oldest stage (D-1 stages of loads stay in flight)
