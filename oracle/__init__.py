@@ -79,6 +79,8 @@ def _load():
     lib.oracle_gemm_fp8.argtypes = [P, P, I64, I64, I64, P]
     lib.oracle_dense_fp8.argtypes = [P, P, P, P, I64, I64, I64, P]
     lib.oracle_expert_ffn_fp8.argtypes = [I64, P, P, P, P, P, I64, I64, P, P, P, P, P, P, P, P, P, P]
+    lib.oracle_quantize_rows_ex.argtypes = [P, I64, I64, I64, P, ctypes.c_int, ctypes.c_float,
+                                            ctypes.c_int, P, P]
     _lib = lib
     return lib
 
@@ -263,6 +265,27 @@ def quantize_rows_fp8(x):
     return q, s
 
 
+SCALE_MODES = {"dynamic": 0, "clipped": 1, "static": 2}
+
+
+def quantize_rows_ex(x, col_mul=None, mode="dynamic", clip=0.0, code="int8"):
+    """Per-row quantisation with an optional per-column factor (SmoothQuant,
+    K100AI page sec. 2.2) and a clipped or static scale (K100AI sec. 2.2,
+    DeepSeek V4 page sec. 3.1); see oracle.c.  Returns (codes, scales)."""
+    x = _c(x, np.float32)
+    if x.ndim == 1:
+        x = x[None, :]
+    rows, cols = x.shape
+    m = None if col_mul is None else _c(col_mul, np.float32)
+    assert m is None or m.shape == (cols,)
+    fp8 = code == "fp8"
+    q = np.empty((rows, cols), np.uint8 if fp8 else np.int8)
+    s = np.empty((rows,), np.float32)
+    _load().oracle_quantize_rows_ex(_p(x), rows, cols, cols, None if m is None else _p(m),
+                                    SCALE_MODES[mode], float(clip), int(fp8), _p(q), _p(s))
+    return q, s
+
+
 def gemm_fp8(a, b):
     """Exact accumulator sum_k E4M3(a) * E4M3(b) in float64; a [M, K], b [N, K] uint8 codes."""
     a = _c(a, np.uint8)
@@ -326,7 +349,8 @@ def expert_ffn_fp8(a_token, a_expert, a_weight, x_q, s_x, w_gu, s_gu, w_d, s_d, 
 # the whole layer
 # --------------------------------------------------------------------------
 def moe_forward(x, wr, bias, w_gu_q, s_gu, w_d_q, s_d, k, tokens=None, want_acc=False,
-                want_h=False, route_tokens=None, code="int8"):
+                want_h=False, route_tokens=None, code="int8", x_smooth=None, x_scale_mode="dynamic",
+                x_clip=0.0):
     """The W8A8 MoE expert layer, step by step.
 
     x      [T, H]   float32 activations
@@ -335,6 +359,9 @@ def moe_forward(x, wr, bias, w_gu_q, s_gu, w_d_q, s_d, k, tokens=None, want_acc=
     w_d_q  [E, H, I]  int8, s_d [E, H] f32
     code   "int8" (the codes above are int8) or "fp8" (uint8 E4M3 codes; the
            activations and h are then quantised to E4M3 as well)
+    x_smooth, x_scale_mode, x_clip: the activation quantisation options of
+           quantize_rows_ex (the weights' input channels then carry the
+           inverse factor; the router reads the unsmoothed x)
 
     ``tokens``: optional sorted subset of token indices for which the expert
     FFN, the outputs o and y are computed (tokens are independent, so a
@@ -350,7 +377,10 @@ def moe_forward(x, wr, bias, w_gu_q, s_gu, w_d_q, s_d, k, tokens=None, want_acc=
     T, H = x.shape
     E = wr.shape[0]
     assert code in ("int8", "fp8")
-    x_q, s_x = quantize_rows(x) if code == "int8" else quantize_rows_fp8(x)
+    if x_smooth is None and x_scale_mode == "dynamic":
+        x_q, s_x = quantize_rows(x) if code == "int8" else quantize_rows_fp8(x)
+    else:
+        x_q, s_x = quantize_rows_ex(x, x_smooth, x_scale_mode, x_clip, code)
     logits = router_logits(x, wr, bias)
     ids, w = topk_softmax(logits, k)
     counts, offsets, sorted_assign = permute(ids, E)

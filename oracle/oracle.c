@@ -338,6 +338,67 @@ ORACLE_API void oracle_quantize_rows_fp8(const float* x, int64_t rows, int64_t c
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Activation scales beyond the per-token absmax.                            */
+/*                                                                          */
+/* [K100AI] sec. 2.2 (SmoothQuant): a per-channel factor reshapes the        */
+/* activations so that their outlier channels flatten, and the weights take  */
+/* the inverse factor on the same input channel, which leaves the product    */
+/* unchanged.  Here the factor is a given vector col_mul[cols] (choosing it  */
+/* needs calibration data): x'[c] = x[c] * col_mul[c] (one fp32 product)     */
+/* before the scale is taken; the weights are quantised with 1/col_mul.      */
+/*                                                                          */
+/* [K100AI] sec. 2.2 and [DSV4] sec. 3.1: a calibrated bound (a high         */
+/* percentile times a safety factor) in place of the row maximum; [DSV4]     */
+/* sec. 3.1 keeps a static part (that bound) and a dynamic part (the         */
+/* per-token scale computed at run time).  Readings adopted:                 */
+/*   mode 0, dynamic:  s = max|x'| / Q                                       */
+/*   mode 1, clipped:  s = min(max|x'|, clip) / Q   (the static bound caps   */
+/*                     the dynamic per-token scale)                          */
+/*   mode 2, static:   s = clip / Q for every row                            */
+/* with Q = 127 (INT8) or 448 (FP8 E4M3).  Values beyond the scale's range   */
+/* saturate: INT8 clamps to [-128, 127], E4M3 to +-448.                      */
+/* ------------------------------------------------------------------------ */
+ORACLE_API void oracle_quantize_rows_ex(const float* x, int64_t rows, int64_t cols, int64_t ld,
+                                        const float* col_mul, int mode, float clip, int fp8,
+                                        void* q_out, float* scale) {
+#pragma omp parallel
+    {
+        float* xs = (float*)malloc((size_t)(cols > 0 ? cols : 1) * sizeof(float));
+#pragma omp for schedule(static)
+        for (int64_t r = 0; r < rows; ++r) {
+            const float* xr = x + r * ld;
+            float amax = 0.0f;
+            for (int64_t c = 0; c < cols; ++c) {
+                xs[c] = col_mul ? xr[c] * col_mul[c] : xr[c];
+                if (fabsf(xs[c]) > amax) amax = fabsf(xs[c]);
+            }
+            float base = amax;
+            if (mode == 1 && clip < amax) base = clip;
+            if (mode == 2) base = clip;
+            const float s = base / (fp8 ? 448.0f : 127.0f);
+            scale[r] = s;
+            for (int64_t c = 0; c < cols; ++c) {
+                if (fp8) {
+                    uint8_t* q = (uint8_t*)q_out + r * cols;
+                    q[c] = (s == 0.0f) ? 0x00 : oracle_e4m3_encode(xs[c] / s);
+                } else {
+                    int8_t* q = (int8_t*)q_out + r * cols;
+                    if (s == 0.0f) {
+                        q[c] = 0;
+                        continue;
+                    }
+                    float v = nearbyintf(xs[c] / s);
+                    if (v > 127.0f) v = 127.0f;
+                    if (v < -128.0f) v = -128.0f;
+                    q[c] = (int8_t)v;
+                }
+            }
+        }
+        free(xs);
+    }
+}
+
 /* FP8 GEMM accumulator: acc[m][n] = sum_k E4M3(a[m][k]) * E4M3(b[n][k]) in
  * fp64.  Products of two E4M3 values have at most 8 significant bits and
  * magnitudes in [2^-18, 448^2]; a sum of up to 2^13 of them needs at most 49

@@ -442,3 +442,94 @@ def test_fp8_single_expert_reduces_to_dense_chain():
     assert np.array_equal(r["x_q"], xq) and np.array_equal(r["h"], h)
     assert np.array_equal(r["h_q"], hq) and np.array_equal(r["s_h"], sh)
     assert np.array_equal(r["y"], o)
+
+
+# ------------------------------------------- smoothing vector and static/clipped scales
+def _scale_of(expr):
+    num, _, den = expr.partition("/")
+    return np.float32(num) / np.float32(den) if den else np.float32(num)
+
+
+def test_scale_options_hand_worked():
+    g = _gold("scale_options_pins.json")
+    for c in g["cases"]:
+        m = None if c["m"] is None else np.array(c["m"], np.float32)
+        q, s = oracle.quantize_rows_ex(np.array(c["x"], np.float32), m, c["mode"], c["clip"], c["code"])
+        assert s[0] == _scale_of(c["s"]), c
+        assert q[0].tolist() == c["q"], c
+
+
+@pytest.mark.parametrize("code", ["int8", "fp8"])
+def test_scale_options_reduce_to_plain_quantisation(code):
+    """m = 1 with the dynamic scale, a clip at or above every row maximum, and a
+    static scale equal to a single row's maximum all give plain absmax codes."""
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((9, 300)) * np.exp(rng.standard_normal((9, 1)))).astype(np.float32)
+    plain = oracle.quantize_rows if code == "int8" else oracle.quantize_rows_fp8
+    q0, s0 = plain(x)
+    for kw in (dict(col_mul=np.ones(300, np.float32)),
+               dict(mode="clipped", clip=float(np.abs(x).max())),
+               dict(mode="clipped", clip=1e30)):
+        q, s = oracle.quantize_rows_ex(x, code=code, **kw)
+        assert np.array_equal(q, q0) and np.array_equal(s, s0), kw
+    amax = np.abs(x[3]).max()
+    q, s = oracle.quantize_rows_ex(x[3:4], mode="static", clip=float(amax), code=code)
+    assert np.array_equal(q[0], q0[3]) and s[0] == s0[3]
+
+
+def test_smoothing_is_a_per_column_factor():
+    """Smoothing by m equals plain quantisation of x * m (the product taken in
+    fp32); a power-of-two factor on one column moves only that column's values
+    (exactly) until it takes over the row maximum."""
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((5, 64)).astype(np.float32)
+    m = np.exp2(rng.integers(-3, 4, 64)).astype(np.float32)
+    q, s = oracle.quantize_rows_ex(x, m)
+    q0, s0 = oracle.quantize_rows(x * m)
+    assert np.array_equal(q, q0) and np.array_equal(s, s0)
+    # a column's factor that is the row's own maximum ratio: that column becomes +-127
+    r = 2
+    c = int(np.argmin(np.abs(x[r])))
+    m2 = np.ones(64, np.float32)
+    m2[c] = np.float32(np.abs(x[r]).max() / abs(x[r, c])) * np.float32(4.0)
+    q2, _ = oracle.quantize_rows_ex(x[r:r + 1], m2)
+    assert abs(int(q2[0, c])) == 127
+
+
+def test_clipped_codes_saturate():
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((6, 256)) * 10).astype(np.float32)
+    clip = 5.0
+    q, s = oracle.quantize_rows_ex(x, mode="clipped", clip=clip)
+    assert np.all(s == np.float32(clip) / np.float32(127))
+    assert np.all(q[x >= clip] == 127) and np.all(q[x <= -clip * 128 / 127] == -128)
+    qf, sf = oracle.quantize_rows_ex(x, mode="clipped", clip=clip, code="fp8")
+    big = np.abs(x) >= clip
+    assert np.all((qf[big] & 0x7F) == 0x7E)  # saturated at 448
+    assert np.all((qf[big] >> 7) == (x[big] < 0))
+
+
+def test_moe_smoothing_equivalence_in_real_arithmetic():
+    """SmoothQuant leaves the product unchanged: with activations on the int8
+    grid (scale 1), a factor m = 1/2 on every column but the first, and the
+    weights' input channels carrying 1/m = 2, the gate-up accumulators equal
+    the unsmoothed ones exactly, so the whole layer's output is identical."""
+    rng = np.random.default_rng(10)
+    T, H, E, k, I = 6, 128, 4, 2, 128
+    x = (2 * rng.integers(-63, 64, (T, H))).astype(np.float32)
+    x[:, 0] = 127.0  # each row's maximum: scale 1, x is its own code (also after smoothing)
+    wr = rng.standard_normal((E, H)).astype(np.float32)
+    w_gu = rng.integers(-63, 64, (E, 2 * I, H)).astype(np.int8)
+    w_d = rng.integers(-127, 128, (E, H, I)).astype(np.int8)
+    s_gu = np.full((E, 2 * I), 1e-4, np.float32)
+    s_d = np.full((E, H), 1e-3, np.float32)
+    m = np.full(H, 0.5, np.float32)
+    m[0] = 1.0
+    w_gu_s = w_gu.copy()
+    w_gu_s[:, :, 1:] *= 2
+    ref = oracle.moe_forward(x, wr, None, w_gu, s_gu, w_d, s_d, k, want_acc=True)
+    sm = oracle.moe_forward(x, wr, None, w_gu_s, s_gu, w_d, s_d, k, x_smooth=m, want_acc=True)
+    assert np.array_equal(sm["x_q"][:, 1:], ref["x_q"][:, 1:] // 2)
+    assert np.array_equal(sm["ids"], ref["ids"])  # the router reads the unsmoothed x
+    assert np.array_equal(sm["acc_gu"], ref["acc_gu"])
+    assert np.array_equal(sm["y"], ref["y"])
