@@ -13,16 +13,19 @@
  *            deployment guide", sec. 2.1 (q = clamp(round(x/s), -128, 127),
  *            per-token activation scales, per-channel weight scales, the
  *            [A,1] x [1,N] scale outer product applied inside the GEMM
- *            epilogue), sec. 3.1 (batch the small per-expert GEMMs),
+ *            epilogue), sec. 2.2 (SmoothQuant factor, percentile-based
+ *            activation bounds), sec. 3.1 (batch the small per-expert GEMMs),
  *            sec. 3.2 (pre-planned buffers for the routing reorder).
  *  [HUNYUAN] "Tencent Hunyuan AI Infra: inference optimisation of a
  *            100B-parameter model on Hopper GPUs", sec. 1.3 (FusedMoE:
  *            gate, top-k, index preparation into contiguous per-expert
  *            segments, gate-up GEMM reading the input through the routing
  *            index, expert GEMM, weighted combine).
- *  [DSV4]    "DeepSeek V4 '950' unified FP8 dataflow on H100", sec. 2.3
+ *  [DSV4]    "DeepSeek V4 '950' unified FP8 dataflow on H100", sec. 2.1
+ *            (E4M3 codes), sec. 2.3
  *            (low-precision inputs, wide accumulator, requantised output),
- *            sec. 2.4 (weight scales per output channel), sec. 4.1 (router
+ *            sec. 2.4 (weight scales per output channel), sec. 3.1 (static
+ *            and dynamic parts of the activation scale), sec. 4.1 (router
  *            kept in fp32).
  *
  * Status codes: every entry point returns a w8a8_status.  On an error no
@@ -67,7 +70,7 @@ W8A8_API const char* w8a8_status_string(int status);
 /* Thread-local detail of the last non-OK status returned on this thread. */
 W8A8_API const char* w8a8_last_error(void);
 
-/* ABI version of this header: 2. */
+/* ABI version of this header: 3. */
 W8A8_API int w8a8_abi_version(void);
 
 /* -------------------------------------------------------------------------
@@ -106,6 +109,33 @@ enum { W8A8_CODE_INT8 = 0, W8A8_CODE_FP8_E4M3 = 1 };
  * as for w8a8_quantize_rows; q holds uint8 E4M3 codes. */
 W8A8_API w8a8_status w8a8_quantize_rows_fp8(const float* x, int64_t rows, int64_t cols, int64_t ld,
                                             uint8_t* q, float* scale, w8a8_stream stream);
+
+/* Activation-scale options ([K100AI] sec. 2.2: SmoothQuant's per-channel
+ * factor, and a high percentile times a safety factor in place of absmax;
+ * [DSV4] sec. 3.1: an activation scale with a static part and a dynamic
+ * per-token part).  With x'[r][c] = x[r][c] * col_mul[c] (one fp32 product;
+ * x' = x when col_mul is NULL) and Q = 127 (INT8) or 448 (E4M3):
+ *   W8A8_SCALE_DYNAMIC  s[r] = max_c |x'[r][c]| / Q       (w8a8_quantize_rows)
+ *   W8A8_SCALE_CLIPPED  s[r] = min(max_c |x'[r][c]|, clip) / Q
+ *   W8A8_SCALE_STATIC   s[r] = clip / Q
+ * and the codes of x'/s as in w8a8_quantize_rows / _fp8, saturating where
+ * |x'/s| exceeds the range (INT8: clamp to [-128, 127]; E4M3: +-448).  The
+ * factor and the bound come from calibration (not done here).  For the
+ * weights of a smoothed layer the caller quantises the weight rows with
+ * col_mul = 1 / factor (the inverse on each input channel), which leaves the
+ * product unchanged. */
+enum { W8A8_SCALE_DYNAMIC = 0, W8A8_SCALE_CLIPPED = 1, W8A8_SCALE_STATIC = 2 };
+
+/* Per-row quantisation with the options above.  col_mul: NULL or [cols]
+ * fp32 device array (4-byte aligned; 16-byte alignment takes the vector
+ * path); scale_mode: a W8A8_SCALE_* value; clip: positive and finite for the
+ * clipped and static modes, ignored for the dynamic one; code:
+ * W8A8_CODE_INT8 (q is int8) or W8A8_CODE_FP8_E4M3 (q is uint8 E4M3).  Other
+ * arguments, limits and errors as for w8a8_quantize_rows;
+ * W8A8_ERR_INVALID_ARGUMENT for an unknown mode or code or a bad clip. */
+W8A8_API w8a8_status w8a8_quantize_rows_ex(const float* x, int64_t rows, int64_t cols, int64_t ld,
+                                           const float* col_mul, int32_t scale_mode, float clip,
+                                           int32_t code, void* q, float* scale, w8a8_stream stream);
 
 /* -------------------------------------------------------------------------
  * Weight packing.  The GEMM kernels read the int8 weight operand in a
@@ -209,6 +239,13 @@ typedef struct {
     const float* s_down;
     int32_t code;  /* W8A8_CODE_INT8 or W8A8_CODE_FP8_E4M3: the code of w_gate_up
                       and w_down, and the code the layer quantises x and h to */
+    /* Options of the per-token quantisation of x (see w8a8_quantize_rows_ex;
+     * zero-initialised: plain dynamic absmax).  x_smooth: NULL or [H] fp32,
+     * 16-byte aligned; w_gate_up must then hold the codes of the weights with
+     * 1/x_smooth on their input channels.  The router reads the unsmoothed x. */
+    const float* x_smooth;
+    int32_t x_scale_mode;
+    float x_clip;
 } w8a8_moe_weights;
 
 /* Byte offsets of the intermediates inside the workspace. */

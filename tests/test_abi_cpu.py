@@ -46,7 +46,7 @@ def exported_symbols():
 
 def test_header_parses():
     fns = header_functions()
-    assert len(fns) == 13, sorted(fns)
+    assert len(fns) == 14, sorted(fns)
 
 
 def test_every_declared_function_is_exported():
@@ -73,7 +73,7 @@ def test_status_strings_and_version():
     for code, name in names.items():
         assert lib.w8a8_status_string(code).decode() == name
     assert lib.w8a8_status_string(99).decode() == "W8A8_UNKNOWN_STATUS"
-    assert lib.w8a8_abi_version() == 2
+    assert lib.w8a8_abi_version() == 3
 
 
 def _shape(T, H, E, k, I):
@@ -149,6 +149,14 @@ def test_forward_checks_workspace_and_alignment():
     assert st == 4
     st = lib.w8a8_moe_forward(sh, ctypes.byref(w), base, base, base + 2 * 65536, 1 << 30, None)
     assert st == 1  # y aliases x
+    smooth_bad = _lib.MoeWeights(base, None, base, base, base, base, 0, base + 4, 0, 0.0)
+    st = lib.w8a8_moe_forward(sh, ctypes.byref(smooth_bad), base, base + 65536, base + 2 * 65536,
+                              1 << 30, None)
+    assert st == 4  # x_smooth must be 16-byte aligned
+    clip_bad = _lib.MoeWeights(base, None, base, base, base, base, 0, None, 2, -1.0)
+    st = lib.w8a8_moe_forward(sh, ctypes.byref(clip_bad), base, base + 65536, base + 2 * 65536,
+                              1 << 30, None)
+    assert st == 1 and "clip" in lib.w8a8_last_error().decode()
     bad = _lib.MoeWeights(base, None, base, base, base, base, 7)
     st = lib.w8a8_moe_forward(sh, ctypes.byref(bad), base, base + 65536, base + 2 * 65536, 1 << 30,
                               None)
@@ -168,6 +176,14 @@ def test_gemm_and_quant_argument_checks():
     assert lib.w8a8_quantize_rows(base, 4, 16, 8, base, base, None) == 1           # ld < cols
     assert lib.w8a8_quantize_rows(None, 0, 16, 16, None, None, None) == 0          # rows = 0
     assert lib.w8a8_quantize_rows(base + 2, 4, 16, 16, base, base, None) == 4
+    # scale options: unknown mode, missing or non-finite bound, unknown code, misaligned factor
+    assert lib.w8a8_quantize_rows_ex(base, 4, 16, 16, None, 3, 1.0, 0, base, base, None) == 1
+    assert lib.w8a8_quantize_rows_ex(base, 4, 16, 16, None, 1, 0.0, 0, base, base, None) == 1
+    assert lib.w8a8_quantize_rows_ex(base, 4, 16, 16, None, 2, float("inf"), 0, base, base, None) == 1
+    assert lib.w8a8_quantize_rows_ex(base, 4, 16, 16, None, 2, float("nan"), 0, base, base, None) == 1
+    assert lib.w8a8_quantize_rows_ex(base, 4, 16, 16, None, 0, 0.0, 5, base, base, None) == 1
+    assert lib.w8a8_quantize_rows_ex(base, 4, 16, 16, base + 2, 0, 0.0, 0, base, base, None) == 4
+    assert lib.w8a8_quantize_rows_ex(None, 0, 16, 16, None, 1, 2.0, 1, None, None, None) == 0
 
 
 def test_pack_size():

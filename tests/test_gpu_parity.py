@@ -119,14 +119,27 @@ def test_dense_workload_sampled(w8):
 
 
 # ------------------------------------------------------------------ MoE layer
-def _weights(w8, inp):
+MODES = {"dynamic": 0, "clipped": 1, "static": 2}
+
+
+def _qkw(w8, qopts):
+    """Layer options of the x quantisation for the binding (qopts: oracle names)."""
+    if not qopts:
+        return {}
+    sm = qopts.get("x_smooth")
+    return dict(x_smooth=None if sm is None else torch.from_numpy(sm).cuda(),
+                x_scale_mode=MODES[qopts.get("x_scale_mode", "dynamic")],
+                x_clip=qopts.get("x_clip", 0.0))
+
+
+def _weights(w8, inp, qopts=None):
     if "w_gu_f32" in inp:
         wts, codes = w8.MoEWeights.from_fp32(inp["wr"], inp["b"], inp["w_gu_f32"], inp["w_d_f32"],
-                                             keep_codes=True)
+                                             keep_codes=True, **_qkw(w8, qopts))
         return wts, codes
     codes = dict(w_gu=inp["w_gu"], s_gu=inp["s_gu"], w_d=inp["w_d"], s_d=inp["s_d"])
     return w8.MoEWeights.from_int8(inp["wr"], inp["b"], inp["w_gu"], inp["s_gu"], inp["w_d"],
-                                   inp["s_d"]), codes
+                                   inp["s_d"], **_qkw(w8, qopts)), codes
 
 
 def _gpu_moe(w8, inp, wts):
@@ -140,13 +153,19 @@ def _gpu_moe(w8, inp, wts):
     return g
 
 
-def _oracle_codes(inp, codes):
+def _oracle_codes(inp, codes, qopts=None):
     """The oracle's own int8 weights: for fp32 weights it quantises them itself
-    (and the test checks the GPU's offline quantisation against that)."""
+    (and the test checks the GPU's offline quantisation against that; with a
+    smoothing vector m the gate-up weights take 1/m on their input channels)."""
     if "w_gu_f32" in inp:
         E, twoI, H = inp["w_gu_f32"].shape
         I = twoI // 2
-        qg, sg = oracle.quantize_rows(to_np(inp["w_gu_f32"]).reshape(E * twoI, H))
+        sm = (qopts or {}).get("x_smooth")
+        if sm is None:
+            qg, sg = oracle.quantize_rows(to_np(inp["w_gu_f32"]).reshape(E * twoI, H))
+        else:
+            qg, sg = oracle.quantize_rows_ex(to_np(inp["w_gu_f32"]).reshape(E * twoI, H),
+                                             col_mul=np.float32(1.0) / sm)
         qd, sd = oracle.quantize_rows(to_np(inp["w_d_f32"]).reshape(E * H, I))
         ora = dict(w_gu=qg.reshape(E, twoI, H), s_gu=sg.reshape(E, twoI),
                    w_d=qd.reshape(E, H, I), s_d=sd.reshape(E, H))
@@ -156,16 +175,17 @@ def _oracle_codes(inp, codes):
     return {n: to_np(v) for n, v in codes.items()}
 
 
-def check_moe(w8, inp, tokens=None, report=None):
+def check_moe(w8, inp, tokens=None, report=None, qopts=None):
     T, H, E, k, I = inp["T"], inp["H"], inp["E"], inp["k"], inp["I"]
-    _say(f"moe T={T} H={H} E={E} k={k} I={I} tokens={'all' if tokens is None else len(tokens)}")
-    wts, codes = _weights(w8, inp)
+    _say(f"moe T={T} H={H} E={E} k={k} I={I} tokens={'all' if tokens is None else len(tokens)}"
+         f"{'' if not qopts else ' x options ' + str(sorted(qopts))}")
+    wts, codes = _weights(w8, inp, qopts)
     g = _gpu_moe(w8, inp, wts)
-    oc = _oracle_codes(inp, codes)
+    oc = _oracle_codes(inp, codes, qopts)
     x = to_np(inp["x"])
     b = to_np(inp["b"])
     o = oracle.moe_forward(x, to_np(inp["wr"]), b, oc["w_gu"], oc["s_gu"], oc["w_d"], oc["s_d"], k,
-                           tokens=tokens, want_h=True)
+                           tokens=tokens, want_h=True, **(qopts or {}))
     tok = o["tokens"]
 
     # 1. per-token quantisation: exact
@@ -370,3 +390,63 @@ def test_quantize_rows_half_integer_and_tiny_scales(w8):
         qo, so = oracle.quantize_rows(xs)
         assert np.array_equal(to_np(sc), so)
         assert np.array_equal(to_np(q), qo)
+
+
+# ------------------------------------------- activation-scale options (smoothing, clip, static)
+QEX_SHAPES = [(5, 100), (33, 1024), (7, 1028), (6, 4096), (3, 8192), (2, 10001), (4, 8200)]
+
+
+@pytest.mark.parametrize("rows,cols", QEX_SHAPES)
+@pytest.mark.parametrize("code", ["int8", "fp8"])
+def test_quantize_rows_ex_bitexact(w8, rows, cols, code):
+    """Smoothing factor, clipped and static scales: codes and scales equal the
+    oracle's bit for bit on every kernel path (register-cached rows, one
+    workgroup per row, and the general two-pass path)."""
+    _say(f"quantize_rows_ex rows={rows} cols={cols} code={code}")
+    rng = np.random.default_rng(rows * 31 + cols)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x[:, :: max(1, cols // 11)] *= 40.0
+    m = (np.exp2(rng.integers(-3, 4, cols)) * rng.uniform(0.5, 2.0, cols)).astype(np.float32)
+    amax = np.abs(x * m).max(axis=1)
+    clip = float(np.median(amax)) * 0.7
+    xd = torch.from_numpy(x).cuda()
+    md = torch.from_numpy(m).cuda()
+    c = w8.CODE_FP8 if code == "fp8" else w8.CODE_INT8
+    for mode in ("dynamic", "clipped", "static"):
+        for use_m in (False, True):
+            q, s = w8.quantize_rows(xd, code=c, col_mul=md if use_m else None, scale_mode=MODES[mode],
+                                    clip=clip)
+            qo, so = oracle.quantize_rows_ex(x, m if use_m else None, mode, clip, code)
+            assert np.array_equal(to_np(s), so), (mode, use_m)
+            qg = to_np(q)
+            assert np.array_equal(qg.view(qo.dtype), qo), (mode, use_m, int((qg.view(qo.dtype) != qo).sum()))
+
+
+@pytest.mark.parametrize("case", [
+    dict(T=100, H=256, E=16, k=4, I=256, weights="fp32", mode="clipped", smooth=True),
+    dict(T=300, H=256, E=8, k=2, I=256, weights="fp32", mode="static", smooth=True),
+    dict(T=64, H=512, E=8, k=2, I=128, weights="int8", mode="clipped", smooth=False),
+], ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_moe_with_scale_options(w8, case):
+    """The whole layer with a smoothing vector on x (the gate-up weights
+    quantised with its inverse) and a clipped or static x scale, against the
+    oracle at the INT8 bar (x codes exact, routing, h, codes, o, y)."""
+    case = dict(case)
+    mode, smooth = case.pop("mode"), case.pop("smooth")
+    over = dict(n_outlier=2, outlier_scale=20.0, bf16_x=False, bias="zero")
+    over.update(case)
+    inp = synth.moe_inputs("edge", device="cuda", **over)
+    H = inp["H"]
+    rng = np.random.default_rng(H)
+    qopts = dict(x_scale_mode=mode)
+    x = to_np(inp["x"])
+    if smooth:
+        m = (1.0 / np.sqrt(np.abs(x).max(axis=0) + 1e-3)).astype(np.float32)  # flattens outlier columns
+        m *= rng.uniform(0.9, 1.1, H).astype(np.float32)
+        qopts["x_smooth"] = m
+        xs = x * m
+    else:
+        xs = x
+    amax = np.abs(xs).max(axis=1)
+    qopts["x_clip"] = float(np.quantile(amax, 0.5))  # half of the tokens are clipped
+    check_moe(w8, inp, qopts=qopts)

@@ -42,10 +42,15 @@ class MoeShape(ctypes.Structure):
                 ("top_k", ctypes.c_int64), ("I", ctypes.c_int64)]
 
 
+SCALE_DYNAMIC, SCALE_CLIPPED, SCALE_STATIC = 0, 1, 2
+
+
 class MoeWeights(ctypes.Structure):
     _fields_ = [("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
                 ("w_gate_up", ctypes.c_void_p), ("s_gate_up", ctypes.c_void_p),
-                ("w_down", ctypes.c_void_p), ("s_down", ctypes.c_void_p), ("code", ctypes.c_int32)]
+                ("w_down", ctypes.c_void_p), ("s_down", ctypes.c_void_p), ("code", ctypes.c_int32),
+                ("x_smooth", ctypes.c_void_p), ("x_scale_mode", ctypes.c_int32),
+                ("x_clip", ctypes.c_float)]
 
 
 LAYOUT_FIELDS = ["total_bytes", "x_q", "x_scale", "logits", "topk_ids", "topk_w", "expert_counts",
@@ -65,6 +70,8 @@ SIGNATURES = {
     "w8a8_abi_version": (ctypes.c_int, []),
     "w8a8_quantize_rows": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "w8a8_quantize_rows_fp8": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "w8a8_quantize_rows_ex": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, ctypes.c_int32, ctypes.c_float,
+                                             ctypes.c_int32, _P, _P, _P]),
     "w8a8_gemm_fp8": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]),
     "w8a8_pack_weights_size": (ctypes.c_int, [_I64, _I64, _I64, ctypes.c_int,
                                               ctypes.POINTER(ctypes.c_size_t)]),

@@ -13,7 +13,7 @@ from . import _lib
 from ._lib import check, lib
 
 __all__ = [
-    "quantize_rows", "pack_weights", "gemm", "gemm_i32", "MoEWeights", "moe_workspace_layout",
+    "quantize_rows", "smoothing_inverse", "pack_weights", "gemm", "gemm_i32", "MoEWeights", "moe_workspace_layout",
     "moe_forward", "workspace_views",
 ]
 
@@ -36,10 +36,13 @@ def _dev(t: torch.Tensor, dtype, name):
 
 
 def quantize_rows(x: torch.Tensor, q: Optional[torch.Tensor] = None,
-                  scale: Optional[torch.Tensor] = None, code: int = _lib.CODE_INT8):
+                  scale: Optional[torch.Tensor] = None, code: int = _lib.CODE_INT8,
+                  col_mul: Optional[torch.Tensor] = None, scale_mode: int = _lib.SCALE_DYNAMIC,
+                  clip: float = 0.0):
     """Per-row quantisation of a [rows, cols] fp32 matrix (any leading
-    dimension via stride(0)) to int8 codes or (code=CODE_FP8) uint8 E4M3 codes.
-    Returns (q [rows, cols], scale fp32 [rows])."""
+    dimension via stride(0)) to int8 codes or (code=CODE_FP8) uint8 E4M3 codes,
+    optionally with a per-column factor col_mul [cols] and a clipped or static
+    scale (w8a8_quantize_rows_ex).  Returns (q [rows, cols], scale fp32 [rows])."""
     if not x.is_cuda or x.dtype != torch.float32 or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a 2-D fp32 GPU tensor with unit column stride")
     rows, cols = x.shape
@@ -48,9 +51,26 @@ def quantize_rows(x: torch.Tensor, q: Optional[torch.Tensor] = None,
         q = torch.empty((rows, cols), dtype=torch.uint8 if fp8 else torch.int8, device=x.device)
     if scale is None:
         scale = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    if col_mul is not None or scale_mode != _lib.SCALE_DYNAMIC:
+        if col_mul is not None:
+            _dev(col_mul, torch.float32, "col_mul")
+            if col_mul.shape != (cols,):
+                raise ValueError("col_mul must have one entry per column")
+        check(lib.w8a8_quantize_rows_ex(_ptr(x), rows, cols, x.stride(0), _ptr(col_mul), scale_mode,
+                                        float(clip), code, _ptr(q), _ptr(scale), _stream()))
+        return q, scale
     fn = lib.w8a8_quantize_rows_fp8 if fp8 else lib.w8a8_quantize_rows
     check(fn(_ptr(x), rows, cols, x.stride(0), _ptr(q), _ptr(scale), _stream()))
     return q, scale
+
+
+def smoothing_inverse(smooth: torch.Tensor) -> torch.Tensor:
+    """1 / smooth, each an IEEE fp32 division done on the host (the factor the
+    weights' input channels take; a per-layer calibration vector), returned
+    on smooth's device."""
+    import numpy as np
+    m = smooth.detach().float().cpu().numpy()
+    return torch.from_numpy(np.float32(1.0) / m).to(smooth.device)
 
 
 def pack_weights(w: torch.Tensor, kind: int = _lib.PACK_PLAIN) -> torch.Tensor:
@@ -105,31 +125,43 @@ class MoEWeights:
     w_down: torch.Tensor              # packed int8 (PLAIN) of [E, H, I]
     s_down: torch.Tensor              # [E, H] fp32
     code: int = _lib.CODE_INT8        # CODE_INT8 or CODE_FP8 (E4M3 codes)
+    x_smooth: Optional[torch.Tensor] = None  # [H] fp32 SmoothQuant factor on x, or None
+    x_scale_mode: int = _lib.SCALE_DYNAMIC   # scale of x: dynamic, clipped or static
+    x_clip: float = 0.0                      # the bound of the clipped / static modes
 
     @classmethod
-    def from_int8(cls, router_w, router_b, w_gu, s_gu, w_d, s_d):
+    def from_int8(cls, router_w, router_b, w_gu, s_gu, w_d, s_d, x_smooth=None,
+                  x_scale_mode: int = _lib.SCALE_DYNAMIC, x_clip: float = 0.0):
         """From int8 codes [E, 2I, H] / [E, H, I] with per-output-channel scales
-        (uint8 tensors: FP8 E4M3 codes, and the layer runs with FP8 codes)."""
+        (uint8 tensors: FP8 E4M3 codes, and the layer runs with FP8 codes).
+        With x_smooth the gate-up codes must already carry 1/x_smooth on their
+        input channels."""
         E, twoI, H = w_gu.shape
         code = _lib.CODE_FP8 if w_gu.dtype == torch.uint8 else _lib.CODE_INT8
         return cls(E, H, twoI // 2, router_w.contiguous(),
                    None if router_b is None else router_b.contiguous(),
                    pack_weights(w_gu.contiguous(), _lib.PACK_GATE_UP), s_gu.contiguous(),
-                   pack_weights(w_d.contiguous(), _lib.PACK_PLAIN), s_d.contiguous(), code)
+                   pack_weights(w_d.contiguous(), _lib.PACK_PLAIN), s_d.contiguous(), code,
+                   None if x_smooth is None else x_smooth.contiguous(), x_scale_mode, float(x_clip))
 
     @classmethod
     def from_fp32(cls, router_w, router_b, w_gu_f32, w_d_f32, keep_codes=False,
-                  code: int = _lib.CODE_INT8):
+                  code: int = _lib.CODE_INT8, x_smooth=None, x_scale_mode: int = _lib.SCALE_DYNAMIC,
+                  x_clip: float = 0.0):
         """Quantise fp32 expert weights per output channel with the library's
-        row quantiser (offline step), then pack.  With keep_codes the unpacked
-        codes and scales are returned as well."""
+        row quantiser (offline step), then pack.  With x_smooth (SmoothQuant)
+        the gate-up weights are quantised with 1/x_smooth on their input
+        channels.  With keep_codes the unpacked codes and scales are returned
+        as well."""
         E, twoI, H = w_gu_f32.shape
         I = twoI // 2
-        q_gu, s_gu = quantize_rows(w_gu_f32.reshape(E * twoI, H).contiguous(), code=code)
+        inv = None if x_smooth is None else smoothing_inverse(x_smooth)
+        q_gu, s_gu = quantize_rows(w_gu_f32.reshape(E * twoI, H).contiguous(), code=code, col_mul=inv)
         q_d, s_d = quantize_rows(w_d_f32.reshape(E * H, I).contiguous(), code=code)
         q_gu = q_gu.view(E, twoI, H)
         q_d = q_d.view(E, H, I)
-        w = cls.from_int8(router_w, router_b, q_gu, s_gu.view(E, twoI), q_d, s_d.view(E, H))
+        w = cls.from_int8(router_w, router_b, q_gu, s_gu.view(E, twoI), q_d, s_d.view(E, H),
+                          x_smooth, x_scale_mode, x_clip)
         if keep_codes:
             return w, dict(w_gu=q_gu, s_gu=s_gu.view(E, twoI), w_d=q_d, s_d=s_d.view(E, H))
         return w
@@ -138,7 +170,9 @@ class MoEWeights:
         return _lib.MoeWeights(self.router_w.data_ptr(),
                                None if self.router_b is None else self.router_b.data_ptr(),
                                self.w_gate_up.data_ptr(), self.s_gate_up.data_ptr(),
-                               self.w_down.data_ptr(), self.s_down.data_ptr(), self.code)
+                               self.w_down.data_ptr(), self.s_down.data_ptr(), self.code,
+                               None if self.x_smooth is None else self.x_smooth.data_ptr(),
+                               self.x_scale_mode, self.x_clip)
 
 
 def _shape(T, H, E, k, I):

@@ -125,10 +125,22 @@ const char* w8a8_status_string(int status) {
 
 const char* w8a8_last_error(void) { return g_last_error.c_str(); }
 
-int w8a8_abi_version(void) { return 2; }
+int w8a8_abi_version(void) { return 3; }
+
+// The activation-scale options: mode and bound (clip > 0 and finite for the
+// clipped and static modes; ignored for the dynamic one).
+static w8a8_status check_scale_opts(int mode, float clip, const float* col_mul) {
+    if (mode != W8A8_SCALE_DYNAMIC && mode != W8A8_SCALE_CLIPPED && mode != W8A8_SCALE_STATIC)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "unknown scale mode %d", mode);
+    if (mode != W8A8_SCALE_DYNAMIC && !(clip > 0.0f && clip <= 3.4e38f))
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "clip must be positive and finite for scale mode %d", mode);
+    if (col_mul && !aligned(col_mul, 4)) return fail(W8A8_ERR_MISALIGNED, "col_mul not 4-byte aligned");
+    return W8A8_OK;
+}
 
 static w8a8_status quantize_rows_code(const float* x, int64_t rows, int64_t cols, int64_t ld, int8_t* q,
-                                      float* scale, int code, w8a8_stream stream) {
+                                      float* scale, int code, w8a8_stream stream,
+                                      const w8a8::QuantOpts& opt = w8a8::QuantOpts{}) {
     if (rows < 0 || cols < 0 || ld < 0) return fail(W8A8_ERR_INVALID_ARGUMENT, "negative size");
     if (cols < 1 || cols > (int64_t(1) << 24))
         return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "cols=%lld: need 1 <= cols <= 2^24", (long long)cols);
@@ -137,7 +149,7 @@ static w8a8_status quantize_rows_code(const float* x, int64_t rows, int64_t cols
     if (rows == 0) return W8A8_OK;
     if (!x || !q || !scale) return fail(W8A8_ERR_INVALID_ARGUMENT, "NULL pointer");
     if (!aligned(x, 4) || !aligned(scale, 4)) return fail(W8A8_ERR_MISALIGNED, "x/scale not 4-byte aligned");
-    return check_hip(w8a8::launch_quantize_rows(x, rows, cols, ld, q, scale, code, (hipStream_t)stream),
+    return check_hip(w8a8::launch_quantize_rows(x, rows, cols, ld, q, scale, code, (hipStream_t)stream, opt),
                      "quantize_rows launch");
 }
 
@@ -149,6 +161,21 @@ w8a8_status w8a8_quantize_rows(const float* x, int64_t rows, int64_t cols, int64
 w8a8_status w8a8_quantize_rows_fp8(const float* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* q,
                                    float* scale, w8a8_stream stream) {
     return quantize_rows_code(x, rows, cols, ld, (int8_t*)q, scale, w8a8::CODE_FP8, stream);
+}
+
+w8a8_status w8a8_quantize_rows_ex(const float* x, int64_t rows, int64_t cols, int64_t ld,
+                                  const float* col_mul, int32_t scale_mode, float clip, int32_t code,
+                                  void* q, float* scale, w8a8_stream stream) {
+    w8a8_status st = check_scale_opts(scale_mode, clip, col_mul);
+    if (st != W8A8_OK) return st;
+    if (code != W8A8_CODE_INT8 && code != W8A8_CODE_FP8_E4M3)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "unknown code %d", (int)code);
+    w8a8::QuantOpts opt;
+    opt.col_mul = col_mul;
+    opt.mode = scale_mode;
+    opt.clip = clip;
+    return quantize_rows_code(x, rows, cols, ld, (int8_t*)q, scale,
+                              code == W8A8_CODE_FP8_E4M3 ? w8a8::CODE_FP8 : w8a8::CODE_INT8, stream, opt);
 }
 
 w8a8_status w8a8_pack_weights_size(int64_t groups, int64_t n, int64_t k, int kind, size_t* bytes) {
@@ -262,6 +289,13 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     if (wts->code != W8A8_CODE_INT8 && wts->code != W8A8_CODE_FP8_E4M3)
         return fail(W8A8_ERR_INVALID_ARGUMENT, "unknown weight code %d", (int)wts->code);
     const int code = wts->code == W8A8_CODE_FP8_E4M3 ? w8a8::CODE_FP8 : w8a8::CODE_INT8;
+    if ((st = check_scale_opts(wts->x_scale_mode, wts->x_clip, wts->x_smooth)) != W8A8_OK) return st;
+    if (wts->x_smooth && !aligned(wts->x_smooth, 16))
+        return fail(W8A8_ERR_MISALIGNED, "x_smooth must be 16-byte aligned");
+    w8a8::QuantOpts x_opt;
+    x_opt.col_mul = wts->x_smooth;
+    x_opt.mode = wts->x_scale_mode;
+    x_opt.clip = wts->x_clip;
     if (x == y) return fail(W8A8_ERR_INVALID_ARGUMENT, "y must not alias x");
     const MoePlan plan = plan_moe(shape);
     if (workspace_bytes < plan.lay.total_bytes)
@@ -296,7 +330,7 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
 
     // 1. per-token quantisation
     if ((st = mark(0)) != W8A8_OK) return st;
-    st = check_hip(w8a8::launch_quantize_rows(x, T, H, H, x_q, x_scale, code, s), "quantize x");
+    st = check_hip(w8a8::launch_quantize_rows(x, T, H, H, x_q, x_scale, code, s, x_opt), "quantize x");
     if (st != W8A8_OK) return st;
 
     // 2-4. router, top-k, permutation

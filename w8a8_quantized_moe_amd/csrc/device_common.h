@@ -119,6 +119,10 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
            ((uint32_t)(d & 0xff) << 24);
 }
 
+__device__ __forceinline__ float4 mul4(float4 v, float4 m) {
+    return make_float4(v.x * m.x, v.y * m.y, v.z * m.z, v.w * m.w);
+}
+
 __device__ __forceinline__ float amax4(float4 v) {
     return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 }
@@ -134,15 +138,29 @@ __device__ __forceinline__ float code_range() {
     return CODE == CODE_FP8 ? 448.0f : 127.0f;
 }
 
+// The E4M3 conversion's input: the IEEE quotient v / s, saturated at +-448
+// (a capped or static scale lets |v / s| exceed the range; below it the
+// clamp changes nothing, since values up to 464 round to 448 anyway).
+__device__ __forceinline__ float fp8_quotient(float v, float s) {
+    if (s == 0.0f) return 0.0f;
+    return fminf(fmaxf(v / s, -448.0f), 448.0f);
+}
+
+// The scale's base for a row whose (smoothed) maximum is amax.
+__device__ __forceinline__ float scale_base(float amax, const QuantOpts& opt) {
+    if (opt.mode == SCALE_STATIC) return opt.clip;
+    if (opt.mode == SCALE_CLIPPED && opt.clip < amax) return opt.clip;
+    return amax;
+}
+
 // Four codes of one row packed into a 32-bit word (element 0 in the low byte).
 template <int CODE>
 __device__ __forceinline__ uint32_t encode4(const float4& v, float s, float rs) {
     if (CODE == CODE_INT8)
         return pack4(quant_fast(v.x, s, rs), quant_fast(v.y, s, rs), quant_fast(v.z, s, rs),
                      quant_fast(v.w, s, rs));
-    const bool z = (s == 0.0f);
-    const float a = z ? 0.0f : v.x / s, b = z ? 0.0f : v.y / s;
-    const float c = z ? 0.0f : v.z / s, d = z ? 0.0f : v.w / s;
+    const float a = fp8_quotient(v.x, s), b = fp8_quotient(v.y, s);
+    const float c = fp8_quotient(v.z, s), d = fp8_quotient(v.w, s);
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (uint32_t)w;
@@ -151,8 +169,7 @@ __device__ __forceinline__ uint32_t encode4(const float4& v, float s, float rs) 
 template <int CODE>
 __device__ __forceinline__ uint8_t encode1(float v, float s) {
     if (CODE == CODE_INT8) return (uint8_t)(int8_t)quant_one(v, s);
-    const float a = (s == 0.0f) ? 0.0f : v / s;
-    return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(a, 0.0f, 0, false) & 0xff);
+    return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(fp8_quotient(v, s), 0.0f, 0, false) & 0xff);
 }
 
 }  // namespace w8a8

@@ -74,7 +74,9 @@ enum Code : int {
 // 16 bytes of a lane are two 8-byte k groups; one v_mfma_f32_16x16x32_fp8_fp8
 // per group (lane l then holds k-bytes (l/16)*8 .. +7 of its group, the same
 // grouping in both operands), so the two products together cover all 64 k,
-// accumulated in fp32.
+// accumulated in fp32.  (That FP8 MFMA issues at a quarter of the rate of
+// the 16x16x128 one below: the register-fed skinny kernel, which streams
+// weights at HBM speed, uses it; the LDS-tiled GEMM uses mma128_fp8.)
 typedef long v2l __attribute__((ext_vector_type(2)));
 template <int CODE>
 struct AccOf {
@@ -144,9 +146,21 @@ constexpr int TILE_CTR_COUNT = 16;  // gate-up queues 0..7, down queues 8..15
 // Compute units of the current device (queried once per device).
 int device_cu_count();
 
+// Activation-scale options of the per-row quantiser ("W8A8 quantisation of
+// MiniMax-M3 on K100AI", sec. 2.2; "DeepSeek V4 '950'", sec. 3.1): a
+// per-column factor applied before the scale is taken (SmoothQuant), and the
+// scale's base: the row maximum (dynamic), the row maximum capped by a
+// calibrated bound (clipped), or the bound alone (static).
+enum ScaleMode : int { SCALE_DYNAMIC = 0, SCALE_CLIPPED = 1, SCALE_STATIC = 2 };
+struct QuantOpts {
+    const float* col_mul = nullptr;  // [cols] or nullptr
+    int mode = SCALE_DYNAMIC;
+    float clip = 0.0f;               // > 0 for the clipped and static modes
+};
+
 // ---- launchers (each returns the launch status) ----
 hipError_t launch_quantize_rows(const float* x, int64_t rows, int64_t cols, int64_t ld, int8_t* q,
-                                float* scale, int code, hipStream_t s);
+                                float* scale, int code, hipStream_t s, const QuantOpts& opt = QuantOpts{});
 
 hipError_t launch_pack_weights(const int8_t* w, int64_t groups, int64_t n, int64_t k, int kind,
                                int8_t* packed, hipStream_t s);

@@ -22,7 +22,7 @@ namespace {
 template <int CODE, int VPL>
 __global__ __launch_bounds__(256) void quant_rows_cached(const float* __restrict__ x, int64_t rows,
                                                          int cols, int64_t ld, int8_t* __restrict__ q,
-                                                         float* __restrict__ scale) {
+                                                         float* __restrict__ scale, QuantOpts opt) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
@@ -35,13 +35,14 @@ __global__ __launch_bounds__(256) void quant_rows_cached(const float* __restrict
         const int c = i * 64 + lane;
         if (c < nv) {
             v[i] = xr[c];
+            if (opt.col_mul) v[i] = mul4(v[i], reinterpret_cast<const float4*>(opt.col_mul)[c]);
             amax = fmaxf(amax, amax4(v[i]));
         } else {
             v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
     }
     amax = wave_max(amax);
-    const float s = amax / code_range<CODE>();
+    const float s = scale_base(amax, opt) / code_range<CODE>();
     const float rs = 1.0f / s;
     if (lane == 0) scale[row] = s;
     uint32_t* qr = reinterpret_cast<uint32_t*>(q + row * (int64_t)cols);
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(256) void quant_rows_cached(const float* __restrict
 template <int CODE, int VPT>
 __global__ __launch_bounds__(256) void quant_rows_block(const float* __restrict__ x, int64_t rows,
                                                         int cols, int64_t ld, int8_t* __restrict__ q,
-                                                        float* __restrict__ scale) {
+                                                        float* __restrict__ scale, QuantOpts opt) {
     __shared__ float wmax[4];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t row = blockIdx.x;
@@ -72,6 +73,7 @@ __global__ __launch_bounds__(256) void quant_rows_block(const float* __restrict_
         const int c = i * 256 + tid;
         if (c < nv) {
             v[i] = xr[c];
+            if (opt.col_mul) v[i] = mul4(v[i], reinterpret_cast<const float4*>(opt.col_mul)[c]);
             amax = fmaxf(amax, amax4(v[i]));
         } else {
             v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(256) void quant_rows_block(const float* __restrict_
     if (lane == 0) wmax[wv] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-    const float s = amax / code_range<CODE>();
+    const float s = scale_base(amax, opt) / code_range<CODE>();
     const float rs = 1.0f / s;
     if (tid == 0) scale[row] = s;
     uint32_t* qr = reinterpret_cast<uint32_t*>(q + row * (int64_t)cols);
@@ -99,47 +101,49 @@ template <int CODE>
 __global__ __launch_bounds__(256) void quant_rows_twopass(const float* __restrict__ x, int64_t rows,
                                                           int64_t cols, int64_t ld,
                                                           int8_t* __restrict__ q,
-                                                          float* __restrict__ scale) {
+                                                          float* __restrict__ scale, QuantOpts opt) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
     const float* xr = x + row * ld;
+    const float* m = opt.col_mul;
     float amax = 0.0f;
-    for (int64_t c = lane; c < cols; c += 64) amax = fmaxf(amax, fabsf(xr[c]));
+    for (int64_t c = lane; c < cols; c += 64) amax = fmaxf(amax, fabsf(m ? xr[c] * m[c] : xr[c]));
     amax = wave_max(amax);
-    const float s = amax / code_range<CODE>();
+    const float s = scale_base(amax, opt) / code_range<CODE>();
     if (lane == 0) scale[row] = s;
     int8_t* qr = q + row * cols;
-    for (int64_t c = lane; c < cols; c += 64) qr[c] = (int8_t)encode1<CODE>(xr[c], s);
+    for (int64_t c = lane; c < cols; c += 64) qr[c] = (int8_t)encode1<CODE>(m ? xr[c] * m[c] : xr[c], s);
 }
 
 template <int CODE>
 hipError_t launch_quant(const float* x, int64_t rows, int64_t cols, int64_t ld, int8_t* q,
-                        float* scale, hipStream_t s) {
+                        float* scale, const QuantOpts& opt, hipStream_t s) {
     const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
     const bool vec = (cols % 4 == 0) && (ld % 4 == 0) && ((uintptr_t)x % 16 == 0) &&
-                     ((uintptr_t)q % 4 == 0) && cols <= 8 * 1024;
+                     ((uintptr_t)q % 4 == 0) && ((uintptr_t)opt.col_mul % 16 == 0) &&
+                     cols <= 8 * 1024;
     if (vec && cols > 1024) {
         const int nv = (int)(cols / 4);
         const int need = (nv + 255) / 256;
         const dim3 g1((unsigned)rows);
         if (need <= 2)
-            quant_rows_block<CODE, 2><<<g1, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
+            quant_rows_block<CODE, 2><<<g1, block, 0, s>>>(x, rows, (int)cols, ld, q, scale, opt);
         else if (need <= 4)
-            quant_rows_block<CODE, 4><<<g1, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
+            quant_rows_block<CODE, 4><<<g1, block, 0, s>>>(x, rows, (int)cols, ld, q, scale, opt);
         else
-            quant_rows_block<CODE, 8><<<g1, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
+            quant_rows_block<CODE, 8><<<g1, block, 0, s>>>(x, rows, (int)cols, ld, q, scale, opt);
     } else if (vec) {
         const int nv = (int)(cols / 4);
         const int need = (nv + 63) / 64;
         if (need <= 1)
-            quant_rows_cached<CODE, 1><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
+            quant_rows_cached<CODE, 1><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale, opt);
         else if (need <= 2)
-            quant_rows_cached<CODE, 2><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
+            quant_rows_cached<CODE, 2><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale, opt);
         else
-            quant_rows_cached<CODE, 4><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale);
+            quant_rows_cached<CODE, 4><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale, opt);
     } else {
-        quant_rows_twopass<CODE><<<grid, block, 0, s>>>(x, rows, cols, ld, q, scale);
+        quant_rows_twopass<CODE><<<grid, block, 0, s>>>(x, rows, cols, ld, q, scale, opt);
     }
     return hipGetLastError();
 }
@@ -147,10 +151,10 @@ hipError_t launch_quant(const float* x, int64_t rows, int64_t cols, int64_t ld, 
 }  // namespace
 
 hipError_t launch_quantize_rows(const float* x, int64_t rows, int64_t cols, int64_t ld, int8_t* q,
-                                float* scale, int code, hipStream_t s) {
+                                float* scale, int code, hipStream_t s, const QuantOpts& opt) {
     if (rows == 0) return hipSuccess;
-    if (code == CODE_FP8) return launch_quant<CODE_FP8>(x, rows, cols, ld, q, scale, s);
-    if (code == CODE_INT8) return launch_quant<CODE_INT8>(x, rows, cols, ld, q, scale, s);
+    if (code == CODE_FP8) return launch_quant<CODE_FP8>(x, rows, cols, ld, q, scale, opt, s);
+    if (code == CODE_INT8) return launch_quant<CODE_INT8>(x, rows, cols, ld, q, scale, opt, s);
     return hipErrorInvalidValue;
 }
 
