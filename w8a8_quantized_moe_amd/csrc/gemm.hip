@@ -114,11 +114,23 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
         row0 = mt * BM;
         row_end = min(row0 + BM, p.M);
     }
+    // A segment's last tile with at most FM*16 valid rows (a "half tile" for
+    // WM = 2) runs its own schedule (run_half below): only the first FM*16
+    // rows are copied, so a stage is smaller and the ring deeper, and all
+    // waves share those rows and split the columns, FN/WM fragment columns
+    // each.  (INT8 only; for the gate-up epilogue only where each wave keeps
+    // whole gate/up column pairs.)
+    constexpr bool HALF_OK = CODE == CODE_INT8 && FN % WM == 0 &&
+                             (EPI != EPI_GATE_UP || (FN / WM) % 2 == 0);
+    const int rows_valid = (int)(row_end - row0);
+    const bool half = HALF_OK && rows_valid <= FM * 16;
+    // first fragment row / column of this wave
+    const int a_base = half ? 0 : wm * FM;
+    const int b_base = half ? wn * FN + wm * (FN / WM) : wn * FN;
     // fragment rows of this wave holding at least one valid row (the rest of a
     // segment's last, partial tile is neither read nor multiplied)
-    const int rows_valid = (int)(row_end - row0);
-    const int fm_active =
-        __builtin_amdgcn_readfirstlane(min(FM, max(0, (rows_valid - wm * FM * 16 + 15) / 16)));
+    const int fm_active = __builtin_amdgcn_readfirstlane(
+        half ? min(FM, (rows_valid + 15) / 16) : min(FM, max(0, (rows_valid - wm * FM * 16 + 15) / 16)));
 
     // ---- per-row metadata for the epilogue ----
     if (tid < BM) {
@@ -172,10 +184,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     // MFMA A operand: lane l holds row l%16, 16-byte k-chunk l/16 of the block
     const int a_slot = 4 * (lane & 15) + ((lane >> 4) ^ ((lane >> 2) & 3));
     auto frag_a = [&](int ks, int i) {
-        return *reinterpret_cast<const LDS_AS v4i*>(lds + (ks % NS) * STAGE + (wm * FM + i) * 1024 + a_slot * 16);
+        return *reinterpret_cast<const LDS_AS v4i*>(lds + (ks % NS) * STAGE + (a_base + i) * 1024 + a_slot * 16);
     };
     auto frag_b = [&](int ks, int j) {
-        return *reinterpret_cast<const LDS_AS v4i*>(lds + (ks % NS) * STAGE + (NBA + wn * FN + j) * 1024 +
+        return *reinterpret_cast<const LDS_AS v4i*>(lds + (ks % NS) * STAGE + (NBA + b_base + j) * 1024 +
                                              lane * 16);
     };
 
@@ -208,7 +220,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
             fb8[j].lo = frag_b(0, j);
             fb8[j].hi = frag_b(1, j);
         }
-    } else {
+    } else if (!half) {  // (a half tile fills its own ring: run_half)
         // prologue: NS-1 stages in flight, stage 0's fragments in registers
 #pragma unroll
         for (int s = 0; s < NS - 1; ++s)
@@ -224,26 +236,29 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     }
 
     // ---- epilogue.  Lane l, register r of accumulator block (i, j) holds
-    //      row (wm*FM+i)*16 + (l/16)*4 + r, column (wn*FN+j)*16 + l%16.  The
+    //      row (a_base+i)*16 + (l/16)*4 + r, column (b_base+j)*16 + l%16 (j < NF,
+    //      the wave's fragment columns).  The
     //      values are finished in registers, staged through the (now idle) LDS
     //      ring 32 rows at a time, and leave as 16-byte stores that cover whole
     //      256-byte (128-byte for h) row segments.  It runs inside each compute
     //      variant below, so the accumulators never have to be merged across
     //      the variants' register assignments. ----
-    constexpr int OCOLS = (EPI == EPI_GATE_UP) ? FN * 8 : FN * 16;  // output columns per wave
-    constexpr int SROW = OCOLS + 4;                                 // padded staging stride (words)
-    static_assert(NW * 32 * SROW * 4 <= NS * STAGE, "epilogue staging fits in the LDS ring");
-    auto epilogue = [&](AccT (&acc)[FM][FN]) {
+    static_assert(NW * 32 * (((EPI == EPI_GATE_UP) ? FN * 8 : FN * 16) + 4) * 4 <= NS * STAGE,
+                  "epilogue staging fits in the LDS ring");
+    auto epilogue = [&](AccT (&acc)[FM][FN], auto n_tag) {
+        constexpr int NF = decltype(n_tag)::value;
+        constexpr int OCOLS = (EPI == EPI_GATE_UP) ? NF * 8 : NF * 16;  // output columns per wave
+        constexpr int SROW = OCOLS + 4;                                 // padded staging stride (words)
         __syncthreads();  // the ring is idle; row metadata written before the loop is visible
         uint32_t* stg = reinterpret_cast<uint32_t*>(smem) + wave * (32 * SROW);
         const int col_in_blk = lane & 15;
         const int I = p.I, N = p.N;
         // first output column of this wave
-        const int64_t col0 = (EPI == EPI_GATE_UP) ? (int64_t)(nt * NBB + wn * FN) / 2 * 16
-                                                  : (int64_t)nt * BN + wn * FN * 16;
-        float s_col[FN];
+        const int64_t col0 = (EPI == EPI_GATE_UP) ? (int64_t)(nt * NBB + b_base) / 2 * 16
+                                                  : (int64_t)nt * BN + b_base * 16;
+        float s_col[NF];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
+        for (int j = 0; j < NF; ++j) {
             if (EPI == EPI_GATE_UP) {
                 const int jp = j >> 1;
                 const int ch = (int)col0 + jp * 16 + col_in_blk;
@@ -264,19 +279,19 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int lr = di * 16 + (lane >> 4) * 4 + r;            // staged row
-                    const int row = (wm * FM + i) * 16 + (lane >> 4) * 4 + r;  // tile row
+                    const int row = (a_base + i) * 16 + (lane >> 4) * 4 + r;  // tile row
                     if (EPI == EPI_GATE_UP) {
                         // column blocks alternate gate / up for the same 16 channels
                         const float sx = row_scale[row];
 #pragma unroll
-                        for (int jp = 0; jp < FN / 2; ++jp) {
+                        for (int jp = 0; jp < NF / 2; ++jp) {
                             const float gv = ((float)acc[i][2 * jp][r] * sx) * s_col[2 * jp];
                             const float uv = ((float)acc[i][2 * jp + 1][r] * sx) * s_col[2 * jp + 1];
                             stg[lr * SROW + jp * 16 + col_in_blk] = __float_as_uint(silu_f32(gv) * uv);
                         }
                     } else {
 #pragma unroll
-                        for (int j = 0; j < FN; ++j) {
+                        for (int j = 0; j < NF; ++j) {
                             uint32_t v;
                             if (EPI == EPI_DENSE_I32) {
                                 v = (uint32_t)(int)acc[i][j][r];
@@ -299,7 +314,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
             for (int q = 0; q < 32 / RPI; ++q) {
                 const int lr = q * RPI + lane / LPR;
                 const int c4 = (lane % LPR) * 4;
-                const int row = (wm * FM + i0) * 16 + lr;
+                const int row = (a_base + i0) * 16 + lr;
                 const int64_t grow = row0 + row;
                 if (grow < row_end) {
                     const v4i v = *reinterpret_cast<const v4i*>(stg + lr * SROW + c4);
@@ -363,7 +378,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
             }
         }
         mfma_and_refill(f_tag, acc, 0, false);
-        epilogue(acc);
+        epilogue(acc, std::integral_constant<int, FN>{});
     };
     if constexpr (PAIRS) {
         // FP8: pair q's MFMAs run from registers while pair q+1's fragments
@@ -405,15 +420,119 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
                     }
                 }
             }
-            epilogue(acc);
+            epilogue(acc, std::integral_constant<int, FN>{});
         };
         if (fm_active > FM / 2) run_pairs(std::integral_constant<int, FM>{});
         else if (fm_active > 0) run_pairs(std::integral_constant<int, FM / 2>{});
         else run_pairs(std::integral_constant<int, 0>{});
     } else {
-        if (fm_active > FM / 2) run(std::integral_constant<int, FM>{});
-        else if (fm_active > 0) run(std::integral_constant<int, FM / 2>{});
-        else run(std::integral_constant<int, 0>{});
+        // A half tile: only its first FM*16 rows are copied, so a stage holds
+        // FM A blocks instead of BM/16 and the same LDS ring takes more stages
+        // (5 instead of 4 for 256x256 tiles: four in flight instead of three).
+        // A segment's last tile streams the whole weight tile for few rows,
+        // which makes it bound by the copy pipeline's latency; the deeper
+        // ring and all eight waves at work (each on FN/WM fragment columns of
+        // those rows) shorten it.
+        auto run_half = [&](auto f_tag) {
+            constexpr int F = decltype(f_tag)::value;
+            constexpr int NF = FN / WM;
+            constexpr int NBLK_H = FM + NBB;
+            static_assert(NBLK_H % NW == 0, "half-tile blocks must split evenly over the waves");
+            constexpr int DPW_H = NBLK_H / NW;
+            constexpr int STAGE_H = NBLK_H * 1024;
+            constexpr int NS_H = (NS * STAGE) / STAGE_H < 8 ? (NS * STAGE) / STAGE_H : 8;
+            static_assert(NS_H >= NS && NS_H * STAGE_H <= NS * STAGE, "the half-tile ring fits the ring");
+            const int8_t* hsrc[DPW_H];
+            int hstride[DPW_H];
+#pragma unroll
+            for (int i = 0; i < DPW_H; ++i) {
+                const int b = wave + NW * i;
+                if (b < FM) {  // activation rows b*16 .. b*16+15, swizzled as in the full tile
+                    int64_t r = row0 + b * 16 + (lane >> 2);
+                    if (r >= row_end) r = row0;
+                    int64_t src_row = r;
+                    if (EPI == EPI_GATE_UP)
+                        src_row = min(max((int64_t)(p.sorted_assign[r] / p.topk), (int64_t)0), p.a_rows - 1);
+                    hsrc[i] = p.A + src_row * K + (((lane & 3) ^ ((lane >> 4) & 3)) * 16);
+                    hstride[i] = 64;
+                } else {
+                    const int nb = nt * NBB + (b - FM);
+                    hsrc[i] = p.B + (int64_t)g * p.b_group_bytes + (int64_t)nb * KB * 1024 + lane * 16;
+                    hstride[i] = 1024;
+                }
+            }
+            auto issue_h = [&](int ks) {
+                const LDS_AS int8_t* stage = lds + (ks % NS_H) * STAGE_H;
+#pragma unroll
+                for (int i = 0; i < DPW_H; ++i)
+                    dma16(hsrc[i] + (int64_t)ks * hstride[i], stage + (wave + NW * i) * 1024);
+            };
+            auto frag_a_h = [&](int ks, int i) {
+                return *reinterpret_cast<const LDS_AS v4i*>(lds + (ks % NS_H) * STAGE_H + i * 1024 + a_slot * 16);
+            };
+            auto frag_b_h = [&](int ks, int j) {
+                return *reinterpret_cast<const LDS_AS v4i*>(lds + (ks % NS_H) * STAGE_H +
+                                                            (FM + b_base + j) * 1024 + lane * 16);
+            };
+            // prologue: NS_H-1 stages in flight, stage 0's fragments in registers
+#pragma unroll
+            for (int s = 0; s < NS_H - 1; ++s)
+                if (s < nk) issue_h(s);
+            if (nk - 1 >= NS_H - 2) wait_vmcnt<(NS_H - 2) * DPW_H>();
+            else wait_vmcnt<0>();
+            barrier_nofence();
+#pragma unroll
+            for (int i = 0; i < F; ++i) fa[i] = frag_a_h(0, i);
+#pragma unroll
+            for (int j = 0; j < NF; ++j) fb[j] = frag_b_h(0, j);
+            AccT acc[FM][FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = AccT{};
+            auto mma_refill = [&](int next_ks, bool refill) {
+#pragma unroll
+                for (int i = 0; i < F; ++i) {
+#pragma unroll
+                    for (int j = 0; j < NF; ++j) acc[i][j] = mma16<CODE>(fa[i], fb[j], acc[i][j]);
+                    if (refill) fa[i] = frag_a_h(next_ks, i);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+            int ks = 0;
+            // steady state: stage ks+1 landed (NS_H-3 newer stages may still fly)
+            for (; ks + NS_H - 1 < nk; ++ks) {
+                wait_vmcnt<(NS_H - 3) * DPW_H>();
+                barrier_nofence();
+                issue_h(ks + NS_H - 1);
+                mma_refill(ks + 1, true);
+#pragma unroll
+                for (int j = 0; j < NF; ++j) fb[j] = frag_b_h(ks + 1, j);
+            }
+            // drain: nothing left to issue
+            for (; ks + 1 < nk; ++ks) {
+                wait_vmcnt<0>();
+                barrier_nofence();
+                mma_refill(ks + 1, true);
+#pragma unroll
+                for (int j = 0; j < NF; ++j) fb[j] = frag_b_h(ks + 1, j);
+            }
+            mma_refill(0, false);
+            epilogue(acc, std::integral_constant<int, NF>{});
+        };
+        bool done = false;
+        if constexpr (HALF_OK) {
+            if (half) {
+                if (fm_active > FM / 2) run_half(std::integral_constant<int, FM>{});
+                else run_half(std::integral_constant<int, FM / 2>{});
+                done = true;
+            }
+        }
+        if (!done) {
+            if (fm_active > FM / 2) run(std::integral_constant<int, FM>{});
+            else if (fm_active > 0) run(std::integral_constant<int, FM / 2>{});
+            else run(std::integral_constant<int, 0>{});
+        }
     }
     };
 
