@@ -192,34 +192,50 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     };
 
     const int nk = K / 64;
-    // FP8 codes run on the 16x16x128 FP8 MFMA (the 16x16x32 one issues at a
-    // quarter of its rate): one instruction takes lane l's 16-byte chunk of two
-    // consecutive stages, so the FP8 variant consumes the ring in stage pairs.
-    constexpr bool PAIRS = (CODE == CODE_FP8);
-    static_assert(!PAIRS || NS == 4, "the FP8 stage pairs need a ring of exactly two pairs");
-    v4i fa[PAIRS ? 1 : FM], fb[PAIRS ? 1 : FN];
-    // FP8: a pair's fragments, the first stage in the low and the second in
-    // the high 16 bytes of the 32-byte MFMA operand
-    v8i fa8[PAIRS ? FM : 1], fb8[PAIRS ? FN : 1];
-    if constexpr (PAIRS) {
-        // prologue: both pairs of the ring in flight, pair 0's fragments in registers
+    // FP8 codes run on the 32x32x64 FP8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4
+    // with unit block scales): one 64-k stage feeds it directly, lane l
+    // supplying row (column) l%32 and the stage's k bytes (l/32)*32 .. +31, read
+    // as two 16-byte chunks from the same LDS blocks the INT8 fragments use.
+    // A wave's 128x64 outputs are 4x2 blocks of 32x32.  (The 16x16x32 FP8 MFMA
+    // issues at a quarter of the rate.)
+    constexpr bool M32 = (CODE == CODE_FP8);
+    constexpr int FM32 = FM / 2, FN32 = FN / 2;  // 32x32 blocks per wave
+    static_assert(!M32 || (FM % 2 == 0 && FN % 2 == 0), "whole 32x32 blocks per wave");
+    v4i fa[M32 ? 1 : FM], fb[M32 ? 1 : FN];
+    v8i fa32[M32 ? FM32 : 1], fb32[M32 ? FN32 : 1];
+    // rows (a_base + 2i + (l/16)%2)*16 + l%16, k chunks 2h and 2h+1 (h = l/32)
+    auto frag_a32 = [&](int ks, int i) {
+        const int blk = a_base + 2 * i + ((lane >> 4) & 1);
+        const int rr = lane & 15, h = lane >> 5;
+        const LDS_AS int8_t* base = lds + (ks % NS) * STAGE + blk * 1024;
+        v8i t;
+        t.lo = *reinterpret_cast<const LDS_AS v4i*>(base + (4 * rr + ((2 * h) ^ (rr >> 2))) * 16);
+        t.hi = *reinterpret_cast<const LDS_AS v4i*>(base + (4 * rr + ((2 * h + 1) ^ (rr >> 2))) * 16);
+        return t;
+    };
+    // columns (b_base + 2j + (l/16)%2)*16 + l%16 (packed lane slot c + 16*chunk)
+    auto frag_b32 = [&](int ks, int j) {
+        const int blk = NBA + b_base + 2 * j + ((lane >> 4) & 1);
+        const int cc = lane & 15, h = lane >> 5;
+        const LDS_AS int8_t* base = lds + (ks % NS) * STAGE + blk * 1024;
+        v8i t;
+        t.lo = *reinterpret_cast<const LDS_AS v4i*>(base + (cc + 32 * h) * 16);
+        t.hi = *reinterpret_cast<const LDS_AS v4i*>(base + (cc + 32 * h + 16) * 16);
+        return t;
+    };
+    if constexpr (M32) {
+        // prologue: NS-1 stages in flight, stage 0's fragments in registers
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
+        for (int s = 0; s < NS - 1; ++s)
             if (s < nk) issue(s);
-        if (nk >= 4) wait_vmcnt<2 * DPW>();
+        if (nk - 1 >= NS - 2) wait_vmcnt<(NS - 2) * DPW>();
         else wait_vmcnt<0>();
         barrier_nofence();
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-            if (i < fm_active) {
-                fa8[i].lo = frag_a(0, i);
-                fa8[i].hi = frag_a(1, i);
-            }
+        for (int i = 0; i < FM32; ++i)
+            if (2 * i < fm_active) fa32[i] = frag_a32(0, i);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            fb8[j].lo = frag_b(0, j);
-            fb8[j].hi = frag_b(1, j);
-        }
+        for (int j = 0; j < FN32; ++j) fb32[j] = frag_b32(0, j);
     } else if (!half) {  // (a half tile fills its own ring: run_half)
         // prologue: NS-1 stages in flight, stage 0's fragments in registers
 #pragma unroll
@@ -245,6 +261,34 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     //      the variants' register assignments. ----
     static_assert(NW * 32 * (((EPI == EPI_GATE_UP) ? FN * 8 : FN * 16) + 4) * 4 <= NS * STAGE,
                   "epilogue staging fits in the LDS ring");
+    // one staged pass of 32 rows (from tile row rbase) leaves as 16-byte stores
+    auto write_pass = [&](auto n_tag, const uint32_t* stg, int rbase, int64_t col0) {
+        constexpr int NF = decltype(n_tag)::value;
+        constexpr int OCOLS = (EPI == EPI_GATE_UP) ? NF * 8 : NF * 16;
+        constexpr int SROW = OCOLS + 4;
+        const int I = p.I, N = p.N;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's staging complete
+        // each lane moves 16 bytes; a wave covers 64*4/OCOLS rows per instruction
+        constexpr int LPR = OCOLS / 4;   // lanes per row
+        constexpr int RPI = 64 / LPR;    // rows per instruction
+#pragma unroll
+        for (int q = 0; q < 32 / RPI; ++q) {
+            const int lr = q * RPI + lane / LPR;
+            const int c4 = (lane % LPR) * 4;
+            const int row = rbase + lr;
+            const int64_t grow = row0 + row;
+            if (grow < row_end) {
+                const v4i v = *reinterpret_cast<const v4i*>(stg + lr * SROW + c4);
+                int64_t dst;
+                if (EPI == EPI_GATE_UP) dst = grow * I + col0 + c4;
+                else if (EPI == EPI_DOWN) dst = (int64_t)row_slot[row] * N + col0 + c4;
+                else dst = grow * N + col0 + c4;
+                if (EPI == EPI_DENSE_I32) *reinterpret_cast<v4i*>(p.out_i32 + dst) = v;
+                else *reinterpret_cast<v4i*>(p.out_f32 + dst) = v;
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next pass
+    };
     auto epilogue = [&](AccT (&acc)[FM][FN], auto n_tag) {
         constexpr int NF = decltype(n_tag)::value;
         constexpr int OCOLS = (EPI == EPI_GATE_UP) ? NF * 8 : NF * 16;  // output columns per wave
@@ -306,27 +350,69 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
                     }
                 }
             }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's staging complete
-            // write out: each lane moves 16 bytes; a wave covers 64*4/OCOLS rows
-            constexpr int LPR = OCOLS / 4;   // lanes per row
-            constexpr int RPI = 64 / LPR;    // rows per instruction
+            write_pass(n_tag, stg, (a_base + i0) * 16, col0);
+        }
+    };
+
+    // ---- the FP8 epilogue: register q of 32x32 block (i, j) in lane l holds
+    //      row (a_base + 2i)*16 + (q/4)*8 + (l/32)*4 + q%4, column
+    //      (b_base + 2j)*16 + l%32; the gate and up values of one channel sit
+    //      16 lanes apart. ----
+    auto epilogue32 = [&](v4f (&acc)[M32 ? FM32 : 1][M32 ? FN32 : 1][4]) {
+        constexpr int NF = FN;
+        constexpr int OCOLS = (EPI == EPI_GATE_UP) ? NF * 8 : NF * 16;
+        constexpr int SROW = OCOLS + 4;
+        __syncthreads();  // the ring is idle; row metadata written before the loop is visible
+        uint32_t* stg = reinterpret_cast<uint32_t*>(smem) + wave * (32 * SROW);
+        const int I = p.I, N = p.N;
+        const int h = lane >> 5, c32 = lane & 31, up = (lane >> 4) & 1;
+        const int64_t col0 = (EPI == EPI_GATE_UP) ? (int64_t)(nt * NBB + b_base) / 2 * 16
+                                                  : (int64_t)nt * BN + b_base * 16;
+        float s_col[FN32];
 #pragma unroll
-            for (int q = 0; q < 32 / RPI; ++q) {
-                const int lr = q * RPI + lane / LPR;
-                const int c4 = (lane % LPR) * 4;
-                const int row = (a_base + i0) * 16 + lr;
-                const int64_t grow = row0 + row;
-                if (grow < row_end) {
-                    const v4i v = *reinterpret_cast<const v4i*>(stg + lr * SROW + c4);
-                    int64_t dst;
-                    if (EPI == EPI_GATE_UP) dst = grow * I + col0 + c4;
-                    else if (EPI == EPI_DOWN) dst = (int64_t)row_slot[row] * N + col0 + c4;
-                    else dst = grow * N + col0 + c4;
-                    if (EPI == EPI_DENSE_I32) *reinterpret_cast<v4i*>(p.out_i32 + dst) = v;
-                    else *reinterpret_cast<v4i*>(p.out_f32 + dst) = v;
+        for (int j = 0; j < FN32; ++j) {
+            if (EPI == EPI_GATE_UP)
+                s_col[j] = p.s_b[(int64_t)g * 2 * I + (up ? I : 0) + col0 + j * 16 + (lane & 15)];
+            else
+                s_col[j] = p.s_b[(int64_t)g * N + col0 + j * 32 + c32];
+        }
+#pragma unroll
+        for (int i = 0; i < FM32; ++i) {
+            if (2 * i >= fm_active) break;
+            if (EPI == EPI_GATE_UP) {
+                // registers q and q+1 are rows lr0 and lr0+1: a gate lane keeps
+                // row lr0 and hands its row-(lr0+1) gate value to its up partner
+                // (16 lanes away), which keeps row lr0+1 and hands back its row-lr0
+                // up value, so every lane finishes one h value per register pair
+#pragma unroll
+                for (int q = 0; q < 16; q += 2) {
+                    const int lr0 = (q / 4) * 8 + h * 4 + (q % 4);
+                    const int row = (a_base + 2 * i) * 16 + lr0;
+                    const float sx0 = row_scale[row], sx1 = row_scale[row + 1];
+#pragma unroll
+                    for (int j = 0; j < FN32; ++j) {
+                        const float v0 = (acc[i][j][q / 4][q % 4] * sx0) * s_col[j];
+                        const float v1 = (acc[i][j][q / 4][q % 4 + 1] * sx1) * s_col[j];
+                        const float got = __shfl_xor(up ? v0 : v1, 16, 64);
+                        const float gv = up ? got : v0, uv = up ? v1 : got;
+                        stg[(lr0 + up) * SROW + j * 16 + (lane & 15)] = __float_as_uint(silu_f32(gv) * uv);
+                    }
                 }
             }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next pass
+            if (EPI != EPI_GATE_UP) {
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int lr = (q / 4) * 8 + h * 4 + (q % 4);    // staged row
+                    const int row = (a_base + 2 * i) * 16 + lr;      // tile row
+#pragma unroll
+                    for (int j = 0; j < FN32; ++j) {
+                        const float dq = (acc[i][j][q / 4][q % 4] * row_scale[row]) * s_col[j];
+                        const float v = (EPI == EPI_DOWN) ? row_w[row] * dq : dq;
+                        stg[lr * SROW + j * 32 + c32] = __float_as_uint(v);
+                    }
+                }
+            }
+            write_pass(std::integral_constant<int, NF>{}, stg, (a_base + 2 * i) * 16, col0);
         }
     };
 
@@ -380,51 +466,54 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
         mfma_and_refill(f_tag, acc, 0, false);
         epilogue(acc, std::integral_constant<int, FN>{});
     };
-    if constexpr (PAIRS) {
-        // FP8: pair q's MFMAs run from registers while pair q+1's fragments
-        // stream in from LDS (each A fragment row right after its MFMAs, the B
-        // fragments after the last row); the copies of pair q+2 go to the two
-        // ring slots pair q left.  The reads ahead are unconditional: past the
-        // last pair they read stale ring slots whose values are never used
-        // (conditional reads would cost register copies at every join).
-        auto run_pairs = [&](auto f_tag) {
+    if constexpr (M32) {
+        // FP8: stage ks's MFMAs run from registers while stage ks+1's fragments
+        // come in (each A fragment row right after its MFMAs, B after the
+        // stage's MFMAs), as in the INT8 loop.  F = 32-row fragment rows computed.
+        auto run32 = [&](auto f_tag) {
             constexpr int F = decltype(f_tag)::value;
-            AccT acc[FM][FN];
+            v4f acc[M32 ? FM32 : 1][M32 ? FN32 : 1][4];
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+            for (int i = 0; i < FM32; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = AccT{};
-            const int np = nk / 2;
-            for (int q = 0; q < np; ++q) {
-                if (q + 1 < np) {
-                    wait_vmcnt<0>();    // pair q+1 landed (nothing newer is in flight)
-                    barrier_nofence();  // ... for every wave, and every wave holds pair q
-                    if (2 * q + 4 < nk) {
-                        issue(2 * q + 4);
-                        issue(2 * q + 5);
-                    }
-                }
+                for (int j = 0; j < FN32; ++j)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[i][j][c] = v4f{0.f, 0.f, 0.f, 0.f};
+            auto mma_refill = [&](int next_ks, bool refill) {
 #pragma unroll
                 for (int i = 0; i < F; ++i) {
 #pragma unroll
-                    for (int j = 0; j < FN; ++j) acc[i][j] = mma128_fp8(fa8[i], fb8[j], acc[i][j]);
-                    fa8[i].lo = frag_a(2 * q + 2, i);
-                    fa8[i].hi = frag_a(2 * q + 3, i);
+                    for (int j = 0; j < FN32; ++j) mma32_fp8(fa32[i], fb32[j], acc[i][j]);
+                    if (refill) fa32[i] = frag_a32(next_ks, i);
                     __builtin_amdgcn_sched_barrier(0);
                 }
+            };
+            int ks = 0;
+            for (; ks + NS - 1 < nk; ++ks) {
+                wait_vmcnt<(NS - 3) * DPW>();
+                barrier_nofence();
+                issue(ks + NS - 1);
+                mma_refill(ks + 1, true);
                 if (F > 0) {
 #pragma unroll
-                    for (int j = 0; j < FN; ++j) {
-                        fb8[j].lo = frag_b(2 * q + 2, j);
-                        fb8[j].hi = frag_b(2 * q + 3, j);
-                    }
+                    for (int j = 0; j < FN32; ++j) fb32[j] = frag_b32(ks + 1, j);
                 }
             }
-            epilogue(acc, std::integral_constant<int, FN>{});
+            for (; ks + 1 < nk; ++ks) {
+                wait_vmcnt<0>();
+                barrier_nofence();
+                mma_refill(ks + 1, true);
+                if (F > 0) {
+#pragma unroll
+                    for (int j = 0; j < FN32; ++j) fb32[j] = frag_b32(ks + 1, j);
+                }
+            }
+            mma_refill(0, false);
+            epilogue32(acc);
         };
-        if (fm_active > FM / 2) run_pairs(std::integral_constant<int, FM>{});
-        else if (fm_active > 0) run_pairs(std::integral_constant<int, FM / 2>{});
-        else run_pairs(std::integral_constant<int, 0>{});
+        if (fm_active > FM / 2) run32(std::integral_constant<int, FM32>{});
+        else if (fm_active > 0) run32(std::integral_constant<int, FM32 / 2>{});
+        else run32(std::integral_constant<int, 0>{});
     } else {
         // A half tile: only its first FM*16 rows are copied, so a stage holds
         // FM A blocks instead of BM/16 and the same LDS ring takes more stages
@@ -587,16 +676,13 @@ template <int BM, int BN, int WM, int WN, int NS>
 hipError_t launch_tile(int epi, const GemmParams& p, int64_t blocks, hipStream_t s) {
     const dim3 grid((unsigned)blocks), block(WM * WN * 64);
     if (p.code == CODE_FP8) {
-        if constexpr (BN == 128) {  // the only FP8 tile (gemm_tile_n)
-            switch (epi) {
-                case EPI_DENSE_F32: gemm_i8<BM, BN, WM, WN, NS, EPI_DENSE_F32, CODE_FP8><<<grid, block, 0, s>>>(p); break;
-                case EPI_GATE_UP: gemm_i8<BM, BN, WM, WN, NS, EPI_GATE_UP, CODE_FP8><<<grid, block, 0, s>>>(p); break;
-                case EPI_DOWN: gemm_i8<BM, BN, WM, WN, NS, EPI_DOWN, CODE_FP8><<<grid, block, 0, s>>>(p); break;
-                default: return hipErrorInvalidValue;
-            }
-            return hipGetLastError();
+        switch (epi) {
+            case EPI_DENSE_F32: gemm_i8<BM, BN, WM, WN, NS, EPI_DENSE_F32, CODE_FP8><<<grid, block, 0, s>>>(p); break;
+            case EPI_GATE_UP: gemm_i8<BM, BN, WM, WN, NS, EPI_GATE_UP, CODE_FP8><<<grid, block, 0, s>>>(p); break;
+            case EPI_DOWN: gemm_i8<BM, BN, WM, WN, NS, EPI_DOWN, CODE_FP8><<<grid, block, 0, s>>>(p); break;
+            default: return hipErrorInvalidValue;
         }
-        return hipErrorInvalidValue;
+        return hipGetLastError();
     }
     if (p.code != CODE_INT8) return hipErrorInvalidValue;
     switch (epi) {
@@ -611,10 +697,7 @@ hipError_t launch_tile(int epi, const GemmParams& p, int64_t blocks, hipStream_t
 
 }  // namespace
 
-int gemm_tile_n(int64_t N, int code) {
-    // FP8 keeps two stages of fragments in registers: 256x128 tiles
-    return (code == CODE_INT8 && N % 256 == 0) ? 256 : 128;
-}
+int gemm_tile_n(int64_t N, int /*code*/) { return (N % 256 == 0) ? 256 : 128; }
 
 int device_cu_count() {
     static std::atomic<int> cache[64];

@@ -76,7 +76,7 @@ enum Code : int {
 // grouping in both operands), so the two products together cover all 64 k,
 // accumulated in fp32.  (That FP8 MFMA issues at a quarter of the rate of
 // the 16x16x128 one below: the register-fed skinny kernel, which streams
-// weights at HBM speed, uses it; the LDS-tiled GEMM uses mma128_fp8.)
+// weights at HBM speed, uses it; the LDS-tiled GEMM uses mma32_fp8.)
 typedef long v2l __attribute__((ext_vector_type(2)));
 template <int CODE>
 struct AccOf {
@@ -98,11 +98,18 @@ __device__ __forceinline__ typename AccOf<CODE>::type mma16(const v4i& a, const 
     }
 }
 
-// 16x16x128 FP8 E4M3 x E4M3 MFMA, fp32 accumulator (block scales fixed at 2^0:
-// E8M0 exponent 127).  A and B lanes pair the same byte positions, so the
-// product sums the 128 k of both operands whatever k each byte stands for.
-__device__ __forceinline__ v4f mma128_fp8(const v8i& a, const v8i& b, const v4f& c) {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+// 32x32x64 FP8 E4M3 x E4M3 MFMA with an fp32 accumulator (block scales fixed
+// at 2^0: E8M0 exponent 127).  A and B lanes pair the same byte positions, so
+// the product sums the 64 k of both operands whatever k each byte stands for.
+// The 16 accumulator registers are held as 4 x v4f (register q in [q/4][q%4]).
+typedef float v16f __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ void mma32_fp8(const v8i& a, const v8i& b, v4f (&c)[4]) {
+    v16f t;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) t[q] = c[q / 4][q % 4];
+    t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, t, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) c[q / 4][q % 4] = t[q];
 }
 
 enum Epilogue : int {
