@@ -124,7 +124,7 @@ def copy_calibration(torch, nbytes=1 << 30, reps=5):
                       "gbps_read_plus_write": round(2 * nbytes / dt / 1e9, 1)}), flush=True)
 
 
-def stage_work(T, H, E, k, I, touched):
+def stage_work(T, H, E, k, I, touched, code="int8"):
     """Algorithmic work per launch of each stage: (bound, amount, unit, peak).
 
     The grouped GEMMs count both their int8 ops and their algorithmic bytes
@@ -136,11 +136,12 @@ def stage_work(T, H, E, k, I, touched):
     gu_ops, dn_ops = 2 * A * H * 2 * I, 2 * A * I * H
     gu_bytes = touched * (2 * I * H + 8 * I) + A * H + 4 * T + 4 * A * I
     dn_bytes = touched * (H * I + 4 * H) + A * I + 8 * A + 4 * A * H
-    ridge = PEAK_INT8_OPS / PEAK_HBM
+    peak_mma = PEAK_INT8_OPS if code == "int8" else PEAK_FP8_OPS
+    ridge = peak_mma / PEAK_HBM
 
     def gemm(ops, nbytes):
         if ops / nbytes >= ridge:
-            return ("mfma", ops, "TOP/s", PEAK_INT8_OPS)
+            return ("mfma", ops, "TOP/s" if code == "int8" else "TFLOP/s", peak_mma)
         return ("hbm", nbytes, "GB/s", PEAK_HBM)
 
     return {
@@ -319,7 +320,7 @@ def main():
 
     counts = w8.workspace_views(ws, T, H, E, k, I)["expert_counts"].cpu()
     touched = int((counts > 0).sum())
-    work = stage_work(T, H, E, k, I, touched)
+    work = stage_work(T, H, E, k, I, touched, args.code)
     dom = max(stages, key=lambda s: stage_ms[s])
     bound, amount, unit, peak = work[dom]
     scale = 1e9 if unit == "GB/s" else 1e12
