@@ -17,13 +17,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int64_t t = i / hv;
     const int c = (int)(i - t * hv);
     const v4f* src = reinterpret_cast<const v4f*>(o) + (t * k) * hv + c;
+    // all k loads in flight before the sum (k <= MAX_TOPK)
+    v4f v[MAX_TOPK];
+#pragma unroll
+    for (int j = 0; j < MAX_TOPK; ++j)
+        if (j < k) v[j] = __builtin_nontemporal_load(src + (int64_t)j * hv);
     v4f acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-        const v4f v = __builtin_nontemporal_load(src + (int64_t)j * hv);
-        acc.x += v.x;
-        acc.y += v.y;
-        acc.z += v.z;
-        acc.w += v.w;
+#pragma unroll
+    for (int j = 0; j < MAX_TOPK; ++j) {
+        if (j < k) {
+            acc.x += v[j].x;
+            acc.y += v[j].y;
+            acc.z += v[j].z;
+            acc.w += v[j].w;
+        }
     }
     reinterpret_cast<v4f*>(y)[i] = acc;
 }
