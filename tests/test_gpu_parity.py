@@ -67,7 +67,11 @@ def test_quantize_hand_worked(w8):
 
 # ------------------------------------------------------------------ dense GEMM
 GEMM_SHAPES = [(1, 128, 128), (5, 256, 384), (128, 128, 128), (300, 384, 256), (129, 128, 1024),
-               (513, 640, 2048)]
+               (513, 640, 2048),
+               # 256-wide tiles: a 100-row half tile (all waves on 128 rows, deeper
+               # ring), a second m-tile of exactly 128 rows, a 200-row partial tile,
+               # and a half tile with a two-stage K loop
+               (100, 512, 640), (384, 256, 256), (200, 256, 256), (60, 256, 128)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
