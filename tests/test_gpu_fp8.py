@@ -300,3 +300,11 @@ def test_fp8_moe_large_shape_sampled(w8):
     checked on a few tokens (each touches 8 experts)."""
     inp = synth.moe_inputs("large", device="cuda", weights="fp8")
     check_moe_fp8(w8, inp, tokens=np.array([0, 7777, 16383]))
+
+
+def test_fp8_moe_ragged_narrow_hidden(w8):
+    """E4M3 codes with H = 384 (the down GEMM on 256x128 tiles), ragged T and a
+    segment mix of full, partial and half m-tiles."""
+    inp = synth.moe_inputs("edge", device="cuda", T=713, H=384, E=5, k=3, I=384, n_outlier=2,
+                           outlier_scale=20.0, bf16_x=False, bias="zero", weights="fp32")
+    check_moe_fp8(w8, inp)
