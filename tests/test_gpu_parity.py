@@ -311,6 +311,10 @@ EDGE = [
     dict(T=120, H=256, E=64, k=2, I=256, bias="zipf"),
     dict(T=128, H=256, E=64, k=2, I=128, bias="zipf"),
     dict(T=20, H=384, E=8, k=1, I=384),
+    # the largest hidden and intermediate sizes the ABI accepts: x (16384
+    # columns) and h (16384 columns) take the two-pass quantiser, K = 16384
+    dict(T=40, H=16384, E=8, k=2, I=128),
+    dict(T=30, H=128, E=4, k=2, I=16384),
 ]
 
 
