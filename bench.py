@@ -84,11 +84,20 @@ KERNEL_SOURCES = ["w8a8_quantized_moe_amd/csrc/gemm.hip", "w8a8_quantized_moe_am
                   "w8a8_quantized_moe_amd/csrc/abi.cpp"]
 
 
+def _code_only(text):
+    """Source text without comments and blank lines (a comment edit does not
+    change the kernels the counters were taken on)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_sources_hash():
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 

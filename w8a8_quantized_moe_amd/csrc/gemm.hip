@@ -13,30 +13,31 @@
 // accumulator, the output requantised for the next GEMM.
 //
 // Kernel shape (BM x BN output tile, WM x WN waves of 64 lanes):
-//  * every wave owns a (BM/WM) x (BN/WN) sub-tile of v_mfma_i32_16x16x64_i8
-//    blocks;
+//  * every wave owns a (BM/WM) x (BN/WN) sub-tile: INT8 as 16x16 blocks of
+//    v_mfma_i32_16x16x64_i8, FP8 as 32x32 blocks of
+//    v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales);
 //  * K advances 64 bytes per pipeline stage; NS stages live in LDS at once;
 //  * operands move global -> LDS with global_load_lds_dwordx4 (no VGPR
-//    staging): one wave instruction moves one 16-row x 64-byte MFMA fragment
-//    (1 KiB), lane l writing its 16 bytes at l*16, and every fragment read
-//    later is one conflict-free ds_read_b128.  The weight operand arrives
-//    pre-packed in fragment order (pack.hip); for the activation operand each
-//    4-lane group fetches one (possibly gathered) row's 64 bytes, stored at an
-//    XOR-swizzled slot;
+//    staging): one wave instruction moves one 16-row x 64-byte block (1 KiB),
+//    lane l writing its 16 bytes at l*16, and every fragment read later is a
+//    conflict-free ds_read_b128 (two per 32-byte FP8 operand).  The weight
+//    operand arrives pre-packed in fragment order (pack.hip); for the
+//    activation operand each 4-lane group fetches one (possibly gathered)
+//    row's 64 bytes, stored at an XOR-swizzled slot;
 //  * NS-1 stages of copies stay in flight: wait for stage s+1 (explicit
 //    vmcnt), barrier, issue stage s+NS-1, then run stage s's MFMAs from
-//    registers while stage s+1's fragments stream in from LDS.
+//    registers while stage s+1's fragments stream in from LDS;
+//  * a segment's last m-tile with at most 128 rows (INT8) copies only those
+//    rows through a deeper ring and spreads them over all waves.
 //
 // Workgroup -> tile order (XCD-aware).  Workgroups are dealt round-robin to the
-// 8 XCDs, so blockIdx % 8 names the XCD; each XCD takes one contiguous range
-// of the logical tile order (group, n-tile, m-tile; m-tile fastest).  Grouped
-// GEMMs thus give each XCD whole experts, and the m-tiles that share a weight
-// tile run side by side: an expert's gathered rows and its weights are
-// fetched into that XCD's L2 about once.  The dense GEMM is split into
-// 8 column stripes ("virtual groups" sharing the same rows), one per XCD, so
-// each weight tile is fetched once and the activations once per XCD.
-// Grouped tile counts are known only on the device (after routing): the grid
-// is sized for the worst case and surplus workgroups exit at once.
+// 8 XCDs, so blockIdx % 8 names the XCD; each XCD owns one contiguous range
+// of the logical tile order (group, n-tile, m-tile; m-tile fastest), so each
+// XCD works on whole experts and the m-tiles that share a weight tile start
+// side by side.  Grouped GEMMs run persistent: one workgroup per CU drains
+// its XCD's range as a queue (a counter the routing zeroed) and then helps
+// the other XCDs.  The dense GEMM is split into 8 column stripes ("virtual
+// groups" sharing the same rows), one per XCD, one tile per workgroup.
 #include <atomic>
 #include <type_traits>
 
