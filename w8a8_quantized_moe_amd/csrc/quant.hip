@@ -8,6 +8,12 @@
 // ("DeepSeek V4 '950' unified FP8 dataflow", sec. 2.1: E4M3, range +-448)
 // s = max|x| / 448 and the code is E4M3(x / s), rounded to nearest even.
 //
+// Options ("W8A8 quantisation of MiniMax-M3 on K100AI", sec. 2.2; "DeepSeek V4
+// '950'", sec. 3.1): a per-column factor (SmoothQuant) multiplies each value
+// in fp32 before the row maximum is taken, and the scale's base is the row
+// maximum (dynamic), the row maximum capped by a calibrated bound (clipped)
+// or the bound alone (static); codes then saturate (INT8 clamp, E4M3 +-448).
+//
 // HBM-bound: each row is read once (cached in VGPRs while its maximum is
 // reduced: one wave per row up to 1024 columns, one 256-thread workgroup per
 // row above), and its codes and scale written once.  Loads and stores are

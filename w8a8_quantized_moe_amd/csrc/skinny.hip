@@ -1,4 +1,6 @@
-// Grouped INT8 GEMM for expert segments of a few rows (the decode regime).
+// Grouped INT8 (or FP8 E4M3) GEMM for expert segments of a few rows (the
+// decode regime).  FP8 uses two v_mfma_f32_16x16x32_fp8_fp8 per 64-k fragment
+// (a quarter of the FP8 matrix rate, which the weight streaming never needs).
 //
 // Same computation and epilogues as the tiled grouped GEMM (gemm.hip): the
 // int32 accumulators of x_q . W^T per expert ("W8A8 quantisation of
