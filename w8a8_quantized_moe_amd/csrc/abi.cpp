@@ -324,7 +324,7 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     int32_t* tile_ctr = (int32_t*)(ws + plan.tile_ctr);
 
     auto mark = [&](int i) -> w8a8_status {
-        if (!events) return W8A8_OK;
+        if (!events || !events[i]) return W8A8_OK;
         return check_hip(hipEventRecord((hipEvent_t)events[i], s), "hipEventRecord");
     };
 
