@@ -326,6 +326,27 @@ def test_moe_edge_cases(w8, case):
     check_moe(w8, inp)
 
 
+# From 2048 tokens the router weights are split into bf16 planes ahead of the
+# router GEMM (expert tiles of 32, 64 or 128 by E); these cover each tile
+# width, an expert count padded to a whole tile, a ragged last token tile and
+# split sums along H.
+ROUTER_PLANES = [
+    dict(T=2048, H=256, E=256, k=8, I=128),
+    dict(T=2100, H=512, E=24, k=2, I=128),
+    dict(T=2049, H=1024, E=50, k=4, I=128),
+    dict(T=4096, H=384, E=200, k=6, I=128),
+    dict(T=2048, H=256, E=100, k=3, I=128, bias="zipf"),
+]
+
+
+@pytest.mark.parametrize("case", ROUTER_PLANES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_moe_router_planes(w8, case):
+    over = dict(n_outlier=2, outlier_scale=20.0, bf16_x=False, bias="zero", weights="int8")
+    over.update(case)
+    inp = synth.moe_inputs("edge", device="cuda", **over)
+    check_moe(w8, inp)
+
+
 def test_moe_router_wide_dynamic_range(w8):
     """Router operands whose values span 2^-20 .. 2^20: column h of x is scaled
     by 2^s_h and column h of the router matrix by 2^-s_h, so every product
@@ -333,7 +354,12 @@ def test_moe_router_wide_dynamic_range(w8):
     binades.  The bf16 three-term split of the router GEMM must still give
     logits within the fp32 error bound of the fp64 oracle, with exact routing
     away from near ties (all checked in check_moe)."""
-    inp = synth.moe_inputs("edge", device="cuda", T=192, H=512, E=40, k=4, I=128, n_outlier=2,
+    for T in (192, 2048):  # router weights split in the GEMM, then ahead of it
+        _wide_range_case(w8, T)
+
+
+def _wide_range_case(w8, T):
+    inp = synth.moe_inputs("edge", device="cuda", T=T, H=512, E=40, k=4, I=128, n_outlier=2,
                            outlier_scale=20.0, bf16_x=False, bias="zero", weights="int8")
     g = torch.Generator(device="cuda").manual_seed(11)
     sh = torch.randint(-20, 21, (inp["H"],), generator=g, device="cuda").float()

@@ -46,8 +46,9 @@ int moe_bm(int64_t A, int64_t E) { return A <= 4 * E ? w8a8::SKINNY_BM : w8a8::G
 
 struct MoePlan {
     w8a8_moe_workspace_layout lay;
-    size_t partial, rank, chunk_counts, chunk_base, mt_prefix, mt_info, tile_ctr;
+    size_t partial, wplanes, rank, chunk_counts, chunk_base, mt_prefix, mt_info, tile_ctr;
     int splits, nchunks;
+    bool has_planes;
 };
 
 w8a8_status check_moe_shape(const w8a8_moe_shape* sh) {
@@ -74,7 +75,8 @@ w8a8_status check_moe_shape(const w8a8_moe_shape* sh) {
 MoePlan plan_moe(const w8a8_moe_shape* sh) {
     MoePlan p{};
     const int64_t T = sh->T, H = sh->H, E = sh->E, k = sh->top_k, I = sh->I, A = T * k;
-    p.splits = T > 0 ? w8a8::router_splits((int)T, (int)E, (int)H) : 1;
+    const w8a8::RouterPlan rp = T > 0 ? w8a8::router_plan((int)T, (int)E, (int)H) : w8a8::RouterPlan{1, 0};
+    p.splits = rp.splits;
     p.nchunks = (int)((T + w8a8::ROUTE_CHUNK - 1) / w8a8::ROUTE_CHUNK);
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -97,6 +99,8 @@ MoePlan plan_moe(const w8a8_moe_shape* sh) {
     L.o = take(A * H * 4);
     L.internal = off;
     p.partial = take((size_t)p.splits * T * E * 4);
+    p.wplanes = rp.planes_bytes ? take(rp.planes_bytes) : 0;
+    p.has_planes = rp.planes_bytes > 0;
     p.rank = take(A * 4);
     p.chunk_counts = take((size_t)E * p.nchunks * 4);
     p.chunk_base = take((size_t)E * p.nchunks * 4);
@@ -337,6 +341,7 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     w8a8::RouteInputs ri{x, wts->router_w, wts->router_b, T, H, E, k, plan.splits, bm};
     w8a8::RouteBuffers rb{};
     rb.partial = (float*)(ws + plan.partial);
+    rb.wplanes = plan.has_planes ? (void*)(ws + plan.wplanes) : nullptr;
     rb.logits = (float*)(ws + L.logits);
     rb.topk_ids = (int32_t*)(ws + L.topk_ids);
     rb.topk_w = topk_w;

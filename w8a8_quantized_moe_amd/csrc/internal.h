@@ -183,21 +183,29 @@ hipError_t launch_gemm(int epi, const GemmParams& p, int64_t max_m_tiles, hipStr
 constexpr int SKINNY_BM = 16;
 hipError_t launch_gemm_skinny(int epi, const GemmParams& p, int64_t max_row_blocks, hipStream_t s);
 
-// Number of partial sums the router GEMM splits H into (so a small token
-// count still yields enough workgroups); the workspace holds S*T*E floats.
-int router_splits(int T, int E, int H);
+// How the router GEMM runs for a shape: the number of partial sums S it
+// splits H into (so a small token count still yields enough workgroups; the
+// workspace then holds S*T*E floats), and whether the router weights are
+// first split into bf16 planes in the workspace (planes_bytes > 0, large
+// token counts) or split inside the GEMM.
+struct RouterPlan {
+    int splits;
+    size_t planes_bytes;
+};
+RouterPlan router_plan(int T, int E, int H);
 
 struct RouteInputs {
     const float* x;         // [T][H]
     const float* router_w;  // [E][H]
     const float* router_b;  // [E] or nullptr
     int T, H, E, k;
-    int splits;             // router_splits(T, E, H)
+    int splits;             // router_plan(T, E, H).splits
     int bm;                 // m-tile height of the grouped GEMMs (GEMM_BM or SKINNY_BM)
 };
 
 struct RouteBuffers {
     float* partial;           // [S][T][E]
+    void* wplanes;            // router_plan(T, E, H).planes_bytes bytes, or nullptr
     float* logits;            // [T][E]
     int32_t* topk_ids;        // [T][k]
     float* topk_w;            // [T][k]

@@ -14,6 +14,11 @@
 //                   terms), 64-token x all-expert tiles (activations read
 //                   once), optionally split along H into S partial sums so
 //                   small token counts still fill the GPU;
+//   router_w_planes (many tokens) splits the router weights into three bf16
+//                   planes in MFMA fragment order, once per call;
+//   router_planes   the same GEMM reading those planes, 128-token x
+//                   32*EB-expert tiles (only the activations are split in
+//                   the main loop);
 //   router_reduce   (split only) sums the S partials in split order (a fixed,
 //                   deterministic order) and adds the bias;
 //   topk_count      per 64-token chunk: picks the top-k by wave arg-max rounds
@@ -235,6 +240,198 @@ __global__ __launch_bounds__(512) void router_bf16x3(const float* __restrict__ x
             }
 }
 
+// The same product with the router weights split ahead of the GEMM.  In the
+// kernel above each wave splits the router rows it multiplies, and the two
+// token halves split the same rows: two thirds of its vector work.  For many
+// tokens the weights are split once per call by router_w_planes into three
+// bf16 planes laid out in MFMA fragment order, and router_planes copies those
+// straight into LDS, so the GEMM splits only its activations.
+//
+// Plane layout: fragment (ks, b, p) = 1 KiB at ((ks * NEB + b) * 3 + p) * 1024
+// for k-stage ks (32 of H), 16-expert block b (NEB blocks, padded with zero
+// rows to a whole expert tile) and term p; lane l's 16 bytes are the eight
+// bf16 terms of expert 16b + l%16, k = 32ks + (l/16)*8 .. +7.
+__global__ __launch_bounds__(256) void router_w_planes(const float* __restrict__ wr, int E, int H, int NEB,
+                                                       int8_t* __restrict__ planes) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one lane of one (ks, b)
+    const int64_t n = (int64_t)(H / RBK) * NEB * 64;
+    if (i >= n) return;
+    const int lane = (int)(i & 63);
+    const int64_t kb = i >> 6;  // ks * NEB + b
+    const int b = (int)(kb % NEB), ks = (int)(kb / NEB);
+    const int e = b * 16 + (lane & 15);
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), c = a;
+    if (e < E) {
+        const float* src = wr + (int64_t)e * H + ks * RBK + (lane >> 4) * 8;
+        a = *reinterpret_cast<const float4*>(src);
+        c = *reinterpret_cast<const float4*>(src + 4);
+    }
+    bf16x8 pl[3];
+    split3(a, c, pl);
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+        *reinterpret_cast<bf16x8*>(planes + (kb * 3 + q) * 1024 + lane * 16) = pl[q];
+}
+
+// Workgroup: 128 tokens x 32*EB experts, 8 waves = 4 token quarters x 2
+// expert halves; a wave owns 32 tokens x 16*EB experts (2 x EB blocks of
+// v_mfma_f32_16x16x32_bf16), as above.  blockIdx.x is the expert tile (so the
+// workgroups that share an activation tile are dispatched together),
+// blockIdx.y the token tile, blockIdx.z the split of H.  A stage holds the
+// activation tile (16 copy blocks of 8 rows, swizzled as above) and the
+// expert tile's 6*EB plane fragments, padded with repeat copies to a whole
+// number of blocks per wave (the repeats land in slots nobody reads).
+template <int EB>
+struct RouterPlanesCfg {
+    static constexpr int XBLK = 16;
+    static constexpr int WBLK = 6 * EB;
+    static constexpr int NBLK = (XBLK + WBLK + 7) / 8 * 8;
+    static constexpr int DPW = NBLK / 8;
+    static constexpr int STAGE = NBLK * 1024;
+    static constexpr int NS = (163840 / STAGE) < 6 ? (163840 / STAGE) : 6;
+};
+
+template <int EB>
+__global__ __launch_bounds__(512) void router_planes(const float* __restrict__ x,
+                                                     const int8_t* __restrict__ planes,
+                                                     const float* __restrict__ bias, int T, int H,
+                                                     int E, int NEB, int ksplit_len,
+                                                     float* __restrict__ partial) {
+    using C = RouterPlanesCfg<EB>;
+    constexpr int NS = C::NS, DPW = C::DPW, STAGE = C::STAGE, XBLK = C::XBLK, WBLK = C::WBLK;
+    static_assert(NS >= 3, "at least one stage in flight beyond the pair being read");
+    __shared__ __attribute__((aligned(1024))) int8_t smem[NS * STAGE];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wt = w >> 1, we = w & 1;
+    const int e_tile = blockIdx.x, m0 = blockIdx.y * 128;
+    const int kbeg = blockIdx.z * ksplit_len;
+    const int nk = ksplit_len / RBK, ks0 = kbeg / RBK;
+
+    // copy sources and their per-stage strides
+    const int8_t* src[DPW];
+    int64_t stride[DPW];
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) {
+        const int b = w + 8 * i;
+        if (b < XBLK) {
+            const int chunk = (lane & 7) ^ (lane >> 3);
+            const int t = min(m0 + b * 8 + (lane >> 3), T - 1);
+            src[i] = reinterpret_cast<const int8_t*>(x + (int64_t)t * H + kbeg + chunk * 4);
+            stride[i] = RBK * 4;
+        } else {
+            const int j = (b < XBLK + WBLK ? b : XBLK) - XBLK;  // padding repeats fragment 0
+            const int64_t frag = ((int64_t)ks0 * NEB + e_tile * 2 * EB + j / 3) * 3 + j % 3;
+            src[i] = planes + frag * 1024 + lane * 16;
+            stride[i] = (int64_t)NEB * 3 * 1024;
+        }
+    }
+    auto issue = [&](int ks) {
+        const int8_t* stage = smem + (ks % NS) * STAGE;
+#pragma unroll
+        for (int i = 0; i < DPW; ++i) dma16(src[i] + (int64_t)ks * stride[i], stage + (w + 8 * i) * 1024);
+    };
+    const int frow = lane & 15, fc = (lane >> 4) * 2;
+    auto read_x = [&](int ks, float4 (&raw)[2][2]) {
+        const int8_t* stage = smem + (ks % NS) * STAGE;
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            const int row = wt * 32 + f * 16 + frow;
+            const int8_t* rp = stage + row * 128;
+            raw[f][0] = *reinterpret_cast<const float4*>(rp + ((fc ^ (row & 7)) * 16));
+            raw[f][1] = *reinterpret_cast<const float4*>(rp + (((fc + 1) ^ (row & 7)) * 16));
+        }
+    };
+    auto read_w = [&](int ks, bf16x8 (&pb)[EB][3]) {
+        const int8_t* stage = smem + (ks % NS) * STAGE + XBLK * 1024;
+#pragma unroll
+        for (int j = 0; j < EB; ++j)
+#pragma unroll
+            for (int q = 0; q < 3; ++q)
+                pb[j][q] = *reinterpret_cast<const bf16x8*>(stage + ((we * EB + j) * 3 + q) * 1024 + lane * 16);
+    };
+
+    v4f acc[2][EB];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < EB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    bf16x8 pa[2][3], pb[EB][3];
+    constexpr int TA[6] = {1, 0, 2, 0, 1, 0};
+    constexpr int TB[6] = {1, 2, 0, 1, 0, 0};
+    auto step = [&](int ks_next, auto next_tag) {
+        constexpr bool NEXT = decltype(next_tag)::value;
+        float4 raw[2][2];
+        bf16x8 na[2][3], nb[EB][3];
+        if (NEXT) {
+            read_x(ks_next, raw);
+            read_w(ks_next, nb);
+        }
+#pragma unroll
+        for (int tm = 0; tm < 6; ++tm) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < EB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[i][TA[tm]], pb[j][TB[tm]],
+                                                                        acc[i][j], 0, 0, 0);
+            if (NEXT && tm < 2) split3(raw[tm][0], raw[tm][1], na[tm]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (NEXT) {
+#pragma unroll
+            for (int t = 0; t < 3; ++t) {
+                pa[0][t] = na[0][t];
+                pa[1][t] = na[1][t];
+#pragma unroll
+                for (int j = 0; j < EB; ++j) pb[j][t] = nb[j][t];
+            }
+        }
+    };
+
+    int issued = 0;
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < nk) {
+            issue(s);
+            ++issued;
+        }
+    if (issued == NS - 1) wait_vmcnt<(NS - 2) * DPW>();
+    else wait_vmcnt<0>();
+    barrier_nofence();
+    {
+        float4 raw[2][2];
+        read_x(0, raw);
+        read_w(0, pb);
+        split3(raw[0][0], raw[0][1], pa[0]);
+        split3(raw[1][0], raw[1][1], pa[1]);
+    }
+    int ks = 0;
+    for (; ks + NS - 1 < nk; ++ks) {
+        wait_vmcnt<(NS - 3) * DPW>();
+        barrier_nofence();
+        issue(ks + NS - 1);
+        step(ks + 1, std::true_type{});
+    }
+    wait_vmcnt<0>();
+    barrier_nofence();
+    for (; ks + 1 < nk; ++ks) step(ks + 1, std::true_type{});
+    step(0, std::false_type{});
+
+    float* out = partial + (int64_t)blockIdx.z * T * E;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < EB; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = m0 + wt * 32 + i * 16 + (lane >> 4) * 4 + r;
+                const int e = (e_tile * 2 * EB + we * EB + j) * 16 + (lane & 15);
+                if (t < T && e < E)
+                    out[(int64_t)t * E + e] = (bias && gridDim.z == 1) ? acc[i][j][r] + bias[e] : acc[i][j][r];
+            }
+}
+
 // logits[t][e] = (sum of the S split partials, in split order) + bias[e]
 __global__ __launch_bounds__(256) void router_reduce(const float* __restrict__ partial, int S,
                                                      const float* __restrict__ bias, int T, int E,
@@ -411,28 +608,49 @@ __global__ __launch_bounds__(256) void scatter(const int32_t* __restrict__ ids, 
 
 }  // namespace
 
-int router_splits(int T, int E, int H) {
-    (void)E;
+// Token counts from which the router weights are split ahead of the GEMM (the
+// extra launch pays once the GEMM runs many token tiles).
+constexpr int ROUTER_PLANES_MIN_T = 2048;
+
+static int router_planes_eb(int E) { return E > 64 ? 4 : (E > 32 ? 2 : 1); }
+
+RouterPlan router_plan(int T, int E, int H) {
+    const bool planes = T >= ROUTER_PLANES_MIN_T;
     // enough workgroups to fill the GPU, at least 8 stages (256 of H) per split
     // (4 when there are few token tiles: each stage of a split costs about one
     // memory round trip); the split count divides the stage count H/32
-    const int tiles = (T + RBM - 1) / RBM;
+    int tiles = (T + RBM - 1) / RBM;
+    size_t bytes = 0;
+    if (planes) {
+        const int eb = router_planes_eb(E), etiles = (E + 32 * eb - 1) / (32 * eb);
+        tiles = (T + 127) / 128 * etiles;
+        bytes = (size_t)H * etiles * 32 * eb * 6;
+    }
     const int stages = H / RBK;
     int s = 1;
     const int min_stages = tiles >= 16 ? 8 : 4;
     while (tiles * s < 256 && stages % (2 * s) == 0 && stages / (2 * s) >= min_stages) s *= 2;
-    return s;
+    return RouterPlan{s, bytes};
 }
 
 hipError_t launch_route(const RouteInputs& in, const RouteBuffers& b, hipStream_t s) {
     const int T = in.T, E = in.E, k = in.k, H = in.H, S = in.splits;
     const int nchunks = (T + ROUTE_CHUNK - 1) / ROUTE_CHUNK;
     MtInfo* mt_info = reinterpret_cast<MtInfo*>(b.mt_info);
-    {
+    float* out = (S == 1) ? b.logits : b.partial;
+    const float *xx = in.x, *wr = in.router_w, *rb = in.router_b;
+    if (b.wplanes) {
+        const int eb = router_planes_eb(E), etiles = (E + 32 * eb - 1) / (32 * eb), neb = etiles * 2 * eb;
+        int8_t* planes = static_cast<int8_t*>(b.wplanes);
+        const int64_t n = (int64_t)(H / RBK) * neb * 64;
+        router_w_planes<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>(wr, E, H, neb, planes);
+        const dim3 grid(etiles, (T + 127) / 128, S);
+        if (eb == 1) router_planes<1><<<grid, 512, 0, s>>>(xx, planes, rb, T, H, E, neb, H / S, out);
+        else if (eb == 2) router_planes<2><<<grid, 512, 0, s>>>(xx, planes, rb, T, H, E, neb, H / S, out);
+        else router_planes<4><<<grid, 512, 0, s>>>(xx, planes, rb, T, H, E, neb, H / S, out);
+    } else {
         const dim3 grid((T + RBM - 1) / RBM, S);
         const int eb = (E + 63) / 64;
-        float* out = (S == 1) ? b.logits : b.partial;
-        const float *xx = in.x, *wr = in.router_w, *rb = in.router_b;
         if (eb == 1) router_bf16x3<1><<<grid, 512, 0, s>>>(xx, wr, rb, T, H, E, H / S, out);
         else if (eb == 2) router_bf16x3<2><<<grid, 512, 0, s>>>(xx, wr, rb, T, H, E, H / S, out);
         else if (eb == 3) router_bf16x3<3><<<grid, 512, 0, s>>>(xx, wr, rb, T, H, E, H / S, out);
