@@ -15,8 +15,10 @@ Prints one JSON line: tokens/s of the whole job over the K timed steps, the
 per-stage times (HIP events recorded on the layer's stream at every stage
 boundary, in a separate pass of K steps before the timed ones), the roofline
 of the dominant kernel (its launch time from the two events around it in
-every timed step), whole-layer INT8 TOPS and algorithmic HBM GB/s, and the
-CPU oracle timed on a bounded token sample.
+every timed step), whole-layer INT8 TOPS and algorithmic HBM GB/s, the rate
+a plain 1 GiB device copy attains (measured after the timed steps), the
+device's CU count and peak clock, and the CPU oracle timed on a bounded token
+sample.
 """
 from __future__ import annotations
 
@@ -25,6 +27,8 @@ import ctypes
 import hashlib
 import json
 import os
+import re
+import subprocess
 import sys
 import time
 
@@ -133,6 +137,44 @@ def copy_calibration(torch, nbytes=1 << 30, reps=5):
     dt = (time.perf_counter() - t0) / reps
     print(json.dumps({"copy_bytes_each_way": nbytes, "reps": reps, "ms": round(dt * 1e3, 4),
                       "gbps_read_plus_write": round(2 * nbytes / dt / 1e9, 1)}), flush=True)
+
+
+def attainable_hbm(torch, nbytes=1 << 30, reps=10):
+    """What a plain device copy reaches on this device (context for the
+    roofline fractions, which use the published 8 TB/s): a 1 GiB copy, bytes
+    read plus written, timed with events after a warm-up."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    gbps = 2 * nbytes * reps / (s.elapsed_time(e) * 1e-3) / 1e9
+    del src, dst
+    return {"copy_GBps": round(gbps, 1), "frac_of_peak": round(gbps * 1e9 / PEAK_HBM, 4),
+            "method": f"torch copy_ of 1 GiB fp32, {reps} reps, read + write bytes"}
+
+
+def device_info(torch):
+    """Compute units and the peak engine clock (rocminfo), with the INT8 matrix
+    peak they imply (8192 int8 ops per CU per clock), beside the published one."""
+    info = {"cus": torch.cuda.get_device_properties(0).multi_processor_count, "max_sclk_mhz": None}
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30).stdout
+        for blk in txt.split("Agent ")[1:]:
+            if "gfx950" in blk:
+                m = re.search(r"Max Clock Freq\. \(MHz\):\s*(\d+)", blk)
+                info["max_sclk_mhz"] = int(m.group(1)) if m else None
+                break
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if info["max_sclk_mhz"]:
+        info["int8_peak_at_max_clock_tops"] = round(8192 * info["cus"] * info["max_sclk_mhz"] / 1e6, 1)
+    return info
 
 
 def stage_work(T, H, E, k, I, touched, code="int8"):
@@ -251,6 +293,8 @@ def bench_dense(args, torch, synth, w8):
     }
     for e in events:
         hip.destroy(e)
+    out_line["attainable_hbm"] = attainable_hbm(torch)
+    out_line["device"] = device_info(torch)
     print(json.dumps(out_line), flush=True)
 
 
@@ -388,6 +432,8 @@ def main():
         "stage_ms": {s: round(v, 4) for s, v in stage_ms.items()},
         "roofline": roofline,
     }
+    out["attainable_hbm"] = attainable_hbm(torch)
+    out["device"] = device_info(torch)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a token sample")
         cb = cpu_baseline(inp, args.cpu_seconds, args.code)
