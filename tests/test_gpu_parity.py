@@ -34,7 +34,9 @@ def _say(msg):
 
 # ------------------------------------------------------------------ quantisation
 QUANT_SHAPES = [(1, 4, 4), (3, 130, 130), (37, 128, 128), (1000, 4096, 4096), (64, 7168, 7168),
-                (5, 8192, 8192), (7, 10000, 10000), (2, 1, 1), (9, 256, 300), (4, 2048, 2051)]
+                (5, 8192, 8192), (7, 10000, 10000), (2, 1, 1), (9, 256, 300), (4, 2048, 2051),
+                # one wave per row up to 2048 columns (eight float4 per lane)
+                (9, 1028, 1028), (70, 1536, 1536), (33, 2048, 2048), (6, 2052, 2052)]
 
 
 @pytest.mark.parametrize("rows,cols,ld", QUANT_SHAPES)
@@ -427,7 +429,7 @@ def test_quantize_rows_half_integer_and_tiny_scales(w8):
 
 
 # ------------------------------------------- activation-scale options (smoothing, clip, static)
-QEX_SHAPES = [(5, 100), (33, 1024), (7, 1028), (6, 4096), (3, 8192), (2, 10001), (4, 8200)]
+QEX_SHAPES = [(5, 100), (33, 1024), (7, 1028), (5, 2048), (6, 4096), (3, 8192), (2, 10001), (4, 8200)]
 
 
 @pytest.mark.parametrize("rows,cols", QEX_SHAPES)

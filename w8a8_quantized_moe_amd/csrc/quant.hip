@@ -15,7 +15,7 @@
 // or the bound alone (static); codes then saturate (INT8 clamp, E4M3 +-448).
 //
 // HBM-bound: each row is read once (cached in VGPRs while its maximum is
-// reduced: one wave per row up to 1024 columns, one 256-thread workgroup per
+// reduced: one wave per row up to 2048 columns, one 256-thread workgroup per
 // row above), and its codes and scale written once.  Loads and stores are
 // 16-byte (read) / 4-byte (write) per lane and contiguous across the wave.
 #include "device_common.h"
@@ -129,7 +129,7 @@ hipError_t launch_quant(const float* x, int64_t rows, int64_t cols, int64_t ld, 
     const bool vec = (cols % 4 == 0) && (ld % 4 == 0) && ((uintptr_t)x % 16 == 0) &&
                      ((uintptr_t)q % 4 == 0) && ((uintptr_t)opt.col_mul % 16 == 0) &&
                      cols <= 8 * 1024;
-    if (vec && cols > 1024) {
+    if (vec && cols > 2048) {
         const int nv = (int)(cols / 4);
         const int need = (nv + 255) / 256;
         const dim3 g1((unsigned)rows);
@@ -146,8 +146,10 @@ hipError_t launch_quant(const float* x, int64_t rows, int64_t cols, int64_t ld, 
             quant_rows_cached<CODE, 1><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale, opt);
         else if (need <= 2)
             quant_rows_cached<CODE, 2><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale, opt);
-        else
+        else if (need <= 4)
             quant_rows_cached<CODE, 4><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale, opt);
+        else
+            quant_rows_cached<CODE, 8><<<grid, block, 0, s>>>(x, rows, (int)cols, ld, q, scale, opt);
     } else {
         quant_rows_twopass<CODE><<<grid, block, 0, s>>>(x, rows, cols, ld, q, scale, opt);
     }
