@@ -89,7 +89,10 @@ def _fp8_gemm_bound(a_codes, b_codes, s_a, s_b, ref):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (100, 256, 384), (257, 384, 1024), (300, 256, 2048),
-                                   (513, 640, 4096)])
+                                   (513, 640, 4096),
+                                   # last m-tiles of 128 and 74 rows on 256-wide tiles (the half-tile
+                                   # schedule: all eight waves on those rows)
+                                   (384, 512, 256), (330, 768, 640)])
 def test_fp8_gemm_within_accumulation_bound(w8, M, N, K):
     print(f"fp8 gemm M={M} N={N} K={K}", flush=True)
     g = torch.Generator().manual_seed(M + N + K)

@@ -119,10 +119,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     // WM = 2) runs its own schedule (run_half below): only the first FM*16
     // rows are copied, so a stage is smaller and the ring deeper, and all
     // waves share those rows and split the columns, FN/WM fragment columns
-    // each.  (INT8 only; for the gate-up epilogue only where each wave keeps
-    // whole gate/up column pairs.)
-    constexpr bool HALF_OK = CODE == CODE_INT8 && FN % WM == 0 &&
-                             (EPI != EPI_GATE_UP || (FN / WM) % 2 == 0);
+    // each.  (For the gate-up epilogue and for FP8 codes, whose 32x32 MFMA
+    // blocks span two fragment columns, only where each wave keeps an even
+    // number of fragment columns.)
+    constexpr bool HALF_OK = FN % WM == 0 &&
+                             ((EPI != EPI_GATE_UP && CODE == CODE_INT8) || (FN / WM) % 2 == 0);
     const int rows_valid = (int)(row_end - row0);
     const bool half = HALF_OK && rows_valid <= FM * 16;
     // first fragment row / column of this wave
@@ -224,7 +225,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
         t.hi = *reinterpret_cast<const LDS_AS v4i*>(base + (cc + 32 * h + 16) * 16);
         return t;
     };
-    if constexpr (M32) {
+    if (half) {
+        // (a half tile fills its own ring: run_half)
+    } else if constexpr (M32) {
         // prologue: NS-1 stages in flight, stage 0's fragments in registers
 #pragma unroll
         for (int s = 0; s < NS - 1; ++s)
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
             if (2 * i < fm_active) fa32[i] = frag_a32(0, i);
 #pragma unroll
         for (int j = 0; j < FN32; ++j) fb32[j] = frag_b32(0, j);
-    } else if (!half) {  // (a half tile fills its own ring: run_half)
+    } else {
         // prologue: NS-1 stages in flight, stage 0's fragments in registers
 #pragma unroll
         for (int s = 0; s < NS - 1; ++s)
@@ -362,8 +365,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     //      row (a_base + 2i)*16 + (q/4)*8 + (l/32)*4 + q%4, column
     //      (b_base + 2j)*16 + l%32; the gate and up values of one channel sit
     //      16 lanes apart. ----
-    auto epilogue32 = [&](v4f (&acc)[M32 ? FM32 : 1][M32 ? FN32 : 1][4]) {
-        constexpr int NF = FN;
+    auto epilogue32 = [&](auto& acc, auto nj_tag) {
+        constexpr int NJ = decltype(nj_tag)::value;  // 32-column blocks of this wave
+        constexpr int NF = 2 * NJ;
         constexpr int OCOLS = (EPI == EPI_GATE_UP) ? NF * 8 : NF * 16;
         constexpr int SROW = OCOLS + 4;
         __syncthreads();  // the ring is idle; row metadata written before the loop is visible
@@ -372,9 +376,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
         const int h = lane >> 5, c32 = lane & 31, up = (lane >> 4) & 1;
         const int64_t col0 = (EPI == EPI_GATE_UP) ? (int64_t)(nt * NBB + b_base) / 2 * 16
                                                   : (int64_t)nt * BN + b_base * 16;
-        float s_col[FN32];
+        float s_col[NJ];
 #pragma unroll
-        for (int j = 0; j < FN32; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             if (EPI == EPI_GATE_UP)
                 s_col[j] = p.s_b[(int64_t)g * 2 * I + (up ? I : 0) + col0 + j * 16 + (lane & 15)];
             else
@@ -394,7 +398,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
                     const int row = (a_base + 2 * i) * 16 + lr0;
                     const float sx0 = row_scale[row], sx1 = row_scale[row + 1];
 #pragma unroll
-                    for (int j = 0; j < FN32; ++j) {
+                    for (int j = 0; j < NJ; ++j) {
                         const float v0 = (acc[i][j][q / 4][q % 4] * sx0) * s_col[j];
                         const float v1 = (acc[i][j][q / 4][q % 4 + 1] * sx1) * s_col[j];
                         const float got = __shfl_xor(up ? v0 : v1, 16, 64);
@@ -409,7 +413,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
                     const int lr = (q / 4) * 8 + h * 4 + (q % 4);    // staged row
                     const int row = (a_base + 2 * i) * 16 + lr;      // tile row
 #pragma unroll
-                    for (int j = 0; j < FN32; ++j) {
+                    for (int j = 0; j < NJ; ++j) {
                         const float dq = (acc[i][j][q / 4][q % 4] * row_scale[row]) * s_col[j];
                         const float v = (EPI == EPI_DOWN) ? row_w[row] * dq : dq;
                         stg[lr * SROW + j * 32 + c32] = __float_as_uint(v);
@@ -470,96 +474,48 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
         mfma_and_refill(f_tag, acc, 0, false);
         epilogue(acc, std::integral_constant<int, FN>{});
     };
-    if constexpr (M32) {
-        // FP8: stage ks's MFMAs run from registers while stage ks+1's fragments
-        // come in (each A fragment row right after its MFMAs, B after the
-        // stage's MFMAs), as in the INT8 loop.  F = 32-row fragment rows computed.
-        auto run32 = [&](auto f_tag) {
-            constexpr int F = decltype(f_tag)::value;
-            v4f acc[M32 ? FM32 : 1][M32 ? FN32 : 1][4];
+    // A half tile: only its first FM*16 rows are copied, so a stage holds
+    // FM A blocks instead of BM/16 and the same LDS ring takes more stages
+    // (5 instead of 4 for 256x256 tiles: four in flight instead of three).
+    // A segment's last tile streams the whole weight tile for few rows,
+    // which makes it bound by the copy pipeline's latency; the deeper
+    // ring and all eight waves at work (each on FN/WM fragment columns of
+    // those rows) shorten it.
+    auto run_half = [&](auto f_tag) {
+        constexpr int F = decltype(f_tag)::value;
+        constexpr int NF = FN / WM;
+        constexpr int NBLK_H = FM + NBB;
+        static_assert(NBLK_H % NW == 0, "half-tile blocks must split evenly over the waves");
+        constexpr int DPW_H = NBLK_H / NW;
+        constexpr int STAGE_H = NBLK_H * 1024;
+        constexpr int NS_H = (NS * STAGE) / STAGE_H < 8 ? (NS * STAGE) / STAGE_H : 8;
+        static_assert(NS_H >= NS && NS_H * STAGE_H <= NS * STAGE, "the half-tile ring fits the ring");
+        const int8_t* hsrc[DPW_H];
+        int hstride[DPW_H];
 #pragma unroll
-            for (int i = 0; i < FM32; ++i)
-#pragma unroll
-                for (int j = 0; j < FN32; ++j)
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) acc[i][j][c] = v4f{0.f, 0.f, 0.f, 0.f};
-            auto mma_refill = [&](int next_ks, bool refill) {
-#pragma unroll
-                for (int i = 0; i < F; ++i) {
-#pragma unroll
-                    for (int j = 0; j < FN32; ++j) mma32_fp8(fa32[i], fb32[j], acc[i][j]);
-                    if (refill) fa32[i] = frag_a32(next_ks, i);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            };
-            int ks = 0;
-            for (; ks + NS - 1 < nk; ++ks) {
-                wait_vmcnt<(NS - 3) * DPW>();
-                barrier_nofence();
-                issue(ks + NS - 1);
-                mma_refill(ks + 1, true);
-                if (F > 0) {
-#pragma unroll
-                    for (int j = 0; j < FN32; ++j) fb32[j] = frag_b32(ks + 1, j);
-                }
+        for (int i = 0; i < DPW_H; ++i) {
+            const int b = wave + NW * i;
+            if (b < FM) {  // activation rows b*16 .. b*16+15, swizzled as in the full tile
+                int64_t r = row0 + b * 16 + (lane >> 2);
+                if (r >= row_end) r = row0;
+                int64_t src_row = r;
+                if (EPI == EPI_GATE_UP)
+                    src_row = min(max((int64_t)(p.sorted_assign[r] / p.topk), (int64_t)0), p.a_rows - 1);
+                hsrc[i] = p.A + src_row * K + (((lane & 3) ^ ((lane >> 4) & 3)) * 16);
+                hstride[i] = 64;
+            } else {
+                const int nb = nt * NBB + (b - FM);
+                hsrc[i] = p.B + (int64_t)g * p.b_group_bytes + (int64_t)nb * KB * 1024 + lane * 16;
+                hstride[i] = 1024;
             }
-            for (; ks + 1 < nk; ++ks) {
-                wait_vmcnt<0>();
-                barrier_nofence();
-                mma_refill(ks + 1, true);
-                if (F > 0) {
+        }
+        auto issue_h = [&](int ks) {
+            const LDS_AS int8_t* stage = lds + (ks % NS_H) * STAGE_H;
 #pragma unroll
-                    for (int j = 0; j < FN32; ++j) fb32[j] = frag_b32(ks + 1, j);
-                }
-            }
-            mma_refill(0, false);
-            epilogue32(acc);
+            for (int i = 0; i < DPW_H; ++i)
+                dma16(hsrc[i] + (int64_t)ks * hstride[i], stage + (wave + NW * i) * 1024);
         };
-        if (fm_active > FM / 2) run32(std::integral_constant<int, FM32>{});
-        else if (fm_active > 0) run32(std::integral_constant<int, FM32 / 2>{});
-        else run32(std::integral_constant<int, 0>{});
-    } else {
-        // A half tile: only its first FM*16 rows are copied, so a stage holds
-        // FM A blocks instead of BM/16 and the same LDS ring takes more stages
-        // (5 instead of 4 for 256x256 tiles: four in flight instead of three).
-        // A segment's last tile streams the whole weight tile for few rows,
-        // which makes it bound by the copy pipeline's latency; the deeper
-        // ring and all eight waves at work (each on FN/WM fragment columns of
-        // those rows) shorten it.
-        auto run_half = [&](auto f_tag) {
-            constexpr int F = decltype(f_tag)::value;
-            constexpr int NF = FN / WM;
-            constexpr int NBLK_H = FM + NBB;
-            static_assert(NBLK_H % NW == 0, "half-tile blocks must split evenly over the waves");
-            constexpr int DPW_H = NBLK_H / NW;
-            constexpr int STAGE_H = NBLK_H * 1024;
-            constexpr int NS_H = (NS * STAGE) / STAGE_H < 8 ? (NS * STAGE) / STAGE_H : 8;
-            static_assert(NS_H >= NS && NS_H * STAGE_H <= NS * STAGE, "the half-tile ring fits the ring");
-            const int8_t* hsrc[DPW_H];
-            int hstride[DPW_H];
-#pragma unroll
-            for (int i = 0; i < DPW_H; ++i) {
-                const int b = wave + NW * i;
-                if (b < FM) {  // activation rows b*16 .. b*16+15, swizzled as in the full tile
-                    int64_t r = row0 + b * 16 + (lane >> 2);
-                    if (r >= row_end) r = row0;
-                    int64_t src_row = r;
-                    if (EPI == EPI_GATE_UP)
-                        src_row = min(max((int64_t)(p.sorted_assign[r] / p.topk), (int64_t)0), p.a_rows - 1);
-                    hsrc[i] = p.A + src_row * K + (((lane & 3) ^ ((lane >> 4) & 3)) * 16);
-                    hstride[i] = 64;
-                } else {
-                    const int nb = nt * NBB + (b - FM);
-                    hsrc[i] = p.B + (int64_t)g * p.b_group_bytes + (int64_t)nb * KB * 1024 + lane * 16;
-                    hstride[i] = 1024;
-                }
-            }
-            auto issue_h = [&](int ks) {
-                const LDS_AS int8_t* stage = lds + (ks % NS_H) * STAGE_H;
-#pragma unroll
-                for (int i = 0; i < DPW_H; ++i)
-                    dma16(hsrc[i] + (int64_t)ks * hstride[i], stage + (wave + NW * i) * 1024);
-            };
+        if constexpr (!M32) {
             auto frag_a_h = [&](int ks, int i) {
                 return *reinterpret_cast<const LDS_AS v4i*>(lds + (ks % NS_H) * STAGE_H + i * 1024 + a_slot * 16);
             };
@@ -612,16 +568,132 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
             }
             mma_refill(0, false);
             epilogue(acc, std::integral_constant<int, NF>{});
-        };
-        bool done = false;
-        if constexpr (HALF_OK) {
-            if (half) {
-                if (fm_active > FM / 2) run_half(std::integral_constant<int, FM>{});
-                else run_half(std::integral_constant<int, FM / 2>{});
-                done = true;
+        } else {
+            // FP8: 32x32x64 blocks, each wave on all FM*16 rows (F blocks of 32)
+            // and NF/2 blocks of 32 columns, fragments read as in the full tile
+            constexpr int NJ = NF / 2 > 0 ? NF / 2 : 1;  // (NF is even wherever this runs)
+            auto frag_a32_h = [&](int ks, int i) {
+                const int blk = 2 * i + ((lane >> 4) & 1);
+                const int rr = lane & 15, hh = lane >> 5;
+                const LDS_AS int8_t* base = lds + (ks % NS_H) * STAGE_H + blk * 1024;
+                v8i t;
+                t.lo = *reinterpret_cast<const LDS_AS v4i*>(base + (4 * rr + ((2 * hh) ^ (rr >> 2))) * 16);
+                t.hi = *reinterpret_cast<const LDS_AS v4i*>(base + (4 * rr + ((2 * hh + 1) ^ (rr >> 2))) * 16);
+                return t;
+            };
+            auto frag_b32_h = [&](int ks, int j) {
+                const int blk = FM + b_base + 2 * j + ((lane >> 4) & 1);
+                const int cc = lane & 15, hh = lane >> 5;
+                const LDS_AS int8_t* base = lds + (ks % NS_H) * STAGE_H + blk * 1024;
+                v8i t;
+                t.lo = *reinterpret_cast<const LDS_AS v4i*>(base + (cc + 32 * hh) * 16);
+                t.hi = *reinterpret_cast<const LDS_AS v4i*>(base + (cc + 32 * hh + 16) * 16);
+                return t;
+            };
+#pragma unroll
+            for (int s = 0; s < NS_H - 1; ++s)
+                if (s < nk) issue_h(s);
+            if (nk - 1 >= NS_H - 2) wait_vmcnt<(NS_H - 2) * DPW_H>();
+            else wait_vmcnt<0>();
+            barrier_nofence();
+#pragma unroll
+            for (int i = 0; i < F; ++i) fa32[i] = frag_a32_h(0, i);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) fb32[j] = frag_b32_h(0, j);
+            v4f acc[M32 ? FM32 : 1][NJ][4];
+#pragma unroll
+            for (int i = 0; i < FM32; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[i][j][c] = v4f{0.f, 0.f, 0.f, 0.f};
+            auto mma_refill = [&](int next_ks, bool refill) {
+#pragma unroll
+                for (int i = 0; i < F; ++i) {
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) mma32_fp8(fa32[i], fb32[j], acc[i][j]);
+                    if (refill) fa32[i] = frag_a32_h(next_ks, i);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+            int ks = 0;
+            for (; ks + NS_H - 1 < nk; ++ks) {
+                wait_vmcnt<(NS_H - 3) * DPW_H>();
+                barrier_nofence();
+                issue_h(ks + NS_H - 1);
+                mma_refill(ks + 1, true);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) fb32[j] = frag_b32_h(ks + 1, j);
             }
+            for (; ks + 1 < nk; ++ks) {
+                wait_vmcnt<0>();
+                barrier_nofence();
+                mma_refill(ks + 1, true);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) fb32[j] = frag_b32_h(ks + 1, j);
+            }
+            mma_refill(0, false);
+            epilogue32(acc, std::integral_constant<int, NJ>{});
         }
-        if (!done) {
+    };
+    bool done = false;
+    if constexpr (HALF_OK) {
+        if (half) {
+            if (fm_active > FM / 2) run_half(std::integral_constant<int, M32 ? FM32 : FM>{});
+            else run_half(std::integral_constant<int, M32 ? FM32 / 2 : FM / 2>{});
+            done = true;
+        }
+    }
+    if (!done) {
+        if constexpr (M32) {
+            // FP8: stage ks's MFMAs run from registers while stage ks+1's fragments
+            // come in (each A fragment row right after its MFMAs, B after the
+            // stage's MFMAs), as in the INT8 loop.  F = 32-row fragment rows computed.
+            auto run32 = [&](auto f_tag) {
+                constexpr int F = decltype(f_tag)::value;
+                v4f acc[M32 ? FM32 : 1][M32 ? FN32 : 1][4];
+#pragma unroll
+                for (int i = 0; i < FM32; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN32; ++j)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) acc[i][j][c] = v4f{0.f, 0.f, 0.f, 0.f};
+                auto mma_refill = [&](int next_ks, bool refill) {
+#pragma unroll
+                    for (int i = 0; i < F; ++i) {
+#pragma unroll
+                        for (int j = 0; j < FN32; ++j) mma32_fp8(fa32[i], fb32[j], acc[i][j]);
+                        if (refill) fa32[i] = frag_a32(next_ks, i);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                };
+                int ks = 0;
+                for (; ks + NS - 1 < nk; ++ks) {
+                    wait_vmcnt<(NS - 3) * DPW>();
+                    barrier_nofence();
+                    issue(ks + NS - 1);
+                    mma_refill(ks + 1, true);
+                    if (F > 0) {
+#pragma unroll
+                        for (int j = 0; j < FN32; ++j) fb32[j] = frag_b32(ks + 1, j);
+                    }
+                }
+                for (; ks + 1 < nk; ++ks) {
+                    wait_vmcnt<0>();
+                    barrier_nofence();
+                    mma_refill(ks + 1, true);
+                    if (F > 0) {
+#pragma unroll
+                        for (int j = 0; j < FN32; ++j) fb32[j] = frag_b32(ks + 1, j);
+                    }
+                }
+                mma_refill(0, false);
+                epilogue32(acc, std::integral_constant<int, FN32>{});
+            };
+            if (fm_active > FM / 2) run32(std::integral_constant<int, FM32>{});
+            else if (fm_active > 0) run32(std::integral_constant<int, FM32 / 2>{});
+            else run32(std::integral_constant<int, 0>{});
+        } else {
             if (fm_active > FM / 2) run(std::integral_constant<int, FM>{});
             else if (fm_active > 0) run(std::integral_constant<int, FM / 2>{});
             else run(std::integral_constant<int, 0>{});
