@@ -27,8 +27,9 @@
 //  * NS-1 stages of copies stay in flight: wait for stage s+1 (explicit
 //    vmcnt), barrier, issue stage s+NS-1, then run stage s's MFMAs from
 //    registers while stage s+1's fragments stream in from LDS;
-//  * a segment's last m-tile with at most 128 rows (INT8) copies only those
-//    rows through a deeper ring and spreads them over all waves.
+//  * a segment's last m-tile with at most 128 rows copies only those rows
+//    through a deeper ring and spreads them over all waves (INT8 and FP8;
+//    for FP8 on 256-wide tiles).
 //
 // Workgroup -> tile order (XCD-aware).  Workgroups are dealt round-robin to the
 // 8 XCDs, so blockIdx % 8 names the XCD; each XCD owns one contiguous range
