@@ -264,7 +264,8 @@ typedef struct {
     size_t h_scale;        /* fp32  [T*k]           sorted order                 */
     size_t o;              /* fp32  [T*k][H]        weighted expert outputs, row
                                                     a = t*k+j                    */
-    size_t internal;       /* scratch of the routing kernels                     */
+    size_t internal;       /* scratch: router split sums, router weight planes
+                              (from 2048 tokens), routing tables, tile queues   */
 } w8a8_moe_workspace_layout;
 
 W8A8_API w8a8_status w8a8_moe_workspace_query(const w8a8_moe_shape* shape, w8a8_moe_workspace_layout* layout);
