@@ -23,6 +23,26 @@
 namespace w8a8 {
 namespace {
 
+// A row's float4 slots i*STRIDE + idx (i < N), times the per-column factor
+// when there is one.  Every load is issued before any value is used: slots
+// past the row's end re-read its last float4 instead of branching around the
+// load (a branch per slot made the compiler wait for each load in turn), and
+// the callers ignore them.
+template <int N, int STRIDE>
+__device__ __forceinline__ void load_row(const float4* __restrict__ xr, const float* col_mul, int nv,
+                                         int idx, float4 (&v)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = xr[min(i * STRIDE + idx, nv - 1)];
+    if (col_mul) {
+        const float4* m = reinterpret_cast<const float4*>(col_mul);
+        float4 f[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) f[i] = m[min(i * STRIDE + idx, nv - 1)];
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = mul4(v[i], f[i]);
+    }
+}
+
 // Vector path: cols % 4 == 0, ld % 4 == 0, x 16-byte aligned.  VPL float4 per
 // lane stay in registers (rows up to VPL*256 elements).
 template <int CODE, int VPL>
@@ -35,18 +55,11 @@ __global__ __launch_bounds__(256) void quant_rows_cached(const float* __restrict
     const float4* xr = reinterpret_cast<const float4*>(x + row * ld);
     const int nv = cols >> 2;
     float4 v[VPL];
+    load_row<VPL, 64>(xr, opt.col_mul, nv, lane, v);
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        const int c = i * 64 + lane;
-        if (c < nv) {
-            v[i] = xr[c];
-            if (opt.col_mul) v[i] = mul4(v[i], reinterpret_cast<const float4*>(opt.col_mul)[c]);
-            amax = fmaxf(amax, amax4(v[i]));
-        } else {
-            v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    }
+    for (int i = 0; i < VPL; ++i)
+        if (i * 64 + lane < nv) amax = fmaxf(amax, amax4(v[i]));
     amax = wave_max(amax);
     const float s = scale_base(amax, opt) / code_range<CODE>();
     const float rs = 1.0f / s;
@@ -73,18 +86,11 @@ __global__ __launch_bounds__(256) void quant_rows_block(const float* __restrict_
     const float4* xr = reinterpret_cast<const float4*>(x + row * ld);
     const int nv = cols >> 2;
     float4 v[VPT];
+    load_row<VPT, 256>(xr, opt.col_mul, nv, tid, v);
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-        const int c = i * 256 + tid;
-        if (c < nv) {
-            v[i] = xr[c];
-            if (opt.col_mul) v[i] = mul4(v[i], reinterpret_cast<const float4*>(opt.col_mul)[c]);
-            amax = fmaxf(amax, amax4(v[i]));
-        } else {
-            v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    }
+    for (int i = 0; i < VPT; ++i)
+        if (i * 256 + tid < nv) amax = fmaxf(amax, amax4(v[i]));
     amax = wave_max(amax);
     if (lane == 0) wmax[wv] = amax;
     __syncthreads();
