@@ -275,9 +275,10 @@ __global__ __launch_bounds__(256) void router_w_planes(const float* __restrict__
 
 // Workgroup: 128 tokens x 32*EB experts, 8 waves = 4 token quarters x 2
 // expert halves; a wave owns 32 tokens x 16*EB experts (2 x EB blocks of
-// v_mfma_f32_16x16x32_bf16), as above.  blockIdx.x is the expert tile (so the
-// workgroups that share an activation tile are dispatched together),
-// blockIdx.y the token tile, blockIdx.z the split of H.  A stage holds the
+// v_mfma_f32_16x16x32_bf16), as above.  blockIdx.x is token tile * expert
+// tiles + expert tile (so the workgroups that share an activation tile are
+// dispatched together; one grid dimension, as the token tiles can exceed the
+// 65535 limit of the others), blockIdx.y the split of H.  A stage holds the
 // activation tile (16 copy blocks of 8 rows, swizzled as above) and the
 // expert tile's 6*EB plane fragments, padded with repeat copies to a whole
 // number of blocks per wave (the repeats land in slots nobody reads).
@@ -303,8 +304,10 @@ __global__ __launch_bounds__(512) void router_planes(const float* __restrict__ x
     __shared__ __attribute__((aligned(1024))) int8_t smem[NS * STAGE];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wt = w >> 1, we = w & 1;
-    const int e_tile = blockIdx.x, m0 = blockIdx.y * 128;
-    const int kbeg = blockIdx.z * ksplit_len;
+    const int etiles = NEB / (2 * EB);
+    const int e_tile = (int)(blockIdx.x % etiles);
+    const int m0 = (int)(blockIdx.x / etiles) * 128;
+    const int kbeg = blockIdx.y * ksplit_len;
     const int nk = ksplit_len / RBK, ks0 = kbeg / RBK;
 
     // copy sources and their per-stage strides
@@ -418,7 +421,7 @@ __global__ __launch_bounds__(512) void router_planes(const float* __restrict__ x
     for (; ks + 1 < nk; ++ks) step(ks + 1, std::true_type{});
     step(0, std::false_type{});
 
-    float* out = partial + (int64_t)blockIdx.z * T * E;
+    float* out = partial + (int64_t)blockIdx.y * T * E;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -428,7 +431,7 @@ __global__ __launch_bounds__(512) void router_planes(const float* __restrict__ x
                 const int t = m0 + wt * 32 + i * 16 + (lane >> 4) * 4 + r;
                 const int e = (e_tile * 2 * EB + we * EB + j) * 16 + (lane & 15);
                 if (t < T && e < E)
-                    out[(int64_t)t * E + e] = (bias && gridDim.z == 1) ? acc[i][j][r] + bias[e] : acc[i][j][r];
+                    out[(int64_t)t * E + e] = (bias && gridDim.y == 1) ? acc[i][j][r] + bias[e] : acc[i][j][r];
             }
 }
 
@@ -644,7 +647,7 @@ hipError_t launch_route(const RouteInputs& in, const RouteBuffers& b, hipStream_
         int8_t* planes = static_cast<int8_t*>(b.wplanes);
         const int64_t n = (int64_t)(H / RBK) * neb * 64;
         router_w_planes<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>(wr, E, H, neb, planes);
-        const dim3 grid(etiles, (T + 127) / 128, S);
+        const dim3 grid((unsigned)(etiles * ((T + 127) / 128)), S);
         if (eb == 1) router_planes<1><<<grid, 512, 0, s>>>(xx, planes, rb, T, H, E, neb, H / S, out);
         else if (eb == 2) router_planes<2><<<grid, 512, 0, s>>>(xx, planes, rb, T, H, E, neb, H / S, out);
         else router_planes<4><<<grid, 512, 0, s>>>(xx, planes, rb, T, H, E, neb, H / S, out);
