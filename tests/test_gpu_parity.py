@@ -349,6 +349,47 @@ def test_moe_router_planes(w8, case):
     check_moe(w8, inp)
 
 
+def test_moe_max_token_count_sampled(w8):
+    """The largest token count the ABI takes with top-1 (T = 9,000,000;
+    T*k <= 2^24): more 128-token router tiles than a grid dimension other
+    than x can hold, and every row index past 2^31 bytes.  The layer is
+    token-independent, so sampled tokens (both sides of the 65535-tile
+    boundary, the last token) are checked against the oracle run on those
+    tokens alone: logits within the fp32 bound, ids exact away from near
+    ties, y within the 1e-3 bar."""
+    T, H, E, k, I = 9_000_000, 128, 4, 1, 128
+    _say(f"moe T={T} H={H} E={E} k={k} I={I} (sampled)")
+    inp = synth.moe_inputs("edge", device="cuda", T=T, H=H, E=E, k=k, I=I, n_outlier=2,
+                           outlier_scale=20.0, bf16_x=False, bias="zero", weights="int8")
+    wts, codes = _weights(w8, inp)
+    lay = w8.moe_workspace_layout(T, H, E, k, I)
+    ws = torch.empty((lay["total_bytes"],), dtype=torch.uint8, device="cuda")
+    y = w8.moe_forward(inp["x"], wts, k, workspace=ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    tok = np.unique(np.concatenate([rng.choice(T, 24, replace=False),
+                                    [0, 65535 * 128 - 1, 65535 * 128, T - 1]]))
+    idx = torch.from_numpy(tok).cuda()
+    views = w8.workspace_views(ws, T, H, E, k, I)
+    g_logits = to_np(views["logits"][idx])
+    g_ids = to_np(views["topk_ids"][idx])
+    g_y = to_np(y[idx])
+    x_s = to_np(inp["x"][idx])
+    wr = to_np(inp["wr"])
+    oc = {n: to_np(v) for n, v in codes.items()}
+    o = oracle.moe_forward(x_s, wr, to_np(inp["b"]), oc["w_gu"], oc["s_gu"], oc["w_d"], oc["s_d"], k)
+    cond = np.abs(x_s).astype(np.float64) @ np.abs(wr).astype(np.float64).T
+    dl = np.abs(g_logits.astype(np.float64) - o["logits"])
+    assert np.all(dl <= 1e-6 + 2.0 ** -24 * 8 * np.sqrt(H) * cond), float(dl.max())
+    flag = near_tie_tokens(o["logits"], g_logits, k)
+    same = np.all(g_ids == o["ids"], axis=1)
+    assert np.all(same | flag)
+    terms = np.abs(o["o"]).reshape(len(tok), k, H).sum(axis=1)
+    sr, mx = sum_rel_metric(g_y[same], o["y"][same], terms[same])
+    assert sr <= Y_TOL and mx <= Y_TOL, (sr, mx)
+    del ws, y, inp
+
+
 def test_moe_router_wide_dynamic_range(w8):
     """Router operands whose values span 2^-20 .. 2^20: column h of x is scaled
     by 2^s_h and column h of the router matrix by 2^-s_h, so every product
