@@ -103,6 +103,21 @@ def test_workspace_layout(T, H, E, k, I):
     assert spans[-1][1] <= lay.internal <= lay.total_bytes
 
 
+@pytest.mark.parametrize("E,etile", [(256, 128), (200, 128), (100, 128), (64, 64), (50, 64), (24, 32)])
+def test_workspace_holds_router_planes_from_2048_tokens(E, etile):
+    # from 2048 tokens the router weights are split into three bf16 planes of
+    # the expert count padded to whole expert tiles: H * E' * 6 bytes more
+    # internal scratch than the per-token growth alone accounts for
+    H, k, I = 512, 2, 128
+    _, a = _query(2047, H, E, k, I)
+    _, b = _query(2048, H, E, k, I)
+    _, c = _query(2049, H, E, k, I)
+    planes = H * (-(-E // etile) * etile) * 6
+    per_token = (c.total_bytes - c.internal) - (b.total_bytes - b.internal)
+    assert (b.total_bytes - b.internal) - (a.total_bytes - a.internal) >= planes
+    assert per_token < planes
+
+
 @pytest.mark.parametrize("T,H,E,k,I,status", [
     (16, 100, 8, 2, 256, 2),      # H not a multiple of 128
     (16, 128, 8, 2, 200, 2),      # I not a multiple of 128
