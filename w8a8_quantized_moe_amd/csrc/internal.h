@@ -49,14 +49,18 @@ __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" :::
 // Issued through inline asm so that the compiler does not model the LDS write:
 // it would otherwise drain the whole copy pipeline (vmcnt(0)) before every
 // LDS read it cannot prove disjoint.  The ring's hazards are handled by hand
-// (explicit vmcnt waits before the workgroup barrier).  Nothing else in the
-// kernel uses M0 (no LDS DMA builtins, no dynamic register indexing).
+// (explicit vmcnt waits before the workgroup barrier).  M0 is reserved by
+// the compiler, so it is not named as clobbered (a reserved register in a
+// clobber list is not preserved anyway); this is safe because nothing else in
+// these kernels uses M0 (no LDS DMA builtins, no dynamic register indexing,
+// no messages), which the generated code confirms: its only M0 writes are
+// these.
 __device__ __forceinline__ void dma16(const int8_t* gsrc, const LDS_AS int8_t* lds_wave_base) {
     const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                  :
                  : "v"(gsrc), "s"(lds)
-                 : "memory", "m0");
+                 : "memory");
 }
 __device__ __forceinline__ void dma16(const int8_t* gsrc, const int8_t* lds_wave_base) {
     dma16(gsrc, (const LDS_AS int8_t*)lds_wave_base);

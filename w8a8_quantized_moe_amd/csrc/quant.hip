@@ -80,6 +80,7 @@ template <int CODE, int VPT>
 __global__ __launch_bounds__(256) void quant_rows_block(const float* __restrict__ x, int64_t rows,
                                                         int cols, int64_t ld, int8_t* __restrict__ q,
                                                         float* __restrict__ scale, QuantOpts opt) {
+    (void)rows;  // the grid holds exactly one workgroup per row
     __shared__ float wmax[4];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t row = blockIdx.x;
