@@ -130,13 +130,30 @@ class _Decoded:
         return self.cache[e]
 
 
-def check_moe_fp8(w8, inp, tokens=None):
+_MODES = {"dynamic": 0, "clipped": 1, "static": 2}
+
+
+def check_moe_fp8(w8, inp, tokens=None, qopts=None):
+    """qopts: the x quantisation options by their oracle names (x_smooth as a
+    numpy vector, x_scale_mode, x_clip); the gate-up weights then take
+    1/x_smooth on their input channels on both sides."""
     T, H, E, k, I = inp["T"], inp["H"], inp["E"], inp["k"], inp["I"]
+    qopts = qopts or {}
+    sm = qopts.get("x_smooth")
     if "w_gu_f32" in inp:
+        kw = {}
+        if qopts:
+            kw = dict(x_smooth=None if sm is None else torch.from_numpy(sm).cuda(),
+                      x_scale_mode=_MODES[qopts.get("x_scale_mode", "dynamic")],
+                      x_clip=qopts.get("x_clip", 0.0))
         wts, codes = w8.MoEWeights.from_fp32(inp["wr"], inp["b"], inp["w_gu_f32"], inp["w_d_f32"],
-                                             keep_codes=True, code=w8.CODE_FP8)
+                                             keep_codes=True, code=w8.CODE_FP8, **kw)
         twoI = 2 * I
-        qg, sg = oracle.quantize_rows_fp8(to_np(inp["w_gu_f32"]).reshape(E * twoI, H))
+        if sm is None:
+            qg, sg = oracle.quantize_rows_fp8(to_np(inp["w_gu_f32"]).reshape(E * twoI, H))
+        else:
+            qg, sg = oracle.quantize_rows_ex(to_np(inp["w_gu_f32"]).reshape(E * twoI, H),
+                                             col_mul=np.float32(1.0) / sm, code="fp8")
         qd, sd = oracle.quantize_rows_fp8(to_np(inp["w_d_f32"]).reshape(E * H, I))
         # offline weight quantisation: exact
         assert np.array_equal(_codes(codes["w_gu"]).reshape(-1, H), qg)
@@ -146,6 +163,7 @@ def check_moe_fp8(w8, inp, tokens=None):
         oc = dict(w_gu=qg.reshape(E, twoI, H), s_gu=sg.reshape(E, twoI), w_d=qd.reshape(E, H, I),
                   s_d=sd.reshape(E, H))
     else:
+        assert not qopts
         wts = w8.MoEWeights.from_int8(inp["wr"], inp["b"], inp["w_gu"], inp["s_gu"], inp["w_d"],
                                       inp["s_d"])
         oc = {n: to_np(inp[n]) for n in ("w_gu", "s_gu", "w_d", "s_d")}
@@ -159,7 +177,7 @@ def check_moe_fp8(w8, inp, tokens=None):
     y = to_np(y)
     x = to_np(inp["x"])
     o = oracle.moe_forward(x, to_np(inp["wr"]), to_np(inp["b"]), oc["w_gu"], oc["s_gu"], oc["w_d"],
-                           oc["s_d"], k, tokens=tokens, want_h=True, want_acc=True, code="fp8")
+                           oc["s_d"], k, tokens=tokens, want_h=True, want_acc=True, code="fp8", **qopts)
     tok = o["tokens"]
     # 1. activation codes and scales: exact
     assert np.array_equal(g["x_q"].view(np.uint8), o["x_q"])
@@ -311,3 +329,19 @@ def test_fp8_moe_ragged_narrow_hidden(w8):
     inp = synth.moe_inputs("edge", device="cuda", T=713, H=384, E=5, k=3, I=384, n_outlier=2,
                            outlier_scale=20.0, bf16_x=False, bias="zero", weights="fp32")
     check_moe_fp8(w8, inp)
+
+
+@pytest.mark.parametrize("mode", ["clipped", "static"])
+def test_fp8_moe_with_scale_options(w8, mode):
+    """E4M3 codes with a smoothing vector on x (the gate-up weights quantised
+    with its inverse) and a clipped or static x scale: x codes and scales
+    exact, the rest within the FP8 bounds above."""
+    inp = synth.moe_inputs("edge", device="cuda", T=300, H=256, E=8, k=2, I=256, n_outlier=2,
+                           outlier_scale=20.0, bf16_x=False, bias="zero", weights="fp32")
+    x = to_np(inp["x"])
+    H = inp["H"]
+    m = (1.0 / np.sqrt(np.abs(x).max(axis=0) + 1e-3)).astype(np.float32)
+    m *= np.random.default_rng(H).uniform(0.9, 1.1, H).astype(np.float32)
+    amax = np.abs(x * m).max(axis=1)
+    check_moe_fp8(w8, inp, qopts=dict(x_smooth=m, x_scale_mode=mode,
+                                      x_clip=float(np.quantile(amax, 0.5))))
