@@ -30,7 +30,9 @@ def _weights(w8, inp):
                   bias="zero", weights="int8")),                        # tiled persistent GEMMs
     ("edge", dict(T=300, H=256, E=8, k=2, I=256, n_outlier=2, outlier_scale=20.0, bf16_x=False,
                   bias="zero", weights="fp8")),                         # the same with E4M3 codes
-], ids=["decode", "tiled", "tiled-fp8"])
+    ("edge", dict(T=2100, H=512, E=100, k=4, I=256, n_outlier=2, outlier_scale=20.0, bf16_x=False,
+                  bias="zero", weights="int8")),                        # router weights split into planes
+], ids=["decode", "tiled", "tiled-fp8", "router-planes"])
 def test_moe_forward_graph_replays_match_eager(w8, workload, over):
     print(f"graph capture: {workload} {over}", flush=True)
     inp = synth.moe_inputs(workload, device="cuda", **over)
