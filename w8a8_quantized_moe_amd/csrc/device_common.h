@@ -38,37 +38,51 @@ __device__ __forceinline__ void write_mt_info(MtInfo* info, int e, int first, in
     for (int q = 0; q < n; ++q) info[first + q] = v;
 }
 
-// k rounds of a wave-wide arg-max over one token's logits (lane l holds
-// experts l, l+64, l+128, l+192 in v[0..3], -inf past E); ties go to the lower
-// expert index.  Lane 0 writes the picks in descending order to ids/vals.
-__device__ __forceinline__ void wave_topk(const float (&vin)[4], int lane, int E, int k, int* ids,
-                                          float* vals) {
-    float v0 = vin[0], v1 = vin[1], v2 = vin[2], v3 = vin[3];
+// k rounds of a wave-wide arg-max over the logits of N tokens of one wave
+// (token u's lane l holds experts l, l+64, l+128, l+192 in v[u][0..3], -inf
+// past E); ties go to the lower expert index.  Lane 0 writes the picks in
+// descending order to ids/vals.  The rounds of the N tokens run in lockstep,
+// so their shuffle chains overlap instead of following one another.
+// Token u writes to ids/vals + u * ustride, and only if u < n_valid.
+template <int N>
+__device__ __forceinline__ void wave_topk_n(float (&v)[N][4], int lane, int E, int k, int n_valid,
+                                            int* ids, float* vals, int ustride) {
 #pragma unroll 1
     for (int j = 0; j < k; ++j) {
-        float bv = v0;
-        int bi = lane;
-        if (v1 > bv) { bv = v1; bi = lane + 64; }
-        if (v2 > bv) { bv = v2; bi = lane + 128; }
-        if (v3 > bv) { bv = v3; bi = lane + 192; }
-        if (bi >= E) bi = 0x7fffffff;  // padding never wins a tie
+        float bv[N];
+        int bi[N];
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            bv[u] = v[u][0];
+            bi[u] = lane;
+            if (v[u][1] > bv[u]) { bv[u] = v[u][1]; bi[u] = lane + 64; }
+            if (v[u][2] > bv[u]) { bv[u] = v[u][2]; bi[u] = lane + 128; }
+            if (v[u][3] > bv[u]) { bv[u] = v[u][3]; bi[u] = lane + 192; }
+            if (bi[u] >= E) bi[u] = 0x7fffffff;  // padding never wins a tie
+        }
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) {
-            const float ov = __shfl_xor(bv, o, 64);
-            const int oi = __shfl_xor(bi, o, 64);
-            if (ov > bv || (ov == bv && oi < bi)) {
-                bv = ov;
-                bi = oi;
+#pragma unroll
+            for (int u = 0; u < N; ++u) {
+                const float ov = __shfl_xor(bv[u], o, 64);
+                const int oi = __shfl_xor(bi[u], o, 64);
+                if (ov > bv[u] || (ov == bv[u] && oi < bi[u])) {
+                    bv[u] = ov;
+                    bi[u] = oi;
+                }
             }
         }
-        if (lane == 0) {
-            ids[j] = bi;
-            vals[j] = bv;
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            if (lane == 0 && u < n_valid) {
+                ids[u * ustride + j] = bi[u];
+                vals[u * ustride + j] = bv[u];
+            }
+            if (bi[u] == lane) v[u][0] = -INFINITY;
+            if (bi[u] == lane + 64) v[u][1] = -INFINITY;
+            if (bi[u] == lane + 128) v[u][2] = -INFINITY;
+            if (bi[u] == lane + 192) v[u][3] = -INFINITY;
         }
-        if (bi == lane) v0 = -INFINITY;
-        if (bi == lane + 64) v1 = -INFINITY;
-        if (bi == lane + 128) v2 = -INFINITY;
-        if (bi == lane + 192) v3 = -INFINITY;
     }
 }
 

@@ -497,12 +497,9 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_count(
             vall[u][i] = (e < E) ? lrow[min(e, E - 1)] : -INFINITY;
         }
     }
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-        const int tl = w + NWAVE * u;
-        if (tl >= nt) break;
-        wave_topk(vall[u], lane, E, k, ids_s + tl * k, val_s + tl * k);
-    }
+    // the wave's tokens are w + NWAVE*u: u < n_valid of them exist
+    const int n_valid = w < nt ? (nt - 1 - w) / NWAVE + 1 : 0;
+    wave_topk_n<TPW>(vall, lane, E, k, n_valid, ids_s + w * k, val_s + w * k, NWAVE * k);
     __syncthreads();
     for (int tl = tid; tl < nt; tl += TOPK_THREADS) {
         const int t = t0 + tl;
@@ -524,9 +521,12 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_count(
     } else {
         // single chunk: counts -> offsets -> m-tile prefixes -> sorted list
         const int cnt = tid < E ? __popcll(mask[tid]) : 0;
-        int tot0, tot1;
-        const int off = block_exclusive_scan<NWAVE>(cnt, &tot0, scan_lds);
-        const int m1 = block_exclusive_scan<NWAVE>((cnt + bm - 1) / bm, &tot1, scan_lds);
+        // one scan for both prefixes: rows in the low 16 bits, m-tiles in the
+        // high 16 (a single chunk holds at most 64*8 rows)
+        int tot;
+        const int both = block_exclusive_scan<NWAVE>(cnt | (((cnt + bm - 1) / bm) << 16), &tot, scan_lds);
+        const int off = both & 0xffff, m1 = both >> 16;
+        const int tot0 = tot & 0xffff, tot1 = tot >> 16;
         if (tid < E) {
             expert_counts[tid] = cnt;
             offsets[tid] = off;
