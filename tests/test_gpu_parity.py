@@ -349,15 +349,16 @@ def test_moe_router_planes(w8, case):
     check_moe(w8, inp)
 
 
-def test_moe_max_token_count_sampled(w8):
-    """The largest token count the ABI takes with top-1 (T = 9,000,000;
-    T*k <= 2^24): more 128-token router tiles than a grid dimension other
-    than x can hold, and every row index past 2^31 bytes.  The layer is
-    token-independent, so sampled tokens (both sides of the 65535-tile
-    boundary, the last token) are checked against the oracle run on those
-    tokens alone: logits within the fp32 bound, ids exact away from near
-    ties, y within the 1e-3 bar."""
-    T, H, E, k, I = 9_000_000, 128, 4, 1, 128
+@pytest.mark.parametrize("T,E,k", [(9_000_000, 4, 1), (1 << 21, 8, 8)], ids=["T9M-top1", "A2^24-top8"])
+def test_moe_max_token_count_sampled(w8, T, E, k):
+    """Token counts at the ABI's limits: T = 9,000,000 with top-1 (more
+    128-token router tiles than a grid dimension other than x can hold) and
+    T*k = 2^24 assignments exactly (top-8 of 8 experts: segments of 2^21
+    rows).  Row offsets run past 2^31 bytes.  The layer is token-independent,
+    so sampled tokens (both sides of the 65535-tile boundary, the last token)
+    are checked against the oracle run on those tokens alone: logits within
+    the fp32 bound, ids exact away from near ties, y within the 1e-3 bar."""
+    H, I = 128, 128
     _say(f"moe T={T} H={H} E={E} k={k} I={I} (sampled)")
     inp = synth.moe_inputs("edge", device="cuda", T=T, H=H, E=E, k=k, I=I, n_outlier=2,
                            outlier_scale=20.0, bf16_x=False, bias="zero", weights="int8")
@@ -367,8 +368,8 @@ def test_moe_max_token_count_sampled(w8):
     y = w8.moe_forward(inp["x"], wts, k, workspace=ws)
     torch.cuda.synchronize()
     rng = np.random.default_rng(5)
-    tok = np.unique(np.concatenate([rng.choice(T, 24, replace=False),
-                                    [0, 65535 * 128 - 1, 65535 * 128, T - 1]]))
+    edges = [0, T - 1] + ([65535 * 128 - 1, 65535 * 128] if T > 65535 * 128 else [])
+    tok = np.unique(np.concatenate([rng.choice(T, 24, replace=False), edges]))
     idx = torch.from_numpy(tok).cuda()
     views = w8.workspace_views(ws, T, H, E, k, I)
     g_logits = to_np(views["logits"][idx])
