@@ -289,9 +289,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
                 else if (EPI == EPI_DOWN) dst = (int64_t)row_slot[row] * N + col0 + c4;
                 else dst = grow * N + col0 + c4;
                 if (EPI == EPI_DENSE_I32) *reinterpret_cast<v4i*>(p.out_i32 + dst) = v;
-                // o is read back only by the combine, long after: stream it past
-                // the caches instead of evicting the tiles' operands
-                else if (EPI == EPI_DOWN) __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(p.out_f32 + dst));
+                // h and o are read back once, by the next pass, from HBM (they
+                // exceed the caches): stream them past the caches instead of
+                // evicting the tiles' operands
+                else if (EPI == EPI_DOWN || EPI == EPI_GATE_UP)
+                    __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(p.out_f32 + dst));
                 else *reinterpret_cast<v4i*>(p.out_f32 + dst) = v;
             }
         }
