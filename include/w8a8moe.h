@@ -120,15 +120,19 @@ W8A8_API w8a8_status w8a8_quantize_rows_fp8(const float* x, int64_t rows, int64_
  *   W8A8_SCALE_STATIC   s[r] = clip / Q
  * and the codes of x'/s as in w8a8_quantize_rows / _fp8, saturating where
  * |x'/s| exceeds the range (INT8: clamp to [-128, 127]; E4M3: +-448).  The
- * factor and the bound come from calibration (not done here).  For the
- * weights of a smoothed layer the caller quantises the weight rows with
- * col_mul = 1 / factor (the inverse on each input channel), which leaves the
- * product unchanged. */
-enum { W8A8_SCALE_DYNAMIC = 0, W8A8_SCALE_CLIPPED = 1, W8A8_SCALE_STATIC = 2 };
+ * factor and the bound come from calibration (not done here).  The weights
+ * of a smoothed layer take the inverse factor on each input channel, which
+ * leaves the product unchanged: quantise their rows with col_mul = the factor
+ * and W8A8_SCALE_COL_RECIPROCAL or'ed into scale_mode, so that
+ * x'[r][c] = x[r][c] * (1 / col_mul[c]), the reciprocal one IEEE fp32
+ * division (round to nearest even) and the product one fp32 multiply. */
+enum { W8A8_SCALE_DYNAMIC = 0, W8A8_SCALE_CLIPPED = 1, W8A8_SCALE_STATIC = 2,
+       W8A8_SCALE_COL_RECIPROCAL = 0x10 };
 
 /* Per-row quantisation with the options above.  col_mul: NULL or [cols]
  * fp32 device array (4-byte aligned; 16-byte alignment takes the vector
- * path); scale_mode: a W8A8_SCALE_* value; clip: positive and finite for the
+ * path); scale_mode: a W8A8_SCALE_* mode, optionally or'ed with
+ * W8A8_SCALE_COL_RECIPROCAL (needs col_mul); clip: positive and finite for the
  * clipped and static modes, ignored for the dynamic one; code:
  * W8A8_CODE_INT8 (q is int8) or W8A8_CODE_FP8_E4M3 (q is uint8 E4M3).  Other
  * arguments, limits and errors as for w8a8_quantize_rows;
@@ -290,6 +294,26 @@ W8A8_API w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape,
                                              const w8a8_moe_weights* weights, const float* x,
                                              float* y, void* workspace, size_t workspace_bytes,
                                              void* const* events, w8a8_stream stream);
+
+/* -------------------------------------------------------------------------
+ * The grouped gate-up GEMM's raw int32 accumulators, for checking ([K100AI]
+ * sec. 2.1: int8 x int8 products summed in int32; [HUNYUAN] sec. 1.3: each
+ * expert's rows read through the routing index).  Runs the layer's gate-up
+ * GEMM again with an epilogue that stores the accumulators instead of
+ * finishing them, over the routing tables a previous w8a8_moe_forward call
+ * (same shape, weights and workspace, INT8 code) left in the workspace; the
+ * workspace is only read.  Enqueue it after that call on the same stream.
+ *   acc: device int32 [T*k][2I], 4-byte aligned, written in full; row r is
+ *        the r-th row of the expert-sorted order (sorted_assign[r] names its
+ *        assignment t*k+j); column c < I holds gate channel c, column I + c
+ *        up channel c: acc[r][c] = sum_h x_q[t][h] * W_gate_up[e][c][h] with
+ *        W_gate_up the unpacked [E][2I][H] codes.
+ * Errors: as w8a8_moe_forward; W8A8_ERR_INVALID_ARGUMENT for E4M3 weights
+ * (their accumulators are fp32) and a NULL acc.
+ * ------------------------------------------------------------------------- */
+W8A8_API w8a8_status w8a8_moe_gate_up_acc(const w8a8_moe_shape* shape, const w8a8_moe_weights* weights,
+                                          const void* workspace, size_t workspace_bytes, int32_t* acc,
+                                          w8a8_stream stream);
 
 #ifdef __cplusplus
 }

@@ -46,7 +46,7 @@ def exported_symbols():
 
 def test_header_parses():
     fns = header_functions()
-    assert len(fns) == 14, sorted(fns)
+    assert len(fns) == 15, sorted(fns)
 
 
 def test_every_declared_function_is_exported():
@@ -176,6 +176,16 @@ def test_forward_checks_workspace_and_alignment():
     st = lib.w8a8_moe_forward(sh, ctypes.byref(bad), base, base + 65536, base + 2 * 65536, 1 << 30,
                               None)
     assert st == 1 and "code" in lib.w8a8_last_error().decode()  # unknown weight code
+    # the gate-up accumulator capture: INT8 codes only, a non-NULL output, a
+    # large enough aligned workspace
+    acc = lib.w8a8_moe_gate_up_acc
+    fp8 = _lib.MoeWeights(base, None, base, base, base, base, 1)
+    assert acc(sh, ctypes.byref(w), base + 2 * 65536, 1 << 30, None, None) == 1
+    assert acc(sh, ctypes.byref(fp8), base + 2 * 65536, 1 << 30, base, None) == 1
+    assert acc(sh, ctypes.byref(w), base + 2 * 65536, 16, base, None) == 3
+    assert acc(sh, ctypes.byref(w), base + 2 * 65536 + 16, 1 << 30, base, None) == 4
+    assert acc(sh, ctypes.byref(w), base + 2 * 65536, 1 << 30, base + 2, None) == 4
+    assert acc(ctypes.byref(_shape(0, 128, 8, 2, 256)), None, None, 0, None, None) == 0
 
 
 def test_gemm_and_quant_argument_checks():
@@ -199,6 +209,10 @@ def test_gemm_and_quant_argument_checks():
     assert lib.w8a8_quantize_rows_ex(base, 4, 16, 16, None, 0, 0.0, 5, base, base, None) == 1
     assert lib.w8a8_quantize_rows_ex(base, 4, 16, 16, base + 2, 0, 0.0, 0, base, base, None) == 4
     assert lib.w8a8_quantize_rows_ex(None, 0, 16, 16, None, 1, 2.0, 1, None, None, None) == 0
+    # the reciprocal flag needs a factor, and combines with a valid mode only
+    assert lib.w8a8_quantize_rows_ex(base, 4, 16, 16, None, 0x10, 0.0, 0, base, base, None) == 1
+    assert lib.w8a8_quantize_rows_ex(base, 4, 16, 16, base, 0x13, 1.0, 0, base, base, None) == 1
+    assert lib.w8a8_quantize_rows_ex(None, 0, 16, 16, base, 0x10, 0.0, 0, None, None, None) == 0
 
 
 def test_pack_size():
@@ -222,3 +236,75 @@ def test_binding_shares_one_hip_runtime():
             "print(len(set(re.findall(r'\\S*libamdhip64\\S*', m))))" % ROOT)
     res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True)
     assert res.stdout.strip() == "1", res.stdout + res.stderr
+
+
+# ---------------------------------------------------------------- binding checks
+# The C ABI receives bare pointers, so the binding checks every tensor's dtype,
+# shape (or byte count) and device before any call: these run on the host,
+# with host tensors, and must raise before anything reaches the library.
+import torch  # noqa: E402
+
+from w8a8_quantized_moe_amd import api  # noqa: E402
+
+
+def _raises(fn, match):
+    with pytest.raises(ValueError, match=match):
+        fn()
+
+
+def test_binding_rejects_bad_gemm_arguments():
+    M, N, K = 4, 128, 128
+    a = torch.zeros(M, K, dtype=torch.int8)
+    b = torch.zeros(N * K, dtype=torch.int8)
+    sa = torch.zeros(M)
+    sb = torch.zeros(N)
+    _raises(lambda: api.gemm(torch.zeros(M, K + 64, dtype=torch.int8), sa, b, sb, N, K), "a_q must have shape")
+    _raises(lambda: api.gemm(a, sa, torch.zeros(N * K - 16, dtype=torch.int8), sb, N, K), "b_packed must hold")
+    _raises(lambda: api.gemm(a, torch.zeros(M + 1), b, sb, N, K), "s_a must have shape")
+    _raises(lambda: api.gemm(a, sa, b, torch.zeros(N // 2), N, K), "s_b must have shape")
+    _raises(lambda: api.gemm(a, sa, b, sb, N, K, out=torch.zeros(M, N - 1)), "out must have shape")
+    _raises(lambda: api.gemm(a, sa, b, sb, N, K, out=torch.zeros(M, N, dtype=torch.float16)), "out must be")
+    _raises(lambda: api.gemm(a, sa, b, sb, N, K, out=torch.zeros(M, N)), "GPU tensor")
+    _raises(lambda: api.gemm_i32(a, b, N, K, out=torch.zeros(M, N)), "out must be torch.int32")
+    _raises(lambda: api.gemm_i32(a.float(), b, N, K), "a_q must be torch.int8")
+    _raises(lambda: api.gemm_i32(a, b, N, K), "GPU tensor")
+
+
+def test_binding_rejects_bad_quantize_arguments():
+    x = torch.zeros(3, 8)
+    _raises(lambda: api.quantize_rows(x), "GPU tensor")
+    _raises(lambda: api.quantize_rows(x.t()), "unit column stride")
+    _raises(lambda: api.quantize_rows(x.double()), "fp32")
+
+
+def _weights(E=4, H=128, I=128, **over):
+    f = dict(router_w=torch.zeros(E, H), router_b=None, w_gate_up=torch.zeros(E * 2 * I * H, dtype=torch.int8),
+             s_gate_up=torch.zeros(E, 2 * I), w_down=torch.zeros(E * H * I, dtype=torch.int8),
+             s_down=torch.zeros(E, H))
+    f.update(over)
+    return api.MoEWeights(E, H, I, **f)
+
+
+def test_binding_rejects_bad_moe_arguments():
+    T, H = 5, 128
+    x = torch.zeros(T, H)
+    _raises(lambda: api.moe_forward(torch.zeros(T, H + 128), _weights(), 2), "x must have shape")
+    _raises(lambda: api.moe_forward(x, _weights(router_w=torch.zeros(4, 64)), 2), "router_w must have shape")
+    _raises(lambda: api.moe_forward(x, _weights(router_b=torch.zeros(5)), 2), "router_b must have shape")
+    _raises(lambda: api.moe_forward(x, _weights(w_gate_up=torch.zeros(100, dtype=torch.int8)), 2),
+            "w_gate_up must hold")
+    _raises(lambda: api.moe_forward(x, _weights(s_down=torch.zeros(4, 64)), 2), "s_down must have shape")
+    _raises(lambda: api.moe_forward(x, _weights(x_smooth=torch.zeros(64)), 2), "x_smooth must have shape")
+    _raises(lambda: api.moe_forward(x, _weights(), 2), "GPU tensor")
+
+
+def test_binding_rejects_bad_moe_outputs():
+    T, H = 5, 128
+    x = torch.zeros(T, H)
+    w = _weights()
+    _raises(lambda: api.moe_forward(x, w, 2, y=torch.zeros(T, H - 1)), "y must have shape")
+    _raises(lambda: api.moe_forward(x, w, 2, y=torch.zeros(T, H, dtype=torch.float64)), "y must be")
+    _raises(lambda: api.moe_forward(x, w, 2, y=torch.zeros(T, H).t()), "y must have shape")
+    _raises(lambda: api.moe_forward(x, w, 2, workspace=torch.zeros(10)), "workspace must be torch.uint8")
+    _raises(lambda: api.moe_forward(x, w, 2, y=torch.zeros(T, H), workspace=torch.zeros(10, dtype=torch.uint8)),
+            "x must be a GPU tensor")

@@ -149,6 +149,8 @@ def _weights(w8, inp, qopts=None):
 
 
 def _gpu_moe(w8, inp, wts):
+    """The layer on the GPU: every intermediate, and (INT8 codes) a function
+    returning the gate-up GEMM's raw accumulators of given expert-sorted rows."""
     T, H, E, k, I = inp["T"], inp["H"], inp["E"], inp["k"], inp["I"]
     lay = w8.moe_workspace_layout(T, H, E, k, I)
     ws = torch.empty((max(lay["total_bytes"], 256),), dtype=torch.uint8, device="cuda")
@@ -156,6 +158,10 @@ def _gpu_moe(w8, inp, wts):
     torch.cuda.synchronize()
     g = {n: to_np(v) for n, v in w8.workspace_views(ws, T, H, E, k, I).items()}
     g["y"] = to_np(y)
+    if wts.code == w8.CODE_INT8:
+        acc = w8.moe_gate_up_acc(T, wts, k, ws)
+        torch.cuda.synchronize()
+        g["acc_gu_rows"] = lambda rows: to_np(acc[torch.as_tensor(rows, dtype=torch.long, device="cuda")])
     return g
 
 
@@ -191,7 +197,7 @@ def check_moe(w8, inp, tokens=None, report=None, qopts=None):
     x = to_np(inp["x"])
     b = to_np(inp["b"])
     o = oracle.moe_forward(x, to_np(inp["wr"]), b, oc["w_gu"], oc["s_gu"], oc["w_d"], oc["s_d"], k,
-                           tokens=tokens, want_h=True, **(qopts or {}))
+                           tokens=tokens, want_h=True, want_acc=True, **(qopts or {}))
     tok = o["tokens"]
 
     # 1. per-token quantisation: exact
@@ -227,6 +233,11 @@ def check_moe(w8, inp, tokens=None, report=None, qopts=None):
     a_rows = (tok[:, None] * k + np.arange(k)[None, :]).reshape(-1)
     ok_rows = np.repeat(same[tok], k)
     rows_g = inv[a_rows]
+    # 5a. the gate-up GEMM's int32 accumulators: bit-exact on every row routed
+    #     like the oracle's (same expert)
+    acc_g = g["acc_gu_rows"](rows_g)
+    assert np.array_equal(acc_g[ok_rows], o["acc_gu"][ok_rows]), \
+        f"gate-up accumulators differ on {int((acc_g != o['acc_gu'])[ok_rows].any(axis=1).sum())} rows"
     h_g = g["h"][rows_g]
     hq_g = g["h_q"][rows_g]
     sh_g = g["h_scale"][rows_g]
@@ -241,9 +252,21 @@ def check_moe(w8, inp, tokens=None, report=None, qopts=None):
     rest = ok_rows & ~h_exact
     if rest.any():
         assert np.abs(hq_g[rest].astype(int) - o["h_q"][rest].astype(int)).max() <= 1
+    # 6a. the down GEMM: on every row whose h codes equal the oracle's, its int32
+    #     accumulators are the oracle's, so o must equal the epilogue
+    #     w * (((float)acc * s_h) * s_d) evaluated in fp32 on those accumulators
+    #     with the GPU's own routing weight and row scale, bit for bit
+    o_g = g["o"][a_rows]
+    hq_same = np.all(hq_g == o["h_q"], axis=1) & ok_rows
+    ids_a = o["ids"][tok].reshape(-1)
+    f32 = np.float32
+    w_ga = g["topk_w"][tok].reshape(-1).astype(f32)
+    o_acc = (o["acc_d"].astype(f32) * sh_g[:, None].astype(f32)) * oc["s_d"][ids_a].astype(f32)
+    o_acc = w_ga[:, None] * o_acc.astype(f32)
+    assert np.array_equal(o_g[hq_same], o_acc[hq_same]), \
+        f"down epilogue differs on {int((o_g != o_acc)[hq_same].any(axis=1).sum())} of {int(hq_same.sum())} rows"
     # o = w * v with v bit-exact on both sides when h_q is: its error is the routing
     # weight's (bounded above from the logit error) plus the rounding of the product
-    o_g = g["o"][a_rows]
     w_rel_a = w_rel[tok].reshape(-1)
     o_err = np.abs(o_g.astype(np.float64) - o["o"])
     o_tol = (w_rel_a[:, None] + 2.0 ** -22) * np.abs(o["o"]).astype(np.float64)
@@ -438,7 +461,9 @@ def test_moe_deterministic_and_token_independent(w8):
     a = _gpu_moe(w8, inp, wts)
     b = _gpu_moe(w8, inp, wts)
     for n in a:
-        assert np.array_equal(a[n], b[n]), n
+        if not callable(a[n]):
+            assert np.array_equal(a[n], b[n]), n
+    assert np.array_equal(a["acc_gu_rows"](np.arange(128)), b["acc_gu_rows"](np.arange(128)))
     # permuting tokens permutes the outputs exactly (same token count, same kernels)
     perm = torch.randperm(inp["T"], generator=torch.Generator().manual_seed(3))
     inp2 = dict(inp)
@@ -498,6 +523,12 @@ def test_quantize_rows_ex_bitexact(w8, rows, cols, code):
             assert np.array_equal(to_np(s), so), (mode, use_m)
             qg = to_np(q)
             assert np.array_equal(qg.view(qo.dtype), qo), (mode, use_m, int((qg.view(qo.dtype) != qo).sum()))
+    # the inverse factor (a smoothed layer's weights): the library takes 1/m
+    # itself; the oracle is handed the reciprocal as an IEEE fp32 division
+    q, s = w8.quantize_rows(xd, code=c, col_mul=md, col_reciprocal=True)
+    qo, so = oracle.quantize_rows_ex(x, np.float32(1.0) / m, "dynamic", 0.0, code)
+    assert np.array_equal(to_np(s), so)
+    assert np.array_equal(to_np(q).view(qo.dtype), qo)
 
 
 @pytest.mark.parametrize("case", [

@@ -43,6 +43,7 @@ class MoeShape(ctypes.Structure):
 
 
 SCALE_DYNAMIC, SCALE_CLIPPED, SCALE_STATIC = 0, 1, 2
+SCALE_COL_RECIPROCAL = 0x10  # or'ed into the mode: the column factor is applied as 1/col_mul
 
 
 class MoeWeights(ctypes.Structure):
@@ -83,6 +84,8 @@ SIGNATURES = {
                                         _P, ctypes.c_size_t, _P]),
     "w8a8_moe_forward_events": (ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeWeights),
                                                _P, _P, _P, ctypes.c_size_t, _P, _P]),
+    "w8a8_moe_gate_up_acc": (ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeWeights), _P,
+                                            ctypes.c_size_t, _P, _P]),
 }
 
 MOE_STAGES = ["quant", "route", "gate_up", "requant", "down", "combine"]

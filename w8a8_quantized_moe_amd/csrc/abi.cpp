@@ -170,6 +170,10 @@ w8a8_status w8a8_quantize_rows_fp8(const float* x, int64_t rows, int64_t cols, i
 w8a8_status w8a8_quantize_rows_ex(const float* x, int64_t rows, int64_t cols, int64_t ld,
                                   const float* col_mul, int32_t scale_mode, float clip, int32_t code,
                                   void* q, float* scale, w8a8_stream stream) {
+    const bool recip = (scale_mode & W8A8_SCALE_COL_RECIPROCAL) != 0;
+    if (recip && !col_mul)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "W8A8_SCALE_COL_RECIPROCAL needs col_mul");
+    scale_mode &= ~W8A8_SCALE_COL_RECIPROCAL;
     w8a8_status st = check_scale_opts(scale_mode, clip, col_mul);
     if (st != W8A8_OK) return st;
     if (code != W8A8_CODE_INT8 && code != W8A8_CODE_FP8_E4M3)
@@ -178,6 +182,7 @@ w8a8_status w8a8_quantize_rows_ex(const float* x, int64_t rows, int64_t cols, in
     opt.col_mul = col_mul;
     opt.mode = scale_mode;
     opt.clip = clip;
+    opt.col_recip = recip;
     return quantize_rows_code(x, rows, cols, ld, (int8_t*)q, scale,
                               code == W8A8_CODE_FP8_E4M3 ? w8a8::CODE_FP8 : w8a8::CODE_INT8, stream, opt);
 }
@@ -422,6 +427,54 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     st = check_hip(w8a8::launch_combine(o, T, k, H, y, s), "combine");
     if (st != W8A8_OK) return st;
     return mark(6);
+}
+
+w8a8_status w8a8_moe_gate_up_acc(const w8a8_moe_shape* shape, const w8a8_moe_weights* wts,
+                                 const void* workspace, size_t workspace_bytes, int32_t* acc,
+                                 w8a8_stream stream) {
+    w8a8_status st = check_moe_shape(shape);
+    if (st != W8A8_OK) return st;
+    if (shape->T == 0) return W8A8_OK;
+    if (!wts || !workspace || !acc || !wts->w_gate_up)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "NULL pointer");
+    if (wts->code != W8A8_CODE_INT8)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "raw accumulators are int32 for INT8 codes only");
+    if (!aligned(wts->w_gate_up, 16) || !aligned(acc, 4))
+        return fail(W8A8_ERR_MISALIGNED, "w_gate_up must be 16-byte and acc 4-byte aligned");
+    if (!aligned(workspace, 256)) return fail(W8A8_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+    const MoePlan plan = plan_moe(shape);
+    if (workspace_bytes < plan.lay.total_bytes)
+        return fail(W8A8_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < required %zu", workspace_bytes,
+                    plan.lay.total_bytes);
+    const int T = (int)shape->T, H = (int)shape->H, E = (int)shape->E, k = (int)shape->top_k,
+              I = (int)shape->I;
+    const int64_t A = (int64_t)T * k;
+    const int bm = moe_bm(A, E);
+    const char* ws = (const char*)workspace;
+    const w8a8_moe_workspace_layout& L = plan.lay;
+    w8a8::GemmParams gu{};
+    gu.A = (const int8_t*)(ws + L.x_q);
+    gu.B = wts->w_gate_up;
+    gu.b_group_bytes = (int64_t)2 * I * H;
+    gu.M = A;
+    gu.N = 2 * I;
+    gu.K = H;
+    gu.seg_offsets = (const int32_t*)(ws + L.expert_offsets);
+    gu.mt_prefix = (const int32_t*)(ws + plan.mt_prefix);
+    gu.mt_info = (const int32_t*)(ws + plan.mt_info);
+    gu.tile_ctr = nullptr;  // one tile per workgroup (the queues were used by the layer's launch)
+    gu.G = E;
+    gu.sorted_assign = (const int32_t*)(ws + L.sorted_assign);
+    gu.topk = k;
+    gu.out_i32 = acc;
+    gu.I = I;
+    gu.a_rows = T;
+    gu.code = w8a8::CODE_INT8;
+    hipStream_t s = (hipStream_t)stream;
+    return check_hip(bm == w8a8::SKINNY_BM
+                         ? w8a8::launch_gemm_skinny(w8a8::EPI_GU_I32, gu, max_m_tiles(A, E, bm), s)
+                         : w8a8::launch_gemm(w8a8::EPI_GU_I32, gu, max_m_tiles(A, E, bm), s),
+                     "gate-up accumulators");
 }
 
 }  // extern "C"

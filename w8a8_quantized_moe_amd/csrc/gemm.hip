@@ -50,6 +50,8 @@ namespace {
 template <int BM, int BN, int WM, int WN, int NS, int EPI, int CODE>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     typedef typename AccOf<CODE>::type AccT;
+    // the gate-up GEMMs read their activation rows through the routing index
+    constexpr bool GATHER = (EPI == EPI_GATE_UP || EPI == EPI_GU_I32);
     constexpr int NW = WM * WN;                  // waves per workgroup
     constexpr int FM = BM / WM / 16;             // fragment rows per wave
     constexpr int FN = BN / WN / 16;             // fragment cols per wave
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     // blocks span two fragment columns, only where each wave keeps an even
     // number of fragment columns.)
     constexpr bool HALF_OK = FN % WM == 0 &&
-                             ((EPI != EPI_GATE_UP && CODE == CODE_INT8) || (FN / WM) % 2 == 0);
+                             ((!GATHER && CODE == CODE_INT8) || (FN / WM) % 2 == 0);
     const int rows_valid = (int)(row_end - row0);
     const bool half = HALF_OK && rows_valid <= FM * 16;
     // first fragment row / column of this wave
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
             int64_t r = row0 + b * 16 + (lane >> 2);
             if (r >= row_end) r = row0;  // rows past the segment read a valid row; results dropped
             int64_t src_row = r;
-            if (EPI == EPI_GATE_UP)
+            if (GATHER)
                 src_row = min(max((int64_t)(p.sorted_assign[r] / p.topk), (int64_t)0), p.a_rows - 1);
             src[i] = p.A + src_row * K + (((lane & 3) ^ ((lane >> 4) & 3)) * 16);
             stride[i] = 64;
@@ -301,6 +303,25 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     };
     auto epilogue = [&](AccT (&acc)[FM][FN], auto n_tag) {
         constexpr int NF = decltype(n_tag)::value;
+        if constexpr (EPI == EPI_GU_I32) {
+            // raw accumulators straight from registers (a checking path): the
+            // column blocks alternate gate / up for the same 16 channels, as in
+            // the gate-up epilogue
+            const int64_t ch0 = (int64_t)(nt * NBB + b_base) / 2 * 16 + (lane & 15);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                if (i >= fm_active) break;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t grow = row0 + (a_base + i) * 16 + (lane >> 4) * 4 + r;
+                    if (grow >= row_end) continue;
+#pragma unroll
+                    for (int j = 0; j < NF; ++j)
+                        p.out_i32[grow * 2 * p.I + ((j & 1) ? p.I : 0) + ch0 + (j >> 1) * 16] = (int)acc[i][j][r];
+                }
+            }
+            return;
+        }
         constexpr int OCOLS = (EPI == EPI_GATE_UP) ? NF * 8 : NF * 16;  // output columns per wave
         constexpr int SROW = OCOLS + 4;                                 // padded staging stride (words)
         __syncthreads();  // the ring is idle; row metadata written before the loop is visible
@@ -502,7 +523,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
                 int64_t r = row0 + b * 16 + (lane >> 2);
                 if (r >= row_end) r = row0;
                 int64_t src_row = r;
-                if (EPI == EPI_GATE_UP)
+                if (GATHER)
                     src_row = min(max((int64_t)(p.sorted_assign[r] / p.topk), (int64_t)0), p.a_rows - 1);
                 hsrc[i] = p.A + src_row * K + (((lane & 3) ^ ((lane >> 4) & 3)) * 16);
                 hstride[i] = 64;
@@ -769,6 +790,7 @@ hipError_t launch_tile(int epi, const GemmParams& p, int64_t blocks, hipStream_t
         case EPI_DENSE_I32: gemm_i8<BM, BN, WM, WN, NS, EPI_DENSE_I32, CODE_INT8><<<grid, block, 0, s>>>(p); break;
         case EPI_GATE_UP: gemm_i8<BM, BN, WM, WN, NS, EPI_GATE_UP, CODE_INT8><<<grid, block, 0, s>>>(p); break;
         case EPI_DOWN: gemm_i8<BM, BN, WM, WN, NS, EPI_DOWN, CODE_INT8><<<grid, block, 0, s>>>(p); break;
+        case EPI_GU_I32: gemm_i8<BM, BN, WM, WN, NS, EPI_GU_I32, CODE_INT8><<<grid, block, 0, s>>>(p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

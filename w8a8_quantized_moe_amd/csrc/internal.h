@@ -121,6 +121,8 @@ enum Epilogue : int {
     EPI_DENSE_I32 = 1,  // out[m][n] = acc
     EPI_GATE_UP = 2,    // h = SiLU(g) * u from interleaved gate/up columns
     EPI_DOWN = 3,       // o[slot][n] = w[slot] * (((float)acc * s_h[r]) * s_d[e][n])
+    EPI_GU_I32 = 4,     // grouped gate-up, raw int32 accumulators: out[r][c] gate channel c,
+                        // out[r][I + c] up channel c (r: sorted row)
 };
 
 struct GemmParams {
@@ -167,6 +169,8 @@ struct QuantOpts {
     const float* col_mul = nullptr;  // [cols] or nullptr
     int mode = SCALE_DYNAMIC;
     float clip = 0.0f;               // > 0 for the clipped and static modes
+    bool col_recip = false;          // apply 1/col_mul[c] (an IEEE fp32 division) instead:
+                                     // the inverse factor a smoothed layer's weights take
 };
 
 // ---- launchers (each returns the launch status) ----

@@ -10,7 +10,8 @@
 //
 // Options ("W8A8 quantisation of MiniMax-M3 on K100AI", sec. 2.2; "DeepSeek V4
 // '950'", sec. 3.1): a per-column factor (SmoothQuant) multiplies each value
-// in fp32 before the row maximum is taken, and the scale's base is the row
+// in fp32 before the row maximum is taken (or its reciprocal, an IEEE fp32
+// division, for the weights of a smoothed layer), and the scale's base is the row
 // maximum (dynamic), the row maximum capped by a calibrated bound (clipped)
 // or the bound alone (static); codes then saturate (INT8 clamp, E4M3 +-448).
 //
@@ -30,8 +31,8 @@ namespace {
 // the callers ignore them.  The row is read once, so the loads are
 // non-temporal (streamed past the caches: 27% faster on the large layer's x).
 template <int N, int STRIDE>
-__device__ __forceinline__ void load_row(const float4* __restrict__ xr, const float* col_mul, int nv,
-                                         int idx, float4 (&v)[N]) {
+__device__ __forceinline__ void load_row(const float4* __restrict__ xr, const float* col_mul, bool recip,
+                                         int nv, int idx, float4 (&v)[N]) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
         const v4f t = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(xr) + min(i * STRIDE + idx, nv - 1));
@@ -42,6 +43,10 @@ __device__ __forceinline__ void load_row(const float4* __restrict__ xr, const fl
         float4 f[N];
 #pragma unroll
         for (int i = 0; i < N; ++i) f[i] = m[min(i * STRIDE + idx, nv - 1)];
+        if (recip) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) f[i] = make_float4(1.0f / f[i].x, 1.0f / f[i].y, 1.0f / f[i].z, 1.0f / f[i].w);
+        }
 #pragma unroll
         for (int i = 0; i < N; ++i) v[i] = mul4(v[i], f[i]);
     }
@@ -59,7 +64,7 @@ __global__ __launch_bounds__(256) void quant_rows_cached(const float* __restrict
     const float4* xr = reinterpret_cast<const float4*>(x + row * ld);
     const int nv = cols >> 2;
     float4 v[VPL];
-    load_row<VPL, 64>(xr, opt.col_mul, nv, lane, v);
+    load_row<VPL, 64>(xr, opt.col_mul, opt.col_recip, nv, lane, v);
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
@@ -91,7 +96,7 @@ __global__ __launch_bounds__(256) void quant_rows_block(const float* __restrict_
     const float4* xr = reinterpret_cast<const float4*>(x + row * ld);
     const int nv = cols >> 2;
     float4 v[VPT];
-    load_row<VPT, 256>(xr, opt.col_mul, nv, tid, v);
+    load_row<VPT, 256>(xr, opt.col_mul, opt.col_recip, nv, tid, v);
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < VPT; ++i)
@@ -124,13 +129,15 @@ __global__ __launch_bounds__(256) void quant_rows_twopass(const float* __restric
     if (row >= rows) return;
     const float* xr = x + row * ld;
     const float* m = opt.col_mul;
+    const bool rc = opt.col_recip;
+    auto xv = [&](int64_t c) { return m ? xr[c] * (rc ? 1.0f / m[c] : m[c]) : xr[c]; };
     float amax = 0.0f;
-    for (int64_t c = lane; c < cols; c += 64) amax = fmaxf(amax, fabsf(m ? xr[c] * m[c] : xr[c]));
+    for (int64_t c = lane; c < cols; c += 64) amax = fmaxf(amax, fabsf(xv(c)));
     amax = wave_max(amax);
     const float s = scale_base(amax, opt) / code_range<CODE>();
     if (lane == 0) scale[row] = s;
     int8_t* qr = q + row * cols;
-    for (int64_t c = lane; c < cols; c += 64) qr[c] = (int8_t)encode1<CODE>(m ? xr[c] * m[c] : xr[c], s);
+    for (int64_t c = lane; c < cols; c += 64) qr[c] = (int8_t)encode1<CODE>(xv(c), s);
 }
 
 template <int CODE>

@@ -58,6 +58,7 @@ hipError_t launch_gemm_skinny(int epi, const GemmParams& p, int64_t max_row_bloc
         switch (epi) {
             case EPI_GATE_UP: gemm_skinny<EPI_GATE_UP, FN, D, CODE_INT8><<<grid, block, 0, s>>>(p); break;
             case EPI_DOWN: gemm_skinny<EPI_DOWN, FN, D, CODE_INT8><<<grid, block, 0, s>>>(p); break;
+            case EPI_GU_I32: gemm_skinny<EPI_GU_I32, FN, D, CODE_INT8><<<grid, block, 0, s>>>(p); break;
             default: return hipErrorInvalidValue;
         }
     } else {

@@ -37,7 +37,7 @@ __device__ __forceinline__ void skinny_item(const GemmParams& p, const int64_t i
     int64_t r = row0 + (lane & 15);
     if (r >= row_end) r = row0;
     int64_t src_row = r;
-    if (EPI == EPI_GATE_UP)
+    if (EPI == EPI_GATE_UP || EPI == EPI_GU_I32)
         src_row = min(max((int64_t)(p.sorted_assign[r] / p.topk), (int64_t)0), p.a_rows - 1);
     const int8_t* a_ptr = p.A + src_row * K + (lane >> 4) * 16;
     // packed weights: fragment (channel block nb, k step kb) at
@@ -103,7 +103,15 @@ __device__ __forceinline__ void skinny_item(const GemmParams& p, const int64_t i
     for (int q = 0; q < 4; ++q) {
         const int64_t grow = row0 + (lane >> 4) * 4 + q;
         if (grow >= row_end) continue;
-        if (EPI == EPI_GATE_UP) {
+        if (EPI == EPI_GU_I32) {
+            // raw accumulators (a checking path): gate channel c at column c,
+            // up channel c at column I + c
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int ch = (cb * FN / 2 + j / 2) * 16 + col_in_blk;
+                p.out_i32[grow * 2 * p.I + ((j & 1) ? p.I : 0) + ch] = (int)acc[j][q];
+            }
+        } else if (EPI == EPI_GATE_UP) {
             // column blocks alternate gate / up for the same 16 channels
             const int64_t t = min(max((int64_t)(p.sorted_assign[grow] / p.topk), (int64_t)0), p.a_rows - 1);
             const float sx = p.s_a[t];
