@@ -9,10 +9,13 @@ to the host); nothing the GPU computed is ever fed into it.  Comparison rules:
   max(1e-5, 2 * the largest |GPU logit - oracle logit| of that token).  Those
   are counted and excluded from the exact downstream comparisons; for every
   token the GPU ids must still be a valid top-k of the GPU's own logits.
-* fp32 epilogue outputs (the weighted per-assignment rows o = w * v): v is
-  bit-exact whenever h_q is, so o's error must be the routing weight's
-  relative error (itself bounded by the logit error) plus one rounding, and
-  element-wise <= 1e-3 (the spec bar).
+* h: bit-exact (both sides evaluate SiLU with a correctly rounded exponential
+  and IEEE fp32 operations); a row may differ only by a double rounding of
+  the exponential, and its codes then only next to a rounding midpoint, by
+  one step.  The grouped GEMMs' int32 accumulators are compared exactly: the
+  gate-up ones directly, the down ones through o, which must equal the
+  epilogue on the oracle's accumulators (corrected for moved codes) bit for
+  bit; o against the oracle's own is then within the routing weight's error.
 * the combined output y = sum_j o_j: error <= 1e-3 relative to sum_j |o_j|
   and to the row maximum (sum_rel_metric); element-wise relative error is
   reported but not bounded, since it is ill-conditioned where terms cancel.
