@@ -296,6 +296,25 @@ W8A8_API w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape,
                                              void* const* events, w8a8_stream stream);
 
 /* -------------------------------------------------------------------------
+ * The layer for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation and kernels as w8a8_moe_forward, with the workspace in a
+ * static device array of W8A8_STATIC_WORKSPACE_BYTES that the library holds
+ * on each device it runs on until the process ends (its address is looked up
+ * once per device, on the first call there).  The call allocates and frees
+ * nothing.  Every call on one device shares that device's array and leaves
+ * its intermediates there: calls that overlap on one device (other streams,
+ * other host threads) race and must be serialised by the caller.  Shapes
+ * whose workspace (w8a8_moe_workspace_query) exceeds the array return
+ * W8A8_ERR_WORKSPACE_TOO_SMALL before any launch; otherwise arguments,
+ * limits and errors as w8a8_moe_forward.
+ * ------------------------------------------------------------------------- */
+#define W8A8_STATIC_WORKSPACE_BYTES (64u << 20)
+
+W8A8_API w8a8_status w8a8_moe_forward_static(const w8a8_moe_shape* shape, const w8a8_moe_weights* weights,
+                                             const float* x, float* y, w8a8_stream stream);
+
+/* -------------------------------------------------------------------------
  * The grouped gate-up GEMM's raw int32 accumulators, for checking ([K100AI]
  * sec. 2.1: int8 x int8 products summed in int32; [HUNYUAN] sec. 1.3: each
  * expert's rows read through the routing index).  Runs the layer's gate-up

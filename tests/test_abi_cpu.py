@@ -46,7 +46,7 @@ def exported_symbols():
 
 def test_header_parses():
     fns = header_functions()
-    assert len(fns) == 15, sorted(fns)
+    assert len(fns) == 16, sorted(fns)
 
 
 def test_every_declared_function_is_exported():
@@ -186,6 +186,15 @@ def test_forward_checks_workspace_and_alignment():
     assert acc(sh, ctypes.byref(w), base + 2 * 65536 + 16, 1 << 30, base, None) == 4
     assert acc(sh, ctypes.byref(w), base + 2 * 65536, 1 << 30, base + 2, None) == 4
     assert acc(ctypes.byref(_shape(0, 128, 8, 2, 256)), None, None, 0, None, None) == 0
+    # the allocation-free entry point: a layer whose workspace exceeds the static
+    # scratch is refused before any device call
+    big = ctypes.byref(_shape(8192, 4096, 64, 2, 1536))
+    st = lib.w8a8_moe_forward_static(big, ctypes.byref(w), base, base + 65536, None)
+    assert st == 3 and "static scratch" in lib.w8a8_last_error().decode()
+    assert lib.w8a8_moe_forward_static(ctypes.byref(_shape(0, 128, 8, 2, 256)), None, None, None, None) == 0
+    lay = _lib.MoeLayout()
+    assert lib.w8a8_moe_workspace_query(ctypes.byref(_shape(64, 4096, 64, 2, 1536)), ctypes.byref(lay)) == 0
+    assert lay.total_bytes <= _lib.STATIC_WORKSPACE_BYTES  # the decode layer fits
 
 
 def test_gemm_and_quant_argument_checks():
@@ -308,3 +317,8 @@ def test_binding_rejects_bad_moe_outputs():
     _raises(lambda: api.moe_forward(x, w, 2, workspace=torch.zeros(10)), "workspace must be torch.uint8")
     _raises(lambda: api.moe_forward(x, w, 2, y=torch.zeros(T, H), workspace=torch.zeros(10, dtype=torch.uint8)),
             "x must be a GPU tensor")
+
+
+def test_static_scratch_size_matches_header():
+    m = re.search(r"#define\s+W8A8_STATIC_WORKSPACE_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.STATIC_WORKSPACE_BYTES

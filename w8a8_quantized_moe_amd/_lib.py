@@ -86,7 +86,11 @@ SIGNATURES = {
                                                _P, _P, _P, ctypes.c_size_t, _P, _P]),
     "w8a8_moe_gate_up_acc": (ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeWeights), _P,
                                             ctypes.c_size_t, _P, _P]),
+    "w8a8_moe_forward_static": (ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeWeights), _P, _P,
+                                               _P]),
 }
+
+STATIC_WORKSPACE_BYTES = 64 << 20  # W8A8_STATIC_WORKSPACE_BYTES
 
 MOE_STAGES = ["quant", "route", "gate_up", "requant", "down", "combine"]
 

@@ -14,7 +14,7 @@ from ._lib import check, lib
 
 __all__ = [
     "quantize_rows", "pack_weights", "gemm", "gemm_i32", "MoEWeights", "moe_workspace_layout",
-    "moe_forward", "moe_gate_up_acc", "workspace_views",
+    "moe_forward", "moe_forward_static", "moe_gate_up_acc", "workspace_views",
 ]
 
 
@@ -270,6 +270,27 @@ def moe_forward(x: torch.Tensor, weights: MoEWeights, top_k: int, y: Optional[to
     else:
         check(lib.w8a8_moe_forward_events(ctypes.byref(sh), ctypes.byref(wts), _ptr(x), _ptr(y),
                                           _ptr(workspace), workspace.numel(), events, _stream()))
+    return y
+
+
+def moe_forward_static(x: torch.Tensor, weights: MoEWeights, top_k: int,
+                       y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The layer without a workspace (w8a8_moe_forward_static): the library's
+    static per-device scratch holds the intermediates, so the call allocates
+    nothing on the device (y is allocated here only if None).  Calls that
+    overlap on one device race on that scratch."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D tensor [T, H]")
+    T, H = x.shape
+    specs = [(x, torch.float32, "x", (T, weights.H))] + weights.specs()
+    if y is not None:
+        specs.append((y, torch.float32, "y", (T, H)))
+    _check_all(*specs)
+    if y is None:
+        y = torch.empty_like(x)
+    sh = _shape(T, H, weights.E, top_k, weights.I)
+    wts = weights._struct()
+    check(lib.w8a8_moe_forward_static(ctypes.byref(sh), ctypes.byref(wts), _ptr(x), _ptr(y), _stream()))
     return y
 
 

@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "internal.h"
@@ -427,6 +428,59 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     st = check_hip(w8a8::launch_combine(o, T, k, H, y, s), "combine");
     if (st != W8A8_OK) return st;
     return mark(6);
+}
+
+}  // extern "C"
+
+// ---- the layer without a caller workspace ----
+// One scratch array per device, allocated with the code object when the
+// library is loaded on that device and held until the process ends.  Host
+// code never uses the array's name as an address: it looks the device
+// address up once per device and passes that to the kernels.
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[W8A8_STATIC_WORKSPACE_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[MAX_DEVICES];  // device address of each device's array, set once
+
+w8a8_status scratch_address(void** out) {
+    int dev = -1;
+    w8a8_status st = check_hip(hipGetDevice(&dev), "hipGetDevice");
+    if (st != W8A8_OK) return st;
+    if (dev < 0 || dev >= MAX_DEVICES) return fail(W8A8_ERR_HIP, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        st = check_hip(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        if (st != W8A8_OK) return st;
+        if (!p) return fail(W8A8_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return W8A8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+w8a8_status w8a8_moe_forward_static(const w8a8_moe_shape* shape, const w8a8_moe_weights* wts,
+                                    const float* x, float* y, w8a8_stream stream) {
+    w8a8_status st = check_moe_shape(shape);
+    if (st != W8A8_OK) return st;
+    if (shape->T == 0) return W8A8_OK;
+    const size_t need = plan_moe(shape).lay.total_bytes;
+    if (need > (size_t)W8A8_STATIC_WORKSPACE_BYTES)
+        return fail(W8A8_ERR_WORKSPACE_TOO_SMALL,
+                    "the layer needs %zu bytes of scratch; the static scratch holds %zu "
+                    "(use w8a8_moe_forward with a workspace)",
+                    need, (size_t)W8A8_STATIC_WORKSPACE_BYTES);
+    void* ws = nullptr;
+    if ((st = scratch_address(&ws)) != W8A8_OK) return st;
+    return w8a8_moe_forward_events(shape, wts, x, y, ws, (size_t)W8A8_STATIC_WORKSPACE_BYTES, nullptr,
+                                   stream);
 }
 
 w8a8_status w8a8_moe_gate_up_acc(const w8a8_moe_shape* shape, const w8a8_moe_weights* wts,
