@@ -47,7 +47,7 @@ int moe_bm(int64_t A, int64_t E) { return A <= 4 * E ? w8a8::SKINNY_BM : w8a8::G
 
 struct MoePlan {
     w8a8_moe_workspace_layout lay;
-    size_t partial, wplanes, rank, chunk_counts, chunk_base, mt_prefix, mt_info, tile_ctr;
+    size_t partial, wplanes, rank, chunk_counts, chunk_base, mt_prefix, mt_info, tile_ctr, xcd_bounds;
     int splits, nchunks;
     bool has_planes;
 };
@@ -108,6 +108,7 @@ MoePlan plan_moe(const w8a8_moe_shape* sh) {
     p.mt_prefix = take((E + 1) * 4);
     p.mt_info = take((size_t)max_m_tiles(A, E, moe_bm(A, E)) * sizeof(w8a8::MtInfo));
     p.tile_ctr = take((size_t)w8a8::TILE_CTR_COUNT * w8a8::TILE_CTR_STRIDE * 4);
+    p.xcd_bounds = take(2 * 9 * 4);
     L.total_bytes = off;
     return p;
 }
@@ -344,7 +345,9 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     if (st != W8A8_OK) return st;
 
     // 2-4. router, top-k, permutation
-    w8a8::RouteInputs ri{x, wts->router_w, wts->router_b, T, H, E, k, plan.splits, bm};
+    const int ntv_gu = (int)(2 * I / w8a8::gemm_tile_n(2 * I, code));
+    const int ntv_dn = (int)(H / w8a8::gemm_tile_n(H, code));
+    w8a8::RouteInputs ri{x, wts->router_w, wts->router_b, T, H, E, k, plan.splits, bm, ntv_gu, ntv_dn};
     w8a8::RouteBuffers rb{};
     rb.partial = (float*)(ws + plan.partial);
     rb.wplanes = plan.has_planes ? (void*)(ws + plan.wplanes) : nullptr;
@@ -360,6 +363,7 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     rb.mt_info = mt_info;
     rb.tile_ctr = tile_ctr;
     rb.sorted_assign = sorted;
+    rb.xcd_bounds = (int32_t*)(ws + plan.xcd_bounds);
     if ((st = mark(1)) != W8A8_OK) return st;
     st = check_hip(w8a8::launch_route(ri, rb, s), "route");
     if (st != W8A8_OK) return st;
@@ -376,6 +380,7 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     gu.mt_prefix = mt_prefix;
     gu.mt_info = mt_info;
     gu.tile_ctr = skinny ? nullptr : tile_ctr;
+    gu.xcd_bounds = rb.xcd_bounds;
     gu.G = E;
     gu.sorted_assign = sorted;
     gu.topk = k;
@@ -408,6 +413,7 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     dn.mt_prefix = mt_prefix;
     dn.mt_info = mt_info;
     dn.tile_ctr = skinny ? nullptr : tile_ctr + 8 * w8a8::TILE_CTR_STRIDE;
+    dn.xcd_bounds = rb.xcd_bounds + 9;
     dn.G = E;
     dn.sorted_assign = sorted;
     dn.topk = k;

@@ -38,6 +38,84 @@ __device__ __forceinline__ void write_mt_info(MtInfo* info, int e, int first, in
     for (int q = 0; q < n; ++q) info[first + q] = v;
 }
 
+// Fixed cost of one GEMM tile in rows of work: a tile with r valid rows takes
+// about as long as (TILE_FIXED_ROWS + r) rows' worth of a full tile's time
+// (the whole weight tile streams through whatever the row count).
+constexpr int TILE_FIXED_ROWS = 200;
+
+// The per-m-tile table in longest-first order and the XCD queue bounds of the
+// two grouped GEMMs.  Called by every thread of one workgroup of NT threads
+// (NT >= MAX_EXPERTS); thread e < E holds expert e's row count cnt, segment
+// start off and m-tile count mc.  Experts are ranked by row count, descending,
+// ties to the lower index; their m-tiles are listed in rank order.  The tile
+// order of a GEMM with ntv column tiles is (rank, column tile, m-tile), m-tile
+// fastest; it is cut into 8 contiguous XCD queues of about equal work, each
+// tile weighing TILE_FIXED_ROWS + its rows, at column-tile boundaries of an
+// expert (the m-tiles sharing a weight tile stay on one XCD, and so do the
+// column tiles of an expert, which share its activation rows, but for the
+// experts a cut falls in).  xb[g*9 + x] (g = 0 gate-up, 1 down) is the first
+// tile of queue x, xb[g*9 + 8] the tile count.  lds: 4*MAX_EXPERTS + NT/64 ints.
+template <int NT>
+__device__ __forceinline__ void write_ranked_tables(int cnt, int off, int mc, int E, MtInfo* mt_info,
+                                                    int32_t* xb, int ntv0, int ntv1, int* lds) {
+    static_assert(NT >= MAX_EXPERTS, "one thread per expert");
+    int* cnt_s = lds;                    // by expert
+    int* cnt_r = lds + MAX_EXPERTS;      // by rank
+    int* mc_r = lds + 2 * MAX_EXPERTS;   // by rank
+    int* first_r = lds + 3 * MAX_EXPERTS;
+    int* scan = lds + 4 * MAX_EXPERTS;
+    const int e = threadIdx.x;
+    if (e < MAX_EXPERTS) cnt_s[e] = e < E ? cnt : -1;
+    __syncthreads();
+    int rank = 0;
+    if (e < E) {
+        for (int i = 0; i < E; ++i) {
+            const int c = cnt_s[i];
+            rank += (c > cnt) || (c == cnt && i < e);
+        }
+        cnt_r[rank] = cnt;
+        mc_r[rank] = mc;
+    }
+    __syncthreads();
+    int total;
+    const int fr = block_exclusive_scan<NT / 64>(e < E ? mc_r[e] : 0, &total, scan);
+    if (e < E) first_r[e] = fr;
+    __syncthreads();
+    if (e < E) write_mt_info(mt_info, e, first_r[rank], mc, off, off + cnt);
+    if (e < 18) {
+        const int g = e / 9, x = e % 9;
+        const int64_t ntv = g ? ntv1 : ntv0;
+        int64_t bound;
+        if (x == 0) {
+            bound = 0;
+        } else if (x == 8) {
+            bound = (int64_t)total * ntv;
+        } else {
+            // the first tile whose cumulative work (before it) reaches x/8 of the
+            // total, rounded down to the expert's column-tile groups
+            int64_t S = 0;
+            for (int r = 0; r < E; ++r) S += (int64_t)mc_r[r] * TILE_FIXED_ROWS + cnt_r[r];
+            const int64_t target = (int64_t)x * S;  // compared with 8 x cumulative work
+            int64_t cum = 0;
+            int r = 0;
+            for (; r < E; ++r) {
+                const int64_t gw = (int64_t)mc_r[r] * TILE_FIXED_ROWS + cnt_r[r];
+                if ((cum + gw) * 8 > target) break;
+                cum += gw;
+            }
+            if (r == E) {
+                bound = (int64_t)total * ntv;
+            } else {
+                const int64_t gw = (int64_t)mc_r[r] * TILE_FIXED_ROWS + cnt_r[r];
+                int64_t cols = ntv * (target - 8 * cum) / (8 * gw);
+                cols = cols < 0 ? 0 : (cols > ntv ? ntv : cols);
+                bound = (int64_t)first_r[r] * ntv + cols * mc_r[r];
+            }
+        }
+        xb[e] = (int32_t)bound;
+    }
+}
+
 // k rounds of a wave-wide arg-max over the logits of N tokens of one wave
 // (token u's lane l holds experts l, l+64, l+128, l+192 in v[u][0..3], -inf
 // past E); ties go to the lower expert index.  Lane 0 writes the picks in

@@ -97,8 +97,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     int g = 0, nt;
     int64_t row0, row_end;
     if (p.seg_offsets) {
-        // the expert-major list of m-tiles: one table load names the expert
-        // (the routing built the table for this BM)
+        // the m-tile table (largest expert first): one table load names the
+        // expert (the routing built the table for this BM)
         const MtInfo info = reinterpret_cast<const MtInfo*>(p.mt_info)[L / p.NTV];
         g = info.group;
         const int64_t local = L - (int64_t)info.first_tile * p.NTV;
@@ -735,21 +735,30 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     // when it ends.
     const int xcd = blockIdx.x & 7;
     const int64_t slots = gridDim.x >> 3;
-    auto queue_len = [&](int xq) { return min(per_xcd, max((int64_t)0, total - (int64_t)xq * per_xcd)); };
+    // queue xq: tiles [queue_beg(xq), queue_beg(xq) + queue_len(xq)) -- equal
+    // tile counts, or the routing's work-balanced bounds (persistent grouped)
+    const bool balanced = p.tile_ctr && p.xcd_bounds;
+    auto queue_beg = [&](int xq) -> int64_t {
+        return balanced ? (int64_t)p.xcd_bounds[xq] : min(total, (int64_t)xq * per_xcd);
+    };
+    auto queue_len = [&](int xq) -> int64_t {
+        return balanced ? (int64_t)(p.xcd_bounds[xq + 1] - p.xcd_bounds[xq])
+                        : min(per_xcd, max((int64_t)0, total - (int64_t)xq * per_xcd));
+    };
     auto next_after = [&](int got_own) -> int {
-        if (got_own < queue_len(xcd)) return (int)((int64_t)xcd * per_xcd + got_own);
+        if (got_own < queue_len(xcd)) return (int)(queue_beg(xcd) + got_own);
         for (int q = 1; q < 8; ++q) {
             const int xq = (xcd + q) & 7;
             if (queue_len(xq) == 0) continue;
             const int got = atomicAdd(p.tile_ctr + TILE_CTR_STRIDE * xq, 1);
-            if (got < queue_len(xq)) return (int)((int64_t)xq * per_xcd + got);
+            if (got < queue_len(xq)) return (int)(queue_beg(xq) + got);
         }
         return -1;
     };
     int64_t sl = blockIdx.x >> 3;  // static slot
     int64_t L;
     if (!p.tile_ctr) {
-        L = (sl < queue_len(xcd)) ? (int64_t)xcd * per_xcd + sl : -1;
+        L = (sl < queue_len(xcd)) ? queue_beg(xcd) + sl : -1;
     } else {
         if (tid0 == 0) next_tile[0] = next_after(atomicAdd(p.tile_ctr + TILE_CTR_STRIDE * xcd, 1));
         __syncthreads();
@@ -763,7 +772,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
         __syncthreads();  // every wave is done with the ring, the row metadata and next_tile
         if (!p.tile_ctr) {
             sl += slots;
-            L = (sl < queue_len(xcd)) ? (int64_t)xcd * per_xcd + sl : -1;
+            L = (sl < queue_len(xcd)) ? queue_beg(xcd) + sl : -1;
         } else {
             if (tid0 == 0) next_tile[0] = next_after(got);
             __syncthreads();

@@ -150,7 +150,12 @@ struct GemmParams {
     int32_t* tile_ctr;   // grouped: 8 zeroed tile counters (stride TILE_CTR_STRIDE), one
                          // queue per XCD, for a persistent launch; nullptr: one tile
                          // per workgroup
+    const int32_t* xcd_bounds;  // grouped persistent: [9] tile ranges of the XCD queues (the
+                                // routing balances them by work); nullptr: equal tile counts
 };
+
+// Column tile width of the tiled GEMM for N output columns.
+int gemm_tile_n(int64_t N, int code);
 
 // Tile-queue counters sit 128 bytes apart; the routing zeroes TILE_CTR_COUNT of them.
 constexpr int TILE_CTR_STRIDE = 32;
@@ -209,6 +214,7 @@ struct RouteInputs {
     int T, H, E, k;
     int splits;             // router_plan(T, E, H).splits
     int bm;                 // m-tile height of the grouped GEMMs (GEMM_BM or SKINNY_BM)
+    int ntv_gu, ntv_dn;     // column tiles of the gate-up and down GEMMs (queue bounds)
 };
 
 struct RouteBuffers {
@@ -226,12 +232,16 @@ struct RouteBuffers {
     int32_t* mt_info;         // [m-tiles][4] MtInfo of every m-tile
     int32_t* tile_ctr;        // [TILE_CTR_COUNT * TILE_CTR_STRIDE] zeroed here for the GEMMs' queues
     int32_t* sorted_assign;   // [T*k]
+    int32_t* xcd_bounds;      // [2][9] XCD queue bounds of the gate-up and down GEMMs
 };
 
 hipError_t launch_route(const RouteInputs& in, const RouteBuffers& b, hipStream_t s);
 
 // One entry of the per-m-tile table the routing writes for the grouped GEMMs,
-// so that a workgroup finds its expert with one load instead of a search.
+// so that a workgroup finds its expert with one load instead of a search.  The
+// table lists the experts' m-tiles largest segment first (ties to the lower
+// expert index), so each of the GEMMs' XCD queues holds its longest tiles first
+// (see write_ranked_tables).
 struct MtInfo {
     int32_t group;       // expert
     int32_t first_tile;  // index of the expert's first m-tile

@@ -470,7 +470,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_count(
     float* __restrict__ wts, int32_t* __restrict__ rank, int32_t* __restrict__ chunk_counts,
     int32_t* __restrict__ expert_counts, int32_t* __restrict__ offsets, int bm,
     int32_t* __restrict__ mt_prefix, MtInfo* __restrict__ mt_info, int32_t* __restrict__ tile_ctr,
-    int32_t* __restrict__ sorted_assign) {
+    int32_t* __restrict__ sorted_assign, int32_t* __restrict__ xcd_bounds, int ntv_gu, int ntv_dn) {
     constexpr int NWAVE = TOPK_THREADS / 64;
     constexpr int TPW = ROUTE_CHUNK / NWAVE;  // tokens per wave
     __shared__ int ids_s[ROUTE_CHUNK * MAX_TOPK];
@@ -478,6 +478,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_count(
     __shared__ unsigned long long mask[MAX_EXPERTS];
     __shared__ int off_s[MAX_EXPERTS];
     __shared__ int scan_lds[NWAVE];
+    __shared__ int rank_lds[FUSED ? 4 * MAX_EXPERTS + 32 : 1];
     const int c = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int t0 = c * ROUTE_CHUNK;
@@ -532,12 +533,13 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_count(
             offsets[tid] = off;
             mt_prefix[tid] = m1;
             off_s[tid] = off;
-            write_mt_info(mt_info, tid, m1, (cnt + bm - 1) / bm, off, off + cnt);
         }
         if (tid == 0) {
             offsets[E] = tot0;
             mt_prefix[E] = tot1;
         }
+        write_ranked_tables<TOPK_THREADS>(cnt, off, (cnt + bm - 1) / bm, E, mt_info, xcd_bounds, ntv_gu, ntv_dn,
+                                         rank_lds);
         if (tid < TILE_CTR_COUNT) tile_ctr[tid * TILE_CTR_STRIDE] = 0;
         __syncthreads();
         for (int al = tid; al < nt * k; al += TOPK_THREADS) {
@@ -573,8 +575,11 @@ __global__ __launch_bounds__(256) void finalize(const int32_t* __restrict__ expe
                                                 int bm, int32_t* __restrict__ offsets,
                                                 int32_t* __restrict__ mt_prefix,
                                                 MtInfo* __restrict__ mt_info,
-                                                int32_t* __restrict__ tile_ctr) {
+                                                int32_t* __restrict__ tile_ctr,
+                                                int32_t* __restrict__ xcd_bounds, int ntv_gu,
+                                                int ntv_dn) {
     __shared__ int lds[4];
+    __shared__ int rank_lds[4 * MAX_EXPERTS + 32];
     const int e = threadIdx.x;
     const int cnt = e < E ? expert_counts[e] : 0;
     int tot0, tot1;
@@ -583,8 +588,8 @@ __global__ __launch_bounds__(256) void finalize(const int32_t* __restrict__ expe
     if (e < E) {
         offsets[e] = off;
         mt_prefix[e] = m1;
-        write_mt_info(mt_info, e, m1, (cnt + bm - 1) / bm, off, off + cnt);
     }
+    write_ranked_tables<256>(cnt, off, (cnt + bm - 1) / bm, E, mt_info, xcd_bounds, ntv_gu, ntv_dn, rank_lds);
     if (e == 0) {
         offsets[E] = tot0;
         mt_prefix[E] = tot1;
@@ -667,18 +672,20 @@ hipError_t launch_route(const RouteInputs& in, const RouteBuffers& b, hipStream_
     if (nchunks == 1) {
         topk_count<true><<<1, TOPK_THREADS, 0, s>>>(b.logits, T, E, k, nchunks, b.topk_ids, b.topk_w, b.rank,
                                                     b.chunk_counts, b.expert_counts, b.expert_offsets, in.bm,
-                                                    b.mt_prefix, mt_info, b.tile_ctr, b.sorted_assign);
-        return hipGetLastError();
+                                                    b.mt_prefix, mt_info, b.tile_ctr, b.sorted_assign,
+                                                    b.xcd_bounds, in.ntv_gu, in.ntv_dn);
+    } else {
+        topk_count<false><<<nchunks, TOPK_THREADS, 0, s>>>(b.logits, T, E, k, nchunks, b.topk_ids, b.topk_w,
+                                                           b.rank, b.chunk_counts, b.expert_counts,
+                                                           b.expert_offsets, in.bm, b.mt_prefix, mt_info,
+                                                           b.tile_ctr, b.sorted_assign, b.xcd_bounds, in.ntv_gu,
+                                                           in.ntv_dn);
+        chunk_scan<<<E, 256, 0, s>>>(b.chunk_counts, nchunks, b.chunk_base, b.expert_counts);
+        finalize<<<1, 256, 0, s>>>(b.expert_counts, E, in.bm, b.expert_offsets, b.mt_prefix, mt_info,
+                                   b.tile_ctr, b.xcd_bounds, in.ntv_gu, in.ntv_dn);
+        scatter<<<nchunks, 256, 0, s>>>(b.topk_ids, T, k, nchunks, b.expert_offsets, b.chunk_base,
+                                        b.rank, b.sorted_assign);
     }
-    topk_count<false><<<nchunks, TOPK_THREADS, 0, s>>>(b.logits, T, E, k, nchunks, b.topk_ids, b.topk_w,
-                                                       b.rank, b.chunk_counts, b.expert_counts,
-                                                       b.expert_offsets, in.bm, b.mt_prefix, mt_info,
-                                                       b.tile_ctr, b.sorted_assign);
-    chunk_scan<<<E, 256, 0, s>>>(b.chunk_counts, nchunks, b.chunk_base, b.expert_counts);
-    finalize<<<1, 256, 0, s>>>(b.expert_counts, E, in.bm, b.expert_offsets, b.mt_prefix, mt_info,
-                               b.tile_ctr);
-    scatter<<<nchunks, 256, 0, s>>>(b.topk_ids, T, k, nchunks, b.expert_offsets, b.chunk_base,
-                                    b.rank, b.sorted_assign);
     return hipGetLastError();
 }
 
