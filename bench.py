@@ -293,8 +293,9 @@ def bench_dense(args, torch, synth, w8):
     }
     for e in events:
         hip.destroy(e)
-    out_line["attainable_hbm"] = attainable_hbm(torch)
-    out_line["device"] = device_info(torch)
+    if not args.kernels_only:
+        out_line["attainable_hbm"] = attainable_hbm(torch)
+        out_line["device"] = device_info(torch)
     print(json.dumps(out_line), flush=True)
 
 
@@ -308,6 +309,9 @@ def main():
     ap.add_argument("--code", default="int8", choices=["int8", "fp8"],
                     help="code type of the expert weights and activations (fp8: E4M3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernels-only", action="store_true",
+                    help="time the layer only: no device-copy rate, no rocminfo query, no CPU "
+                         "baseline (for runs under a counter profiler)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration for the traffic field)")
@@ -432,9 +436,10 @@ def main():
         "stage_ms": {s: round(v, 4) for s, v in stage_ms.items()},
         "roofline": roofline,
     }
-    out["attainable_hbm"] = attainable_hbm(torch)
-    out["device"] = device_info(torch)
-    if not args.no_cpu_baseline:
+    if not args.kernels_only:
+        out["attainable_hbm"] = attainable_hbm(torch)
+        out["device"] = device_info(torch)
+    if not (args.no_cpu_baseline or args.kernels_only):
         log("[bench] timing the CPU oracle on a token sample")
         cb = cpu_baseline(inp, args.cpu_seconds, args.code)
         out["cpu_baseline"] = {kk: (round(v, 3) if isinstance(v, float) else v)

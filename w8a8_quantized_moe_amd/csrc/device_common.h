@@ -54,62 +54,77 @@ constexpr int TILE_FIXED_ROWS = 200;
 // expert (the m-tiles sharing a weight tile stay on one XCD, and so do the
 // column tiles of an expert, which share its activation rows, but for the
 // experts a cut falls in).  xb[g*9 + x] (g = 0 gate-up, 1 down) is the first
-// tile of queue x, xb[g*9 + 8] the tile count.  lds: 4*MAX_EXPERTS + NT/64 ints.
+// tile of queue x, xb[g*9 + 8] the tile count.
+struct alignas(16) RankedLds {
+    int cnt_e[MAX_EXPERTS];        // by expert
+    int cnt_r[MAX_EXPERTS];        // by rank
+    int mc_r[MAX_EXPERTS];         // by rank
+    int first_r[MAX_EXPERTS];      // first m-tile, by rank
+    long long work[MAX_EXPERTS];   // inclusive prefix of the ranks' work per column tile
+    int scan[16];                  // one int per wave of the workgroup (at most 1024 threads)
+};
+
 template <int NT>
 __device__ __forceinline__ void write_ranked_tables(int cnt, int off, int mc, int E, MtInfo* mt_info,
-                                                    int32_t* xb, int ntv0, int ntv1, int* lds) {
-    static_assert(NT >= MAX_EXPERTS, "one thread per expert");
-    int* cnt_s = lds;                    // by expert
-    int* cnt_r = lds + MAX_EXPERTS;      // by rank
-    int* mc_r = lds + 2 * MAX_EXPERTS;   // by rank
-    int* first_r = lds + 3 * MAX_EXPERTS;
-    int* scan = lds + 4 * MAX_EXPERTS;
+                                                    int32_t* xb, int ntv0, int ntv1, RankedLds& l) {
+    static_assert(NT >= MAX_EXPERTS && NT % 64 == 0 && NT <= 1024, "one thread per expert");
     const int e = threadIdx.x;
-    if (e < MAX_EXPERTS) cnt_s[e] = e < E ? cnt : -1;
+    if (e < MAX_EXPERTS) l.cnt_e[e] = e < E ? cnt : -1;
     __syncthreads();
     int rank = 0;
     if (e < E) {
-        for (int i = 0; i < E; ++i) {
-            const int c = cnt_s[i];
-            rank += (c > cnt) || (c == cnt && i < e);
+        const int4* c4 = reinterpret_cast<const int4*>(l.cnt_e);
+        for (int i4 = 0; i4 < (E + 3) / 4; ++i4) {
+            const int4 c = c4[i4];
+            const int i = 4 * i4;
+            rank += (c.x > cnt) || (c.x == cnt && i < e);
+            rank += (c.y > cnt) || (c.y == cnt && i + 1 < e);
+            rank += (c.z > cnt) || (c.z == cnt && i + 2 < e);
+            rank += (c.w > cnt) || (c.w == cnt && i + 3 < e);
         }
-        cnt_r[rank] = cnt;
-        mc_r[rank] = mc;
+        l.cnt_r[rank] = cnt;
+        l.mc_r[rank] = mc;
     }
     __syncthreads();
     int total;
-    const int fr = block_exclusive_scan<NT / 64>(e < E ? mc_r[e] : 0, &total, scan);
-    if (e < E) first_r[e] = fr;
+    const int r_mc = e < E ? l.mc_r[e] : 0;
+    const int fr = block_exclusive_scan<NT / 64>(r_mc, &total, l.scan);
+    long long w = e < E ? (long long)r_mc * TILE_FIXED_ROWS + l.cnt_r[e] : 0;
+    if (e < MAX_EXPERTS) {
+        l.first_r[e] = fr;
+        l.work[e] = w;
+    }
     __syncthreads();
-    if (e < E) write_mt_info(mt_info, e, first_r[rank], mc, off, off + cnt);
+    for (int o = 1; o < MAX_EXPERTS; o <<= 1) {  // inclusive prefix of the work
+        const long long u = (e < MAX_EXPERTS && e >= o) ? l.work[e - o] : 0;
+        __syncthreads();
+        if (e < MAX_EXPERTS) l.work[e] = (w += u);
+        __syncthreads();
+    }
+    if (e < E) write_mt_info(mt_info, e, l.first_r[rank], mc, off, off + cnt);
     if (e < 18) {
         const int g = e / 9, x = e % 9;
         const int64_t ntv = g ? ntv1 : ntv0;
-        int64_t bound;
-        if (x == 0) {
-            bound = 0;
-        } else if (x == 8) {
-            bound = (int64_t)total * ntv;
-        } else {
-            // the first tile whose cumulative work (before it) reaches x/8 of the
-            // total, rounded down to the expert's column-tile groups
-            int64_t S = 0;
-            for (int r = 0; r < E; ++r) S += (int64_t)mc_r[r] * TILE_FIXED_ROWS + cnt_r[r];
-            const int64_t target = (int64_t)x * S;  // compared with 8 x cumulative work
-            int64_t cum = 0;
-            int r = 0;
-            for (; r < E; ++r) {
-                const int64_t gw = (int64_t)mc_r[r] * TILE_FIXED_ROWS + cnt_r[r];
-                if ((cum + gw) * 8 > target) break;
-                cum += gw;
+        int64_t bound = (x == 8) ? (int64_t)total * ntv : 0;
+        if (x > 0 && x < 8) {
+            // the first rank whose work ends past x/8 of the total; the cut
+            // falls at the column tile where x/8 of the work is reached
+            const long long S = l.work[E - 1];
+            const long long target = (long long)x * S;  // against 8 x cumulative work
+            int lo = 0, hi = E;  // smallest r with 8 * work[r] > target
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (8 * l.work[mid] > target) hi = mid;
+                else lo = mid + 1;
             }
-            if (r == E) {
+            if (lo == E) {
                 bound = (int64_t)total * ntv;
             } else {
-                const int64_t gw = (int64_t)mc_r[r] * TILE_FIXED_ROWS + cnt_r[r];
-                int64_t cols = ntv * (target - 8 * cum) / (8 * gw);
+                const long long gw = (long long)l.mc_r[lo] * TILE_FIXED_ROWS + l.cnt_r[lo];
+                const long long cum = l.work[lo] - gw;
+                long long cols = ntv * (target - 8 * cum) / (8 * gw);
                 cols = cols < 0 ? 0 : (cols > ntv ? ntv : cols);
-                bound = (int64_t)first_r[r] * ntv + cols * mc_r[r];
+                bound = (int64_t)l.first_r[lo] * ntv + cols * l.mc_r[lo];
             }
         }
         xb[e] = (int32_t)bound;

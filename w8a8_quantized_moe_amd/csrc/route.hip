@@ -478,7 +478,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_count(
     __shared__ unsigned long long mask[MAX_EXPERTS];
     __shared__ int off_s[MAX_EXPERTS];
     __shared__ int scan_lds[NWAVE];
-    __shared__ int rank_lds[FUSED ? 4 * MAX_EXPERTS + 32 : 1];
+    __shared__ RankedLds ranked_lds[1];  // used by the single-chunk launch
     const int c = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int t0 = c * ROUTE_CHUNK;
@@ -538,8 +538,12 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_count(
             offsets[E] = tot0;
             mt_prefix[E] = tot1;
         }
-        write_ranked_tables<TOPK_THREADS>(cnt, off, (cnt + bm - 1) / bm, E, mt_info, xcd_bounds, ntv_gu, ntv_dn,
-                                         rank_lds);
+        if (bm == SKINNY_BM) {  // the skinny GEMMs take the m-tiles in expert order
+            if (tid < E) write_mt_info(mt_info, tid, m1, (cnt + bm - 1) / bm, off, off + cnt);
+        } else {
+            write_ranked_tables<TOPK_THREADS>(cnt, off, (cnt + bm - 1) / bm, E, mt_info, xcd_bounds, ntv_gu,
+                                              ntv_dn, ranked_lds[0]);
+        }
         if (tid < TILE_CTR_COUNT) tile_ctr[tid * TILE_CTR_STRIDE] = 0;
         __syncthreads();
         for (int al = tid; al < nt * k; al += TOPK_THREADS) {
@@ -579,7 +583,7 @@ __global__ __launch_bounds__(256) void finalize(const int32_t* __restrict__ expe
                                                 int32_t* __restrict__ xcd_bounds, int ntv_gu,
                                                 int ntv_dn) {
     __shared__ int lds[4];
-    __shared__ int rank_lds[4 * MAX_EXPERTS + 32];
+    __shared__ RankedLds ranked_lds;
     const int e = threadIdx.x;
     const int cnt = e < E ? expert_counts[e] : 0;
     int tot0, tot1;
@@ -589,7 +593,12 @@ __global__ __launch_bounds__(256) void finalize(const int32_t* __restrict__ expe
         offsets[e] = off;
         mt_prefix[e] = m1;
     }
-    write_ranked_tables<256>(cnt, off, (cnt + bm - 1) / bm, E, mt_info, xcd_bounds, ntv_gu, ntv_dn, rank_lds);
+    if (bm == SKINNY_BM) {  // the skinny GEMMs take the m-tiles in expert order
+        if (e < E) write_mt_info(mt_info, e, m1, (cnt + bm - 1) / bm, off, off + cnt);
+    } else {
+        write_ranked_tables<256>(cnt, off, (cnt + bm - 1) / bm, E, mt_info, xcd_bounds, ntv_gu, ntv_dn,
+                                 ranked_lds);
+    }
     if (e == 0) {
         offsets[E] = tot0;
         mt_prefix[E] = tot1;
