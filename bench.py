@@ -78,22 +78,24 @@ class HipEvents:
             self.hip.hipEventDestroy(ev)
 
 
-# HBM traffic per dispatch measured with rocprofv3 counters (FETCH_SIZE and
-# WRITE_SIZE, each in its own pass, scaled by what the same counters read for a
-# plain device copy of known size).  Valid only for the kernel sources it was
-# measured on: the hash below must match the sources as they are now.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# Per-dispatch hardware counters of each stage's kernels, measured with
+# rocprofv3 (FETCH_SIZE and WRITE_SIZE each in its own pass, scaled by what the
+# same counters read for a plain device copy of known size; GRBM_COUNT for the
+# engine clock the kernel ran at; SQ_VALU_MFMA_BUSY_CYCLES).  Valid only for
+# the kernel sources they were measured on: the hash below must match the
+# sources as they are now.
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SOURCES = ["w8a8_quantized_moe_amd/csrc/gemm.hip", "w8a8_quantized_moe_amd/csrc/internal.h",
                   "w8a8_quantized_moe_amd/csrc/device_common.h", "w8a8_quantized_moe_amd/csrc/skinny_item.h",
                   "w8a8_quantized_moe_amd/csrc/route.hip", "w8a8_quantized_moe_amd/csrc/quant.hip",
                   "w8a8_quantized_moe_amd/csrc/combine.hip", "w8a8_quantized_moe_amd/csrc/skinny.hip",
                   "w8a8_quantized_moe_amd/csrc/abi.cpp"]
+PEAK_CLOCK_MHZ = 2400.0  # the engine clock the published matrix peaks assume
 
 
 def _code_only(text):
     """Source text without comments and blank lines (a comment edit does not
     change the kernels the counters were taken on)."""
-    import re
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     text = re.sub(r"//[^\n]*", "", text)
     return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
@@ -107,21 +109,34 @@ def kernel_sources_hash():
     return h.hexdigest()
 
 
-def measured_traffic(workload, stage, code="int8"):
-    """HBM bytes per launch of a stage from profiles/traffic.json, or None when
-    there is no measurement or the kernels changed since it was taken."""
+def measured_counters(workload, stage, code="int8"):
+    """The stage's counter record from profiles/counters.json, or None when
+    there is none or the kernels changed since it was taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(COUNTERS_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     if rec.get("sources_sha256") != kernel_sources_hash():
         return None
     key = f"{workload}:{stage}" if code == "int8" else f"{workload}/{code}:{stage}"
-    ent = rec.get("stages", {}).get(key)
+    return rec.get("stages", {}).get(key)
+
+
+def counter_fields(ent, bound, achieved, peak):
+    """traffic (HBM bytes per launch), and for a matrix-bound kernel the engine
+    clock it sustained, the fraction of the peak scaled to that clock, and the
+    MFMA-busy fraction; None where no valid counter record exists."""
+    out = {"traffic": None}
     if not ent:
-        return None
-    return int(ent["fetch_bytes"] + ent["write_bytes"])
+        return out
+    out["traffic"] = int(ent["fetch_bytes"] + ent["write_bytes"])
+    clk = ent.get("clock_mhz")
+    if bound == "mfma" and clk:
+        out["sustained_clock_mhz"] = clk
+        out["frac_at_sustained_clock"] = round(achieved / (peak * clk / PEAK_CLOCK_MHZ), 4)
+        out["mfma_busy"] = ent.get("mfma_busy")
+    return out
 
 
 def copy_calibration(torch, nbytes=1 << 30, reps=5):
@@ -285,8 +300,9 @@ def bench_dense(args, torch, synth, w8):
         "roofline": dict(kernel="gemm", bound="mfma", achieved=round(ops / (g_ms * 1e-3) / 1e12, 2),
                          peak=PEAK_INT8_OPS / 1e12, unit="TOP/s",
                          frac=round(ops / (g_ms * 1e-3) / PEAK_INT8_OPS, 4),
-                         traffic=measured_traffic("dense", "gemm"),
-                         work_per_launch=ops),
+                         work_per_launch=ops,
+                         **counter_fields(measured_counters("dense", "gemm"), "mfma",
+                                          ops / (g_ms * 1e-3), PEAK_INT8_OPS)),
         "quant_roofline": dict(bound="hbm", achieved=round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
                                peak=PEAK_HBM / 1e9, unit="GB/s",
                                frac=round(q_bytes / (q_ms * 1e-3) / PEAK_HBM, 4)),
@@ -402,8 +418,8 @@ def main():
     scale = 1e9 if unit == "GB/s" else 1e12
     achieved = amount / (dom_ms * 1e-3)
     roofline = dict(kernel=dom, bound=bound, achieved=round(achieved / scale, 2),
-                    peak=peak / scale, unit=unit, frac=round(achieved / peak, 4),
-                    traffic=measured_traffic(args.workload, dom, args.code), work_per_launch=amount)
+                    peak=peak / scale, unit=unit, frac=round(achieved / peak, 4), work_per_launch=amount,
+                    **counter_fields(measured_counters(args.workload, dom, args.code), bound, achieved, peak))
 
     step_s = ms_per_step * 1e-3
     int8_ops = 6 * A * H * I

@@ -54,3 +54,29 @@ def test_source_hash_ignores_comments_only():
     c = "int f() { return 2; }\nint g;\n"
     assert bench._code_only(a) == bench._code_only(b)
     assert bench._code_only(a) != bench._code_only(c)
+
+
+def test_counter_fields_scale_to_the_sustained_clock():
+    ent = {"fetch_bytes": 1000, "write_bytes": 24, "clock_mhz": 1800.0, "mfma_busy": 0.6}
+    f = bench.counter_fields(ent, "mfma", achieved=2.0e15, peak=5.0e15)
+    assert f["traffic"] == 1024
+    assert f["sustained_clock_mhz"] == 1800.0
+    # 2.0 of 5.0 POP/s at 2400 MHz is 2.0 of 3.75 at 1800 MHz
+    assert abs(f["frac_at_sustained_clock"] - 2.0 / 3.75) < 1e-4
+    # memory-bound kernels carry traffic only; no record, no fields
+    assert bench.counter_fields(ent, "hbm", 1.0, 2.0) == {"traffic": 1024}
+    assert bench.counter_fields(None, "mfma", 1.0, 2.0) == {"traffic": None}
+
+
+def test_committed_counters_cover_the_dominant_stages():
+    with open(bench.COUNTERS_FILE) as f:
+        rec = json.load(f)
+    st = rec["stages"]
+    for key in ("large:gate_up", "large:down", "prefill:gate_up", "decode:gate_up", "dense:gemm",
+                "large/fp8:gate_up"):
+        assert key in st, key
+        assert st[key]["fetch_bytes"] > 0 and st[key]["avg_us"] > 0
+    # the matrix-bound kernels carry the clock they ran at, below the peak clock
+    for key in ("large:gate_up", "large:down", "dense:gemm"):
+        assert 1000 < st[key]["clock_mhz"] <= bench.PEAK_CLOCK_MHZ
+        assert 0 < st[key]["mfma_busy"] < 1
