@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 # MI355X published peaks (dense)
 PEAK_INT8_OPS = 5.0e15      # int8 MFMA, ops/s
 PEAK_FP8_OPS = 5.0e15       # fp8 MFMA, flop/s (the same as int8 on this chip)
+PEAK_BF16_OPS = 2.5e15      # bf16 MFMA, flop/s (the exact FP8 path multiplies decoded codes here)
 PEAK_FP32_MFMA = 157.3e12   # fp32 matrix, flop/s
 PEAK_HBM = 8.0e12           # bytes/s
 
@@ -204,7 +205,7 @@ def stage_work(T, H, E, k, I, touched, code="int8"):
     gu_ops, dn_ops = 2 * A * H * 2 * I, 2 * A * I * H
     gu_bytes = touched * (2 * I * H + 8 * I) + A * H + 4 * T + 4 * A * I
     dn_bytes = touched * (H * I + 4 * H) + A * I + 8 * A + 4 * A * H
-    peak_mma = PEAK_INT8_OPS if code == "int8" else PEAK_FP8_OPS
+    peak_mma = {"int8": PEAK_INT8_OPS, "fp8": PEAK_BF16_OPS, "fp8_fast": PEAK_FP8_OPS}[code]
     ridge = peak_mma / PEAK_HBM
 
     def gemm(ops, nbytes):
@@ -239,7 +240,8 @@ def cpu_baseline(inp, target_s, code="int8"):
 
     def run(n):
         t0 = time.perf_counter()
-        oracle.moe_forward(x, wr, b, w_gu, s_gu, w_d, s_d, k, route_tokens=np.arange(n), code=code)
+        oracle.moe_forward(x, wr, b, w_gu, s_gu, w_d, s_d, k, route_tokens=np.arange(n),
+                           code="int8" if code == "int8" else "fp8")
         return time.perf_counter() - t0
 
     probe_n = min(8, T)
@@ -322,8 +324,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large",
                     choices=["large", "prefill", "decode", "tiny", "dense"])
-    ap.add_argument("--code", default="int8", choices=["int8", "fp8"],
-                    help="code type of the expert weights and activations (fp8: E4M3)")
+    ap.add_argument("--code", default="int8", choices=["int8", "fp8", "fp8_fast"],
+                    help="code type of the expert weights and activations (fp8: E4M3 codes, exact "
+                         "products summed in fp32 on the bf16 matrix cores; fp8_fast: E4M3 codes on "
+                         "the FP8 matrix cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels-only", action="store_true",
                     help="time the layer only: no device-copy rate, no rocminfo query, no CPU "
@@ -355,13 +359,13 @@ def main():
     T, H, E, k, I = inp["T"], inp["H"], inp["E"], inp["k"], inp["I"]
     A = T * k
     if "w_gu_f32" in inp:
+        code = {"int8": w8.CODE_INT8, "fp8": w8.CODE_FP8, "fp8_fast": w8.CODE_FP8_FAST}[args.code]
         wts, codes = w8.MoEWeights.from_fp32(inp["wr"], inp["b"], inp["w_gu_f32"], inp["w_d_f32"],
-                                             keep_codes=True,
-                                             code=w8.CODE_FP8 if args.code == "fp8" else w8.CODE_INT8)
+                                             keep_codes=True, code=code)
         inp.update(codes)
     else:
         wts = w8.MoEWeights.from_int8(inp["wr"], inp["b"], inp["w_gu"], inp["s_gu"], inp["w_d"],
-                                      inp["s_d"])
+                                      inp["s_d"], fp8_fast=args.code == "fp8_fast")
     lay = w8.moe_workspace_layout(T, H, E, k, I)
     ws = torch.empty((lay["total_bytes"],), dtype=torch.uint8, device="cuda")
     y = torch.empty_like(inp["x"])
@@ -440,11 +444,13 @@ def main():
         "data": f"synthetic (seeded; random {'int8' if args.code == 'int8' else 'FP8 E4M3'} expert "
                 "weights of the layer's shape)",
         "config": {"workload": f"{args.workload} MoE layer T={T} H={H} E={E} top-{k} I={I}"
-                               + ("" if args.code == "int8" else ", FP8 E4M3 codes"),
+                               + {"int8": "", "fp8": ", FP8 E4M3 codes (exact products, fp32 sums)",
+                                  "fp8_fast": ", FP8 E4M3 codes on the FP8 matrix cores"}[args.code],
                    "T": T, "H": H, "E": E, "top_k": k, "I": I, "code": args.code,
                    "parallelism": "none (1 GPU)"},
         f"{args.code}_tops": round(int8_ops / step_s / 1e12, 2),
-        f"{args.code}_frac_of_peak": round(int8_ops / step_s / PEAK_INT8_OPS, 4),
+        f"{args.code}_frac_of_peak": round(int8_ops / step_s / work["gate_up"][3], 4)
+        if work["gate_up"][0] == "mfma" else round(int8_ops / step_s / PEAK_INT8_OPS, 4),
         "alg_hbm_gbps": round(alg_bytes / step_s / 1e9, 1),
         "hbm_frac_of_peak": round(alg_bytes / step_s / PEAK_HBM, 4),
         "experts_touched": touched,

@@ -70,7 +70,7 @@ W8A8_API const char* w8a8_status_string(int status);
 /* Thread-local detail of the last non-OK status returned on this thread. */
 W8A8_API const char* w8a8_last_error(void);
 
-/* ABI version of this header: 3. */
+/* ABI version of this header: 4. */
 W8A8_API int w8a8_abi_version(void);
 
 /* -------------------------------------------------------------------------
@@ -97,7 +97,14 @@ W8A8_API w8a8_status w8a8_quantize_rows(const float* x, int64_t rows, int64_t co
  * OCP E4M3FN format: sign | exponent (bias 7) | mantissa, exponent 0 for
  * subnormals m * 2^-9, no infinities, S.1111.111 = NaN, largest value 448.
  * ------------------------------------------------------------------------- */
-enum { W8A8_CODE_INT8 = 0, W8A8_CODE_FP8_E4M3 = 1 };
+/* W8A8_CODE_FP8_E4M3: E4M3 codes, every product of two codes exact and the
+ * products summed in fp32 -- the fp32 accumulator of [DSV4] sec. 2.3 (E4M3
+ * values are bf16 values, so the bf16 matrix cores multiply them exactly).
+ * W8A8_CODE_FP8_E4M3_FAST: the same codes on the FP8 matrix cores, at twice
+ * that rate, but below that contract: inside one instruction the hardware
+ * aligns each group of 8 consecutive products to the largest of the group
+ * and drops bits below about 2^-13 of it.  Both store identical codes. */
+enum { W8A8_CODE_INT8 = 0, W8A8_CODE_FP8_E4M3 = 1, W8A8_CODE_FP8_E4M3_FAST = 2 };
 
 /* Per-row dynamic FP8 quantisation: the scheme of w8a8_quantize_rows with the
  * E4M3 range ([DSV4] sec. 2.1):
@@ -134,7 +141,7 @@ enum { W8A8_SCALE_DYNAMIC = 0, W8A8_SCALE_CLIPPED = 1, W8A8_SCALE_STATIC = 2,
  * path); scale_mode: a W8A8_SCALE_* mode, optionally or'ed with
  * W8A8_SCALE_COL_RECIPROCAL (needs col_mul); clip: positive and finite for the
  * clipped and static modes, ignored for the dynamic one; code:
- * W8A8_CODE_INT8 (q is int8) or W8A8_CODE_FP8_E4M3 (q is uint8 E4M3).  Other
+ * W8A8_CODE_INT8 (q is int8) or either FP8 code (q is uint8 E4M3).  Other
  * arguments, limits and errors as for w8a8_quantize_rows;
  * W8A8_ERR_INVALID_ARGUMENT for an unknown mode or code or a bad clip. */
 W8A8_API w8a8_status w8a8_quantize_rows_ex(const float* x, int64_t rows, int64_t cols, int64_t ld,
@@ -186,17 +193,25 @@ W8A8_API w8a8_status w8a8_gemm_i32(const int8_t* a_q, const int8_t* b_packed, in
                           int64_t K, int32_t* acc, w8a8_stream stream);
 
 /* The same GEMM with FP8 E4M3 codes ([DSV4] sec. 2.3: fp8 inputs, fp32
- * accumulator): acc[m][n] = sum_k E4M3(a_q[m][k]) * E4M3(b[n][k]) on the FP8
- * matrix cores, out = ((float)acc * s_a[m]) * s_b[n].  Not exact: the
- * accumulator between matrix instructions is fp32, but inside one instruction
- * (128 k) the hardware aligns the products to the largest one and drops bits
- * below about 2^-16 of it; on Gaussian-like codes the error stays below
- * 2^-16 * sum_k |a_k b_k|.  b_packed is the uint8 codes packed like int8
- * weights (w8a8_pack_weights moves bytes).  Limits and errors as for
- * w8a8_gemm. */
+ * accumulator): acc[m][n] = sum_k E4M3(a_q[m][k]) * E4M3(b[n][k]),
+ * out = ((float)acc * s_a[m]) * s_b[n].  Every product is exact; they are
+ * summed in fp32 (16 or 32 products per matrix instruction, then the running
+ * fp32 accumulator): a chain of at most K/16 + 5 fp32 additions per output, so
+ * |acc - exact| <= (K/16 + 5) * 2^-24 * sum_k |a_k b_k| to first order.
+ * b_packed is the uint8 codes packed like int8 weights (w8a8_pack_weights
+ * moves bytes).  Limits and errors as for w8a8_gemm. */
 W8A8_API w8a8_status w8a8_gemm_fp8(const uint8_t* a_q, const float* s_a, const uint8_t* b_packed,
                                    const float* s_b, int64_t M, int64_t N, int64_t K, float* out,
                                    w8a8_stream stream);
+
+/* w8a8_gemm_fp8 on the FP8 matrix cores (W8A8_CODE_FP8_E4M3_FAST): twice the
+ * matrix rate, not exact products: inside one instruction each group of 8
+ * consecutive k is aligned to its largest product and bits below 2^-13 of
+ * that product are dropped; the group sums and the accumulator are fp32.
+ * Arguments, limits and errors as for w8a8_gemm_fp8. */
+W8A8_API w8a8_status w8a8_gemm_fp8_fast(const uint8_t* a_q, const float* s_a, const uint8_t* b_packed,
+                                        const float* s_b, int64_t M, int64_t N, int64_t K, float* out,
+                                        w8a8_stream stream);
 
 /* -------------------------------------------------------------------------
  * The MoE expert layer.
@@ -241,8 +256,10 @@ typedef struct {
     const float* s_gate_up;
     const int8_t* w_down;
     const float* s_down;
-    int32_t code;  /* W8A8_CODE_INT8 or W8A8_CODE_FP8_E4M3: the code of w_gate_up
-                      and w_down, and the code the layer quantises x and h to */
+    int32_t code;  /* W8A8_CODE_INT8, W8A8_CODE_FP8_E4M3 or W8A8_CODE_FP8_E4M3_FAST:
+                      the code of w_gate_up and w_down, the code the layer
+                      quantises x and h to, and (FP8) the matrix cores that
+                      multiply them */
     /* Options of the per-token quantisation of x (see w8a8_quantize_rows_ex;
      * zero-initialised: plain dynamic absmax).  x_smooth: NULL or [H] fp32,
      * 16-byte aligned; w_gate_up must then hold the codes of the weights with

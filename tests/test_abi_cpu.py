@@ -46,7 +46,7 @@ def exported_symbols():
 
 def test_header_parses():
     fns = header_functions()
-    assert len(fns) == 16, sorted(fns)
+    assert len(fns) == 17, sorted(fns)
 
 
 def test_every_declared_function_is_exported():
@@ -73,7 +73,7 @@ def test_status_strings_and_version():
     for code, name in names.items():
         assert lib.w8a8_status_string(code).decode() == name
     assert lib.w8a8_status_string(99).decode() == "W8A8_UNKNOWN_STATUS"
-    assert lib.w8a8_abi_version() == 3
+    assert lib.w8a8_abi_version() == 4
 
 
 def _shape(T, H, E, k, I):
@@ -172,10 +172,16 @@ def test_forward_checks_workspace_and_alignment():
     st = lib.w8a8_moe_forward(sh, ctypes.byref(clip_bad), base, base + 65536, base + 2 * 65536,
                               1 << 30, None)
     assert st == 1 and "clip" in lib.w8a8_last_error().decode()
-    bad = _lib.MoeWeights(base, None, base, base, base, base, 7)
-    st = lib.w8a8_moe_forward(sh, ctypes.byref(bad), base, base + 65536, base + 2 * 65536, 1 << 30,
-                              None)
-    assert st == 1 and "code" in lib.w8a8_last_error().decode()  # unknown weight code
+    for c in (3, 7, -1):
+        bad = _lib.MoeWeights(base, None, base, base, base, base, c)
+        st = lib.w8a8_moe_forward(sh, ctypes.byref(bad), base, base + 65536, base + 2 * 65536, 1 << 30,
+                                  None)
+        assert st == 1 and "code" in lib.w8a8_last_error().decode()  # unknown weight code
+    # both FP8 codes pass the code check (the call then stops at the next one)
+    for c in (_lib.CODE_FP8, _lib.CODE_FP8_FAST):
+        ok = _lib.MoeWeights(base, None, base, base, base, base, c)
+        st = lib.w8a8_moe_forward(sh, ctypes.byref(ok), base, base, base + 2 * 65536, 1 << 30, None)
+        assert st == 1 and "alias" in lib.w8a8_last_error().decode()
     # the gate-up accumulator capture: INT8 codes only, a non-NULL output, a
     # large enough aligned workspace
     acc = lib.w8a8_moe_gate_up_acc
@@ -218,6 +224,13 @@ def test_gemm_and_quant_argument_checks():
     assert lib.w8a8_quantize_rows_ex(base, 4, 16, 16, None, 0, 0.0, 5, base, base, None) == 1
     assert lib.w8a8_quantize_rows_ex(base, 4, 16, 16, base + 2, 0, 0.0, 0, base, base, None) == 4
     assert lib.w8a8_quantize_rows_ex(None, 0, 16, 16, None, 1, 2.0, 1, None, None, None) == 0
+    assert lib.w8a8_quantize_rows_ex(None, 0, 16, 16, None, 1, 2.0, 2, None, None, None) == 0   # FP8 fast
+    assert lib.w8a8_quantize_rows_ex(base, 4, 16, 16, None, 0, 0.0, 3, base, base, None) == 1
+    # the FP8 GEMMs share the INT8 GEMM's checks
+    for fn in (lib.w8a8_gemm_fp8, lib.w8a8_gemm_fp8_fast):
+        assert fn(base, base, base, base, 256, 200, 256, base, None) == 2
+        assert fn(base + 1, base, base, base, 256, 256, 256, base, None) == 4
+        assert fn(None, None, None, None, 0, 256, 256, None, None) == 0
     # the reciprocal flag needs a factor, and combines with a valid mode only
     assert lib.w8a8_quantize_rows_ex(base, 4, 16, 16, None, 0x10, 0.0, 0, base, base, None) == 1
     assert lib.w8a8_quantize_rows_ex(base, 4, 16, 16, base, 0x13, 1.0, 0, base, base, None) == 1

@@ -4,7 +4,7 @@ The computation lives in libw8a8moe.so (hand-written HIP kernels behind the C
 ABI of include/w8a8moe.h); this package is its thin Python binding.  Importing
 it fails if the library has not been built: there is no CPU fallback.
 """
-from ._lib import (CODE_FP8, CODE_INT8, LIB_PATH, PACK_GATE_UP, PACK_PLAIN, SCALE_CLIPPED,  # noqa: F401
+from ._lib import (CODE_FP8, CODE_FP8_FAST, CODE_INT8, LIB_PATH, PACK_GATE_UP, PACK_PLAIN, SCALE_CLIPPED,  # noqa: F401
                    SCALE_COL_RECIPROCAL, SCALE_DYNAMIC, SCALE_STATIC, W8A8Error, check, lib)
 from .api import (MoEWeights, gemm, gemm_i32, moe_forward, moe_forward_static, moe_gate_up_acc,
                   moe_workspace_layout,  # noqa: F401

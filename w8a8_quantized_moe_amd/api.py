@@ -62,7 +62,8 @@ def quantize_rows(x: torch.Tensor, q: Optional[torch.Tensor] = None,
                   col_mul: Optional[torch.Tensor] = None, scale_mode: int = _lib.SCALE_DYNAMIC,
                   clip: float = 0.0, col_reciprocal: bool = False):
     """Per-row quantisation of a [rows, cols] fp32 matrix (any leading
-    dimension via stride(0)) to int8 codes or (code=CODE_FP8) uint8 E4M3 codes,
+    dimension via stride(0)) to int8 codes or (code=CODE_FP8 or CODE_FP8_FAST,
+    which store the same codes) uint8 E4M3 codes,
     optionally with a per-column factor col_mul [cols] and a clipped or static
     scale (w8a8_quantize_rows_ex); with col_reciprocal the factor applied is
     1 / col_mul (the library divides).  Returns (q [rows, cols], scale fp32
@@ -72,7 +73,9 @@ def quantize_rows(x: torch.Tensor, q: Optional[torch.Tensor] = None,
     if not x.is_cuda:
         raise ValueError("x must be a GPU tensor")
     rows, cols = x.shape
-    fp8 = code == _lib.CODE_FP8
+    if code not in (_lib.CODE_INT8, _lib.CODE_FP8, _lib.CODE_FP8_FAST):
+        raise ValueError(f"unknown code {code}")
+    fp8 = code != _lib.CODE_INT8
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8 if fp8 else torch.int8, device=x.device)
     if scale is None:
@@ -116,10 +119,11 @@ def _gemm_specs(a_q, b_packed, N: int, K: int, a_dtype):
     return M, [(a_q, a_dtype, "a_q", (M, K)), (b_packed, (torch.int8, torch.uint8), "b_packed", None, N * K)]
 
 
-def gemm(a_q, s_a, b_packed, s_b, N: int, K: int, out=None) -> torch.Tensor:
+def gemm(a_q, s_a, b_packed, s_b, N: int, K: int, out=None, fp8_fast: bool = False) -> torch.Tensor:
     """Dense W8A8 GEMM: out = ((float)(a_q @ b^T) * s_a[:, None]) * s_b[None, :].
     int8 a_q: int8 codes (exact int32 accumulation); uint8 a_q: FP8 E4M3 codes
-    (fp32 accumulation), with b packed from codes of the same kind.
+    (exact products summed in fp32; with fp8_fast on the FP8 matrix cores),
+    with b packed from codes of the same kind.
     a_q [M, K]; b_packed: N*K bytes from pack_weights; s_a [M]; s_b [N];
     out [M, N] fp32 (allocated if None)."""
     fp8 = isinstance(a_q, torch.Tensor) and a_q.dtype == torch.uint8
@@ -130,7 +134,9 @@ def gemm(a_q, s_a, b_packed, s_b, N: int, K: int, out=None) -> torch.Tensor:
     _check_all(*specs)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=a_q.device)
-    fn = lib.w8a8_gemm_fp8 if fp8 else lib.w8a8_gemm
+    if fp8_fast and not fp8:
+        raise ValueError("fp8_fast needs uint8 (E4M3) codes")
+    fn = (lib.w8a8_gemm_fp8_fast if fp8_fast else lib.w8a8_gemm_fp8) if fp8 else lib.w8a8_gemm
     check(fn(_ptr(a_q), _ptr(s_a), _ptr(b_packed), _ptr(s_b), M, N, K, _ptr(out), _stream()))
     return out
 
@@ -160,20 +166,26 @@ class MoEWeights:
     s_gate_up: torch.Tensor           # [E, 2I] fp32
     w_down: torch.Tensor              # packed int8 (PLAIN) of [E, H, I]
     s_down: torch.Tensor              # [E, H] fp32
-    code: int = _lib.CODE_INT8        # CODE_INT8 or CODE_FP8 (E4M3 codes)
+    code: int = _lib.CODE_INT8        # CODE_INT8, CODE_FP8 or CODE_FP8_FAST (E4M3 codes)
     x_smooth: Optional[torch.Tensor] = None  # [H] fp32 SmoothQuant factor on x, or None
     x_scale_mode: int = _lib.SCALE_DYNAMIC   # scale of x: dynamic, clipped or static
     x_clip: float = 0.0                      # the bound of the clipped / static modes
 
     @classmethod
     def from_int8(cls, router_w, router_b, w_gu, s_gu, w_d, s_d, x_smooth=None,
-                  x_scale_mode: int = _lib.SCALE_DYNAMIC, x_clip: float = 0.0):
+                  x_scale_mode: int = _lib.SCALE_DYNAMIC, x_clip: float = 0.0, fp8_fast: bool = False):
         """From int8 codes [E, 2I, H] / [E, H, I] with per-output-channel scales
-        (uint8 tensors: FP8 E4M3 codes, and the layer runs with FP8 codes).
-        With x_smooth the gate-up codes must already carry 1/x_smooth on their
-        input channels."""
+        (uint8 tensors: FP8 E4M3 codes, and the layer runs with FP8 codes --
+        exact products summed in fp32, or with fp8_fast on the FP8 matrix
+        cores).  With x_smooth the gate-up codes must already carry 1/x_smooth
+        on their input channels."""
         E, twoI, H = w_gu.shape
-        code = _lib.CODE_FP8 if w_gu.dtype == torch.uint8 else _lib.CODE_INT8
+        if w_gu.dtype == torch.uint8:
+            code = _lib.CODE_FP8_FAST if fp8_fast else _lib.CODE_FP8
+        elif fp8_fast:
+            raise ValueError("fp8_fast needs uint8 (E4M3) codes")
+        else:
+            code = _lib.CODE_INT8
         return cls(E, H, twoI // 2, router_w.contiguous(),
                    None if router_b is None else router_b.contiguous(),
                    pack_weights(w_gu.contiguous(), _lib.PACK_GATE_UP), s_gu.contiguous(),
@@ -198,7 +210,7 @@ class MoEWeights:
         q_gu = q_gu.view(E, twoI, H)
         q_d = q_d.view(E, H, I)
         w = cls.from_int8(router_w, router_b, q_gu, s_gu.view(E, twoI), q_d, s_d.view(E, H),
-                          x_smooth, x_scale_mode, x_clip)
+                          x_smooth, x_scale_mode, x_clip, fp8_fast=code == _lib.CODE_FP8_FAST)
         if keep_codes:
             return w, dict(w_gu=q_gu, s_gu=s_gu.view(E, twoI), w_d=q_d, s_d=s_d.view(E, H))
         return w

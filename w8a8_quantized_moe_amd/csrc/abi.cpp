@@ -131,7 +131,7 @@ const char* w8a8_status_string(int status) {
 
 const char* w8a8_last_error(void) { return g_last_error.c_str(); }
 
-int w8a8_abi_version(void) { return 3; }
+int w8a8_abi_version(void) { return 4; }
 
 // The activation-scale options: mode and bound (clip > 0 and finite for the
 // clipped and static modes; ignored for the dynamic one).
@@ -178,15 +178,16 @@ w8a8_status w8a8_quantize_rows_ex(const float* x, int64_t rows, int64_t cols, in
     scale_mode &= ~W8A8_SCALE_COL_RECIPROCAL;
     w8a8_status st = check_scale_opts(scale_mode, clip, col_mul);
     if (st != W8A8_OK) return st;
-    if (code != W8A8_CODE_INT8 && code != W8A8_CODE_FP8_E4M3)
+    if (code != W8A8_CODE_INT8 && code != W8A8_CODE_FP8_E4M3 && code != W8A8_CODE_FP8_E4M3_FAST)
         return fail(W8A8_ERR_INVALID_ARGUMENT, "unknown code %d", (int)code);
     w8a8::QuantOpts opt;
     opt.col_mul = col_mul;
     opt.mode = scale_mode;
     opt.clip = clip;
     opt.col_recip = recip;
+    // both FP8 codes store the same E4M3 values
     return quantize_rows_code(x, rows, cols, ld, (int8_t*)q, scale,
-                              code == W8A8_CODE_FP8_E4M3 ? w8a8::CODE_FP8 : w8a8::CODE_INT8, stream, opt);
+                              code == W8A8_CODE_INT8 ? w8a8::CODE_INT8 : w8a8::CODE_FP8, stream, opt);
 }
 
 w8a8_status w8a8_pack_weights_size(int64_t groups, int64_t n, int64_t k, int kind, size_t* bytes) {
@@ -262,6 +263,13 @@ w8a8_status w8a8_gemm_fp8(const uint8_t* a_q, const float* s_a, const uint8_t* b
                       s_b, M, N, K, out, nullptr, stream);
 }
 
+w8a8_status w8a8_gemm_fp8_fast(const uint8_t* a_q, const float* s_a, const uint8_t* b_packed,
+                               const float* s_b, int64_t M, int64_t N, int64_t K, float* out,
+                               w8a8_stream stream) {
+    return dense_gemm(w8a8::EPI_DENSE_F32, w8a8::CODE_FP8_FAST, (const int8_t*)a_q, s_a,
+                      (const int8_t*)b_packed, s_b, M, N, K, out, nullptr, stream);
+}
+
 w8a8_status w8a8_gemm_i32(const int8_t* a_q, const int8_t* b_packed, int64_t M, int64_t N,
                           int64_t K, int32_t* acc, w8a8_stream stream) {
     return dense_gemm(w8a8::EPI_DENSE_I32, w8a8::CODE_INT8, a_q, nullptr, b_packed, nullptr, M, N, K,
@@ -297,9 +305,12 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
         !aligned(wts->s_down, 4) || (wts->router_b && !aligned(wts->router_b, 4)))
         return fail(W8A8_ERR_MISALIGNED, "x, y, router_w and weights must be 16-byte aligned");
     if (!aligned(workspace, 256)) return fail(W8A8_ERR_MISALIGNED, "workspace must be 256-byte aligned");
-    if (wts->code != W8A8_CODE_INT8 && wts->code != W8A8_CODE_FP8_E4M3)
+    if (wts->code != W8A8_CODE_INT8 && wts->code != W8A8_CODE_FP8_E4M3 &&
+        wts->code != W8A8_CODE_FP8_E4M3_FAST)
         return fail(W8A8_ERR_INVALID_ARGUMENT, "unknown weight code %d", (int)wts->code);
-    const int code = wts->code == W8A8_CODE_FP8_E4M3 ? w8a8::CODE_FP8 : w8a8::CODE_INT8;
+    const int code = wts->code == W8A8_CODE_FP8_E4M3       ? w8a8::CODE_FP8
+                     : wts->code == W8A8_CODE_FP8_E4M3_FAST ? w8a8::CODE_FP8_FAST
+                                                            : w8a8::CODE_INT8;
     if ((st = check_scale_opts(wts->x_scale_mode, wts->x_clip, wts->x_smooth)) != W8A8_OK) return st;
     if (wts->x_smooth && !aligned(wts->x_smooth, 16))
         return fail(W8A8_ERR_MISALIGNED, "x_smooth must be 16-byte aligned");

@@ -203,7 +203,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     // as two 16-byte chunks from the same LDS blocks the INT8 fragments use.
     // A wave's 128x64 outputs are 4x2 blocks of 32x32.  (The 16x16x32 FP8 MFMA
     // issues at a quarter of the rate.)
-    constexpr bool M32 = (CODE == CODE_FP8);
+    constexpr bool M32 = (CODE != CODE_INT8);
     constexpr int FM32 = FM / 2, FN32 = FN / 2;  // 32x32 blocks per wave
     static_assert(!M32 || (FM % 2 == 0 && FN % 2 == 0), "whole 32x32 blocks per wave");
     v4i fa[M32 ? 1 : FM], fb[M32 ? 1 : FN];
@@ -635,7 +635,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
 #pragma unroll
                 for (int i = 0; i < F; ++i) {
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) mma32_fp8(fa32[i], fb32[j], acc[i][j]);
+                    for (int j = 0; j < NJ; ++j) mma32<CODE>(fa32[i], fb32[j], acc[i][j]);
                     if (refill) fa32[i] = frag_a32_h(next_ks, i);
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -686,7 +686,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
 #pragma unroll
                     for (int i = 0; i < F; ++i) {
 #pragma unroll
-                        for (int j = 0; j < FN32; ++j) mma32_fp8(fa32[i], fb32[j], acc[i][j]);
+                        for (int j = 0; j < FN32; ++j) mma32<CODE>(fa32[i], fb32[j], acc[i][j]);
                         if (refill) fa32[i] = frag_a32(next_ks, i);
                         __builtin_amdgcn_sched_barrier(0);
                     }
@@ -789,6 +789,15 @@ hipError_t launch_tile(int epi, const GemmParams& p, int64_t blocks, hipStream_t
             case EPI_DENSE_F32: gemm_i8<BM, BN, WM, WN, NS, EPI_DENSE_F32, CODE_FP8><<<grid, block, 0, s>>>(p); break;
             case EPI_GATE_UP: gemm_i8<BM, BN, WM, WN, NS, EPI_GATE_UP, CODE_FP8><<<grid, block, 0, s>>>(p); break;
             case EPI_DOWN: gemm_i8<BM, BN, WM, WN, NS, EPI_DOWN, CODE_FP8><<<grid, block, 0, s>>>(p); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    if (p.code == CODE_FP8_FAST) {
+        switch (epi) {
+            case EPI_DENSE_F32: gemm_i8<BM, BN, WM, WN, NS, EPI_DENSE_F32, CODE_FP8_FAST><<<grid, block, 0, s>>>(p); break;
+            case EPI_GATE_UP: gemm_i8<BM, BN, WM, WN, NS, EPI_GATE_UP, CODE_FP8_FAST><<<grid, block, 0, s>>>(p); break;
+            case EPI_DOWN: gemm_i8<BM, BN, WM, WN, NS, EPI_DOWN, CODE_FP8_FAST><<<grid, block, 0, s>>>(p); break;
             default: return hipErrorInvalidValue;
         }
         return hipGetLastError();

@@ -179,7 +179,8 @@ hipError_t launch_quant(const float* x, int64_t rows, int64_t cols, int64_t ld, 
 hipError_t launch_quantize_rows(const float* x, int64_t rows, int64_t cols, int64_t ld, int8_t* q,
                                 float* scale, int code, hipStream_t s, const QuantOpts& opt) {
     if (rows == 0) return hipSuccess;
-    if (code == CODE_FP8) return launch_quant<CODE_FP8>(x, rows, cols, ld, q, scale, opt, s);
+    // both FP8 codes store the same E4M3 values
+    if (code == CODE_FP8 || code == CODE_FP8_FAST) return launch_quant<CODE_FP8>(x, rows, cols, ld, q, scale, opt, s);
     if (code == CODE_INT8) return launch_quant<CODE_INT8>(x, rows, cols, ld, q, scale, opt, s);
     return hipErrorInvalidValue;
 }

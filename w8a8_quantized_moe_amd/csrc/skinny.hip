@@ -54,6 +54,12 @@ hipError_t launch_gemm_skinny(int epi, const GemmParams& p, int64_t max_row_bloc
             case EPI_DOWN: gemm_skinny<EPI_DOWN, FN, D, CODE_FP8><<<grid, block, 0, s>>>(p); break;
             default: return hipErrorInvalidValue;
         }
+    } else if (p.code == CODE_FP8_FAST) {
+        switch (epi) {
+            case EPI_GATE_UP: gemm_skinny<EPI_GATE_UP, FN, D, CODE_FP8_FAST><<<grid, block, 0, s>>>(p); break;
+            case EPI_DOWN: gemm_skinny<EPI_DOWN, FN, D, CODE_FP8_FAST><<<grid, block, 0, s>>>(p); break;
+            default: return hipErrorInvalidValue;
+        }
     } else if (p.code == CODE_INT8) {
         switch (epi) {
             case EPI_GATE_UP: gemm_skinny<EPI_GATE_UP, FN, D, CODE_INT8><<<grid, block, 0, s>>>(p); break;
