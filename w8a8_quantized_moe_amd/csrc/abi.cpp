@@ -350,15 +350,26 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
         return check_hip(hipEventRecord((hipEvent_t)events[i], s), "hipEventRecord");
     };
 
-    // 1. per-token quantisation
+    // 1. per-token quantisation: its own launch, or (few tokens, router
+    //    without weight planes) extra workgroups of the router's launch, which
+    //    reads the same x; the "quant" stage is then empty
+    const bool xq_in_route = !plan.has_planes && T <= w8a8::ROUTER_XQUANT_MAX_T;
     if ((st = mark(0)) != W8A8_OK) return st;
-    st = check_hip(w8a8::launch_quantize_rows(x, T, H, H, x_q, x_scale, code, s, x_opt), "quantize x");
-    if (st != W8A8_OK) return st;
+    if (!xq_in_route) {
+        st = check_hip(w8a8::launch_quantize_rows(x, T, H, H, x_q, x_scale, code, s, x_opt), "quantize x");
+        if (st != W8A8_OK) return st;
+    }
 
     // 2-4. router, top-k, permutation
     const int ntv_gu = (int)(2 * I / w8a8::gemm_tile_n(2 * I, code));
     const int ntv_dn = (int)(H / w8a8::gemm_tile_n(H, code));
-    w8a8::RouteInputs ri{x, wts->router_w, wts->router_b, T, H, E, k, plan.splits, bm, ntv_gu, ntv_dn};
+    w8a8::RouteInputs ri{x, wts->router_w, wts->router_b, T, H, E, k, plan.splits, bm, ntv_gu, ntv_dn, {}};
+    if (xq_in_route) {
+        ri.xq.q = x_q;
+        ri.xq.scale = x_scale;
+        ri.xq.opt = x_opt;
+        ri.xq.code = code;
+    }
     w8a8::RouteBuffers rb{};
     rb.partial = (float*)(ws + plan.partial);
     rb.wplanes = plan.has_planes ? (void*)(ws + plan.wplanes) : nullptr;

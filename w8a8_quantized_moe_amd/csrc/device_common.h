@@ -273,6 +273,70 @@ __device__ __forceinline__ uint32_t encode4(const float4& v, float s, float rs) 
     return (uint32_t)w;
 }
 
+// A row's float4 slots i*STRIDE + idx (i < N), times the per-column factor
+// when there is one.  Every load is issued before any value is used: slots
+// past the row's end re-read its last float4 instead of branching around the
+// load (a branch per slot made the compiler wait for each load in turn), and
+// the callers ignore them.  The row is read once, so the loads are
+// non-temporal (streamed past the caches: 27% faster on the large layer's x).
+template <int N, int STRIDE>
+__device__ __forceinline__ void load_row(const float4* __restrict__ xr, const float* col_mul, bool recip,
+                                         int nv, int idx, float4 (&v)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const v4f t = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(xr) + min(i * STRIDE + idx, nv - 1));
+        v[i] = make_float4(t.x, t.y, t.z, t.w);
+    }
+    if (col_mul) {
+        const float4* m = reinterpret_cast<const float4*>(col_mul);
+        float4 f[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) f[i] = m[min(i * STRIDE + idx, nv - 1)];
+        if (recip) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) f[i] = make_float4(1.0f / f[i].x, 1.0f / f[i].y, 1.0f / f[i].z, 1.0f / f[i].w);
+        }
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = mul4(v[i], f[i]);
+    }
+}
+
+// One row quantised by a whole workgroup of NT threads, VPT float4 per thread
+// held in registers (cols % 4 == 0, cols <= 4 * NT * VPT; the row and the
+// factor 16-byte aligned): the row maximum through a wave reduction and NT/64
+// LDS slots (wmax), then the codes as 4-byte stores.  Called by every thread
+// of the workgroup.
+template <int CODE, int NT, int VPT>
+__device__ __forceinline__ void quant_row_wg(const float* __restrict__ xrow, int cols, const QuantOpts& opt,
+                                             int8_t* __restrict__ qrow, float* __restrict__ scale_out,
+                                             float* wmax) {
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const float4* xr = reinterpret_cast<const float4*>(xrow);
+    const int nv = cols >> 2;
+    float4 v[VPT];
+    load_row<VPT, NT>(xr, opt.col_mul, opt.col_recip, nv, tid, v);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+        if (i * NT + tid < nv) amax = fmaxf(amax, amax4(v[i]));
+    amax = wave_max(amax);
+    if (lane == 0) wmax[wv] = amax;
+    __syncthreads();
+    amax = wmax[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) amax = fmaxf(amax, wmax[i]);
+    const float s = scale_base(amax, opt) / code_range<CODE>();
+    const float rs = 1.0f / s;
+    if (tid == 0) *scale_out = s;
+    uint32_t* qr = reinterpret_cast<uint32_t*>(qrow);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int c = i * NT + tid;
+        if (c < nv) qr[c] = encode4<CODE>(v[i], s, rs);
+    }
+}
+
 template <int CODE>
 __device__ __forceinline__ uint8_t encode1(float v, float s) {
     if (CODE == CODE_INT8) return (uint8_t)(int8_t)quant_one(v, s);

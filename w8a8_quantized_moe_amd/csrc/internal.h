@@ -246,6 +246,20 @@ struct RouterPlan {
 };
 RouterPlan router_plan(int T, int E, int H);
 
+// The per-token quantisation of x, run by extra workgroups of the router's
+// launch when the tokens are few (one launch fewer on the layer's critical
+// path; the two read the same x and are otherwise independent).
+struct XQuantJob {
+    int8_t* q = nullptr;     // [T][H] codes; nullptr: no job (x is quantised by its own launch)
+    float* scale = nullptr;  // [T]
+    QuantOpts opt;
+    int code = CODE_INT8;
+};
+// Token counts up to which the router launch also quantises x (its
+// workgroups hold the router's LDS, so many rows are better served by the
+// quantisation kernel's own launch).
+constexpr int ROUTER_XQUANT_MAX_T = 256;
+
 struct RouteInputs {
     const float* x;         // [T][H]
     const float* router_w;  // [E][H]
@@ -254,6 +268,7 @@ struct RouteInputs {
     int splits;             // router_plan(T, E, H).splits
     int bm;                 // m-tile height of the grouped GEMMs (GEMM_BM or SKINNY_BM)
     int ntv_gu, ntv_dn;     // column tiles of the gate-up and down GEMMs (queue bounds)
+    XQuantJob xq;           // x quantised in the same launch (no router planes, T <= ROUTER_XQUANT_MAX_T)
 };
 
 struct RouteBuffers {

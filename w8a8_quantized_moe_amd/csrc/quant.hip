@@ -24,34 +24,6 @@
 namespace w8a8 {
 namespace {
 
-// A row's float4 slots i*STRIDE + idx (i < N), times the per-column factor
-// when there is one.  Every load is issued before any value is used: slots
-// past the row's end re-read its last float4 instead of branching around the
-// load (a branch per slot made the compiler wait for each load in turn), and
-// the callers ignore them.  The row is read once, so the loads are
-// non-temporal (streamed past the caches: 27% faster on the large layer's x).
-template <int N, int STRIDE>
-__device__ __forceinline__ void load_row(const float4* __restrict__ xr, const float* col_mul, bool recip,
-                                         int nv, int idx, float4 (&v)[N]) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const v4f t = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(xr) + min(i * STRIDE + idx, nv - 1));
-        v[i] = make_float4(t.x, t.y, t.z, t.w);
-    }
-    if (col_mul) {
-        const float4* m = reinterpret_cast<const float4*>(col_mul);
-        float4 f[N];
-#pragma unroll
-        for (int i = 0; i < N; ++i) f[i] = m[min(i * STRIDE + idx, nv - 1)];
-        if (recip) {
-#pragma unroll
-            for (int i = 0; i < N; ++i) f[i] = make_float4(1.0f / f[i].x, 1.0f / f[i].y, 1.0f / f[i].z, 1.0f / f[i].w);
-        }
-#pragma unroll
-        for (int i = 0; i < N; ++i) v[i] = mul4(v[i], f[i]);
-    }
-}
-
 // Vector path: cols % 4 == 0, ld % 4 == 0, x 16-byte aligned.  VPL float4 per
 // lane stay in registers (rows up to VPL*256 elements).
 template <int CODE, int VPL>
@@ -91,30 +63,8 @@ __global__ __launch_bounds__(256) void quant_rows_block(const float* __restrict_
                                                         float* __restrict__ scale, QuantOpts opt) {
     (void)rows;  // the grid holds exactly one workgroup per row
     __shared__ float wmax[4];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t row = blockIdx.x;
-    const float4* xr = reinterpret_cast<const float4*>(x + row * ld);
-    const int nv = cols >> 2;
-    float4 v[VPT];
-    load_row<VPT, 256>(xr, opt.col_mul, opt.col_recip, nv, tid, v);
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < VPT; ++i)
-        if (i * 256 + tid < nv) amax = fmaxf(amax, amax4(v[i]));
-    amax = wave_max(amax);
-    if (lane == 0) wmax[wv] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-    const float s = scale_base(amax, opt) / code_range<CODE>();
-    const float rs = 1.0f / s;
-    if (tid == 0) scale[row] = s;
-    uint32_t* qr = reinterpret_cast<uint32_t*>(q + row * (int64_t)cols);
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-        const int c = i * 256 + tid;
-        if (c < nv)
-            qr[c] = encode4<CODE>(v[i], s, rs);
-    }
+    quant_row_wg<CODE, 256, VPT>(x + row * ld, cols, opt, q + row * (int64_t)cols, scale + row, wmax);
 }
 
 // General path: any cols / ld / alignment; the row is read twice (the second

@@ -94,16 +94,41 @@ struct RouterBf16Cfg {
     static constexpr int NS = (163840 / STAGE) < 6 ? (163840 / STAGE) : 6;
 };
 
+// The x-quantisation workgroups of a router launch (blockIdx.y >= S): rows
+// r = q, q + nq, ... with q the workgroup's index among the nq of them, each
+// row by the whole workgroup (quant_row_wg, 512 threads).
+template <int CODE>
+__device__ __forceinline__ void router_xquant_rows(const float* __restrict__ x, int T, int H, int S,
+                                                   const XQuantJob& xq, float* wmax) {
+    const int nq = (gridDim.y - S) * gridDim.x;
+    const int nv = H / 4;
+    for (int r = (blockIdx.y - S) * gridDim.x + blockIdx.x; r < T; r += nq) {
+        const float* xr = x + (int64_t)r * H;
+        int8_t* qr = xq.q + (int64_t)r * H;
+        if (nv <= 512) quant_row_wg<CODE, 512, 1>(xr, H, xq.opt, qr, xq.scale + r, wmax);
+        else if (nv <= 1024) quant_row_wg<CODE, 512, 2>(xr, H, xq.opt, qr, xq.scale + r, wmax);
+        else if (nv <= 2048) quant_row_wg<CODE, 512, 4>(xr, H, xq.opt, qr, xq.scale + r, wmax);
+        else quant_row_wg<CODE, 512, 8>(xr, H, xq.opt, qr, xq.scale + r, wmax);
+        __syncthreads();  // every wave has read wmax before the next row writes it
+    }
+}
+
 template <int EB>
 __global__ __launch_bounds__(512) void router_bf16x3(const float* __restrict__ x,
                                                      const float* __restrict__ wr,
                                                      const float* __restrict__ bias, int T, int H,
-                                                     int E, int ksplit_len,
+                                                     int E, int ksplit_len, int S, XQuantJob xq,
                                                      float* __restrict__ partial) {
     using C = RouterBf16Cfg<EB>;
     constexpr int NS = C::NS, DPW = C::DPW, STAGE = C::STAGE, XBLK = C::XBLK;
     static_assert(NS >= 3, "at least one stage in flight beyond the pair being read");
     __shared__ __attribute__((aligned(1024))) int8_t smem[NS * STAGE];
+    if ((int)blockIdx.y >= S) {  // an x-quantisation workgroup (H <= 16384: 8 float4 per thread)
+        float* wmax = reinterpret_cast<float*>(smem);
+        if (xq.code == CODE_INT8) router_xquant_rows<CODE_INT8>(x, T, H, S, xq, wmax);
+        else router_xquant_rows<CODE_FP8>(x, T, H, S, xq, wmax);
+        return;
+    }
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wt = w >> 2, we = w & 3;
     const int m0 = blockIdx.x * RBM;
@@ -236,7 +261,7 @@ __global__ __launch_bounds__(512) void router_bf16x3(const float* __restrict__ x
                 const int e = (we * EB + j) * 16 + (lane & 15);
                 // a single split writes the finished logits (bias added once)
                 if (t < T && e < E)
-                    out[(int64_t)t * E + e] = (bias && gridDim.y == 1) ? acc[i][j][r] + bias[e] : acc[i][j][r];
+                    out[(int64_t)t * E + e] = (bias && S == 1) ? acc[i][j][r] + bias[e] : acc[i][j][r];
             }
 }
 
@@ -656,6 +681,9 @@ hipError_t launch_route(const RouteInputs& in, const RouteBuffers& b, hipStream_
     MtInfo* mt_info = reinterpret_cast<MtInfo*>(b.mt_info);
     float* out = (S == 1) ? b.logits : b.partial;
     const float *xx = in.x, *wr = in.router_w, *rb = in.router_b;
+    const bool xquant = in.xq.q != nullptr;
+    if (xquant && (b.wplanes || T > ROUTER_XQUANT_MAX_T || H % 4 != 0 || H > 16384))
+        return hipErrorInvalidValue;
     if (b.wplanes) {
         const int eb = router_planes_eb(E), etiles = (E + 32 * eb - 1) / (32 * eb), neb = etiles * 2 * eb;
         int8_t* planes = static_cast<int8_t*>(b.wplanes);
@@ -666,12 +694,15 @@ hipError_t launch_route(const RouteInputs& in, const RouteBuffers& b, hipStream_
         else if (eb == 2) router_planes<2><<<grid, 512, 0, s>>>(xx, planes, rb, T, H, E, neb, H / S, out);
         else router_planes<4><<<grid, 512, 0, s>>>(xx, planes, rb, T, H, E, neb, H / S, out);
     } else {
-        const dim3 grid((T + RBM - 1) / RBM, S);
+        // S router splits per token tile, then (with the x job) enough rows of
+        // quantisation workgroups for one x row each
+        const int tiles = (T + RBM - 1) / RBM;
+        const dim3 grid(tiles, S + (xquant ? (T + tiles - 1) / tiles : 0));
         const int eb = (E + 63) / 64;
-        if (eb == 1) router_bf16x3<1><<<grid, 512, 0, s>>>(xx, wr, rb, T, H, E, H / S, out);
-        else if (eb == 2) router_bf16x3<2><<<grid, 512, 0, s>>>(xx, wr, rb, T, H, E, H / S, out);
-        else if (eb == 3) router_bf16x3<3><<<grid, 512, 0, s>>>(xx, wr, rb, T, H, E, H / S, out);
-        else router_bf16x3<4><<<grid, 512, 0, s>>>(xx, wr, rb, T, H, E, H / S, out);
+        if (eb == 1) router_bf16x3<1><<<grid, 512, 0, s>>>(xx, wr, rb, T, H, E, H / S, S, in.xq, out);
+        else if (eb == 2) router_bf16x3<2><<<grid, 512, 0, s>>>(xx, wr, rb, T, H, E, H / S, S, in.xq, out);
+        else if (eb == 3) router_bf16x3<3><<<grid, 512, 0, s>>>(xx, wr, rb, T, H, E, H / S, S, in.xq, out);
+        else router_bf16x3<4><<<grid, 512, 0, s>>>(xx, wr, rb, T, H, E, H / S, S, in.xq, out);
     }
     if (S > 1) {
         const int64_t n = (int64_t)T * E;
@@ -683,18 +714,18 @@ hipError_t launch_route(const RouteInputs& in, const RouteBuffers& b, hipStream_
                                                     b.chunk_counts, b.expert_counts, b.expert_offsets, in.bm,
                                                     b.mt_prefix, mt_info, b.tile_ctr, b.sorted_assign,
                                                     b.xcd_bounds, in.ntv_gu, in.ntv_dn);
-    } else {
-        topk_count<false><<<nchunks, TOPK_THREADS, 0, s>>>(b.logits, T, E, k, nchunks, b.topk_ids, b.topk_w,
-                                                           b.rank, b.chunk_counts, b.expert_counts,
-                                                           b.expert_offsets, in.bm, b.mt_prefix, mt_info,
-                                                           b.tile_ctr, b.sorted_assign, b.xcd_bounds, in.ntv_gu,
-                                                           in.ntv_dn);
-        chunk_scan<<<E, 256, 0, s>>>(b.chunk_counts, nchunks, b.chunk_base, b.expert_counts);
-        finalize<<<1, 256, 0, s>>>(b.expert_counts, E, in.bm, b.expert_offsets, b.mt_prefix, mt_info,
-                                   b.tile_ctr, b.xcd_bounds, in.ntv_gu, in.ntv_dn);
-        scatter<<<nchunks, 256, 0, s>>>(b.topk_ids, T, k, nchunks, b.expert_offsets, b.chunk_base,
-                                        b.rank, b.sorted_assign);
+        return hipGetLastError();
     }
+    topk_count<false><<<nchunks, TOPK_THREADS, 0, s>>>(b.logits, T, E, k, nchunks,
+                                                       b.topk_ids, b.topk_w, b.rank, b.chunk_counts,
+                                                       b.expert_counts, b.expert_offsets, in.bm, b.mt_prefix,
+                                                       mt_info, b.tile_ctr, b.sorted_assign, b.xcd_bounds,
+                                                       in.ntv_gu, in.ntv_dn);
+    chunk_scan<<<E, 256, 0, s>>>(b.chunk_counts, nchunks, b.chunk_base, b.expert_counts);
+    finalize<<<1, 256, 0, s>>>(b.expert_counts, E, in.bm, b.expert_offsets, b.mt_prefix, mt_info,
+                               b.tile_ctr, b.xcd_bounds, in.ntv_gu, in.ntv_dn);
+    scatter<<<nchunks, 256, 0, s>>>(b.topk_ids, T, k, nchunks, b.expert_offsets, b.chunk_base,
+                                    b.rank, b.sorted_assign);
     return hipGetLastError();
 }
 
