@@ -33,12 +33,17 @@
 //
 // Workgroup -> tile order (XCD-aware).  Workgroups are dealt round-robin to the
 // 8 XCDs, so blockIdx % 8 names the XCD; each XCD owns one contiguous range
-// of the logical tile order (group, n-tile, m-tile; m-tile fastest), so each
+// of the logical tile order (expert, n-tile, m-tile; m-tile fastest), so each
 // XCD works on whole experts and the m-tiles that share a weight tile start
 // side by side.  Grouped GEMMs run persistent: one workgroup per CU drains
 // its XCD's range as a queue (a counter the routing zeroed) and then helps
-// the other XCDs.  The dense GEMM is split into 8 column stripes ("virtual
-// groups" sharing the same rows), one per XCD, one tile per workgroup.
+// the other XCDs.  The routing lists the experts largest first and cuts the
+// order into eight ranges of about equal work, so every queue runs its
+// longest tiles first ("Tencent Hunyuan AI Infra ... Hopper", sec. 1.1: a
+// greedy longest-first tile list; "125B MoE on one RTX 3090", sec. 2.1: the
+// skewed expert loads it balances).  The dense GEMM is split into 8 column
+// stripes ("virtual groups" sharing the same rows), one per XCD, one tile per
+// workgroup.
 #include <atomic>
 #include <type_traits>
 

@@ -1,6 +1,7 @@
 // Grouped INT8 (or FP8 E4M3) GEMM for expert segments of a few rows (the
-// decode regime).  FP8 uses two v_mfma_f32_16x16x32_fp8_fp8 per 64-k fragment
-// (a quarter of the FP8 matrix rate, which the weight streaming never needs).
+// decode regime).  FP8 codes take two matrix instructions per 64-k fragment
+// (mma16: the bf16 cores on decoded codes, or with the fast code the FP8
+// cores' 16x16x32 instruction); the weight streaming never needs more rate.
 //
 // Same computation and epilogues as the tiled grouped GEMM (gemm.hip): the
 // int32 accumulators of x_q . W^T per expert ("W8A8 quantisation of
