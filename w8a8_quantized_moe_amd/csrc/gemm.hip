@@ -39,9 +39,10 @@
 // its XCD's range as a queue (a counter the routing zeroed) and then helps
 // the other XCDs.  The routing lists the experts largest first and cuts the
 // order into eight ranges of about equal work, so every queue runs its
-// longest tiles first ("Tencent Hunyuan AI Infra ... Hopper", sec. 1.1: a
-// greedy longest-first tile list; "125B MoE on one RTX 3090", sec. 2.1: the
-// skewed expert loads it balances).  The dense GEMM is split into 8 column
+// longest tiles first ("Tencent Hunyuan AI Infra ... Hopper", sec. 1.1: tiles
+// dealt to thread blocks by a greedy, load-even assignment, here longest
+// first; "125B MoE on one RTX 3090", sec. 2.1: the hot and cold experts of a
+// skewed routing).  The dense GEMM is split into 8 column
 // stripes ("virtual groups" sharing the same rows), one per XCD, one tile per
 // workgroup.
 #include <atomic>
