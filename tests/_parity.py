@@ -9,10 +9,9 @@ to the host); nothing the GPU computed is ever fed into it.  Comparison rules:
   max(1e-5, 2 * the largest |GPU logit - oracle logit| of that token).  Those
   are counted and excluded from the exact downstream comparisons; for every
   token the GPU ids must still be a valid top-k of the GPU's own logits.
-* h: bit-exact (both sides evaluate SiLU with a correctly rounded exponential
-  and IEEE fp32 operations); a row may differ only by a double rounding of
-  the exponential, and its codes then only next to a rounding midpoint, by
-  one step.  The grouped GEMMs' int32 accumulators are compared exactly: the
+* h: bit-exact on every row (both sides evaluate SiLU with a correctly
+  rounded exponential and IEEE fp32 operations), and so are h's scales and
+  codes.  The grouped GEMMs' int32 accumulators are compared exactly: the
   gate-up ones directly, the down ones through o, which must equal the
   epilogue on the oracle's accumulators (corrected for moved codes) bit for
   bit; o against the oracle's own is then within the routing weight's error.
