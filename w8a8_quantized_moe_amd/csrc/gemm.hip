@@ -89,6 +89,19 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     const int64_t total = (p.seg_offsets ? (int64_t)p.mt_prefix[p.G] : n_mt_dense * p.VG) * p.NTV;
     const int64_t per_xcd = (total + 7) / 8;
 
+    // The claim of the workgroup's next tile (persistent launch): issued by
+    // thread 0 when the current tile's epilogue starts, read after it.
+    // Claiming at the epilogue rather than when a tile starts keeps the
+    // claims in the order the tiles end, which is the order the claimed tiles
+    // start: consecutive tiles (the m-tiles sharing a weight tile, the column
+    // tiles sharing activation rows) then run side by side, whatever the
+    // lengths of the tiles before them.  The epilogue hides the atomic's
+    // latency.
+    int claim_got = 0;
+    auto claim_next = [&]() {
+        if (p.tile_ctr && tid0 == 0) claim_got = atomicAdd(p.tile_ctr + TILE_CTR_STRIDE * (blockIdx.x & 7), 1);
+    };
+
     // One output tile: L -> (group, m-tile, n-tile), K loop, epilogue.
     auto process = [&](const int64_t L) {
     // Thread indices pass through an opaque zero, so that the lane-dependent
@@ -309,6 +322,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     };
     auto epilogue = [&](AccT (&acc)[FM][FN], auto n_tag) {
         constexpr int NF = decltype(n_tag)::value;
+        claim_next();
         if constexpr (EPI == EPI_GU_I32) {
             // raw accumulators straight from registers (a checking path): the
             // column blocks alternate gate / up for the same 16 channels, as in
@@ -397,6 +411,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     //      16 lanes apart. ----
     auto epilogue32 = [&](auto& acc, auto nj_tag) {
         constexpr int NJ = decltype(nj_tag)::value;  // 32-column blocks of this wave
+        claim_next();
         constexpr int NF = 2 * NJ;
         constexpr int OCOLS = (EPI == EPI_GATE_UP) ? NF * 8 : NF * 16;
         constexpr int SROW = OCOLS + 4;
@@ -737,8 +752,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
     // (a counter the routing zeroed); a workgroup takes the next tile of its
     // own XCD's queue and, once that is empty, helps drain the others, so
     // every tile is taken exactly once whatever the number of workgroups per
-    // XCD.  The claim of the next tile is issued when a tile starts and read
-    // when it ends.
+    // XCD.  The claim of the next tile is issued when a tile's epilogue
+    // starts and read when the tile ends (claim_next above).
     const int xcd = blockIdx.x & 7;
     const int64_t slots = gridDim.x >> 3;
     // queue xq: tiles [queue_beg(xq), queue_beg(xq) + queue_len(xq)) -- equal
@@ -772,15 +787,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_i8(GemmParams p) {
         L = __builtin_amdgcn_readfirstlane(next_tile[0]);
     }
     while (L >= 0) {
-        int got = 0;
-        if (p.tile_ctr && tid0 == 0) got = atomicAdd(p.tile_ctr + TILE_CTR_STRIDE * xcd, 1);
-        process(L);
+        process(L);  // claims the next tile at its epilogue (claim_got)
         __syncthreads();  // every wave is done with the ring, the row metadata and next_tile
         if (!p.tile_ctr) {
             sl += slots;
             L = (sl < queue_len(xcd)) ? queue_beg(xcd) + sl : -1;
         } else {
-            if (tid0 == 0) next_tile[0] = next_after(got);
+            if (tid0 == 0) next_tile[0] = next_after(claim_got);
             __syncthreads();
             L = __builtin_amdgcn_readfirstlane(next_tile[0]);
         }
