@@ -232,11 +232,21 @@ def cpu_baseline(inp, target_s, code="int8"):
     x = inp["x"].cpu().numpy()
     wr = inp["wr"].cpu().numpy()
     b = inp["b"].cpu().numpy()
-    w_gu = inp["w_gu"].cpu().numpy()
-    s_gu = inp["s_gu"].cpu().numpy()
-    w_d = inp["w_d"].cpu().numpy()
-    s_d = inp["s_d"].cpu().numpy()
     k, T = inp["k"], inp["T"]
+    if "w_gu_f32" in inp:
+        # fp32 weights: the oracle quantises them itself (per output channel),
+        # as it does in the parity tests; nothing it runs on comes from the GPU path
+        E, I2, H = inp["w_gu_f32"].shape
+        quant = oracle.quantize_rows if code == "int8" else oracle.quantize_rows_fp8
+        w_gu, s_gu = quant(inp["w_gu_f32"].cpu().numpy().reshape(E * I2, H))
+        w_gu, s_gu = w_gu.reshape(E, I2, H), s_gu.reshape(E, I2)
+        w_d, s_d = quant(inp["w_d_f32"].cpu().numpy().reshape(E * H, I2 // 2))
+        w_d, s_d = w_d.reshape(E, H, I2 // 2), s_d.reshape(E, H)
+    else:
+        w_gu = inp["w_gu"].cpu().numpy()
+        s_gu = inp["s_gu"].cpu().numpy()
+        w_d = inp["w_d"].cpu().numpy()
+        s_d = inp["s_d"].cpu().numpy()
 
     def run(n):
         t0 = time.perf_counter()
@@ -328,6 +338,10 @@ def main():
                     help="code type of the expert weights and activations (fp8: E4M3 codes, exact "
                          "products summed in fp32 on the bf16 matrix cores; fp8_fast: E4M3 codes on "
                          "the FP8 matrix cores)")
+    ap.add_argument("--weights", default="codes", choices=["codes", "fp32"],
+                    help="expert weights of the decode, prefill and large layers: codes (int8 or E4M3 "
+                         "codes drawn directly, with per-channel scales) or fp32 (fp32 N(0, 0.02) "
+                         "weights quantised per output channel by the library's offline quantiser)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels-only", action="store_true",
                     help="time the layer only: no device-copy rate, no rocminfo query, no CPU "
@@ -355,14 +369,14 @@ def main():
         return bench_dense(args, torch, synth, w8)
     log(f"[bench] generating workload '{args.workload}' on the GPU")
     over = {} if args.code == "int8" else {"weights": "fp8"}
+    if args.weights == "fp32":
+        over = {"weights": "fp32"}
     inp = synth.moe_inputs(args.workload, device="cuda", **over)
     T, H, E, k, I = inp["T"], inp["H"], inp["E"], inp["k"], inp["I"]
     A = T * k
     if "w_gu_f32" in inp:
         code = {"int8": w8.CODE_INT8, "fp8": w8.CODE_FP8, "fp8_fast": w8.CODE_FP8_FAST}[args.code]
-        wts, codes = w8.MoEWeights.from_fp32(inp["wr"], inp["b"], inp["w_gu_f32"], inp["w_d_f32"],
-                                             keep_codes=True, code=code)
-        inp.update(codes)
+        wts = w8.MoEWeights.from_fp32(inp["wr"], inp["b"], inp["w_gu_f32"], inp["w_d_f32"], code=code)
     else:
         wts = w8.MoEWeights.from_int8(inp["wr"], inp["b"], inp["w_gu"], inp["s_gu"], inp["w_d"],
                                       inp["s_d"], fp8_fast=args.code == "fp8_fast")
@@ -441,12 +455,15 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8" if args.code == "int8" else "fp8_e4m3",
-        "data": f"synthetic (seeded; random {'int8' if args.code == 'int8' else 'FP8 E4M3'} expert "
-                "weights of the layer's shape)",
+        "data": (f"synthetic (seeded; random {'int8' if args.code == 'int8' else 'FP8 E4M3'} expert "
+                 "weights of the layer's shape)") if "w_gu_f32" not in inp else
+                f"synthetic (seeded; fp32 N(0, 0.02) expert weights of the layer's shape, quantised per "
+                f"output channel to {'int8' if args.code == 'int8' else 'FP8 E4M3'} codes)",
         "config": {"workload": f"{args.workload} MoE layer T={T} H={H} E={E} top-{k} I={I}"
                                + {"int8": "", "fp8": ", FP8 E4M3 codes (exact products, fp32 sums)",
                                   "fp8_fast": ", FP8 E4M3 codes on the FP8 matrix cores"}[args.code],
                    "T": T, "H": H, "E": E, "top_k": k, "I": I, "code": args.code,
+                   "weights": "fp32 quantised" if "w_gu_f32" in inp else "codes",
                    "parallelism": "none (1 GPU)"},
         f"{args.code}_tops": round(int8_ops / step_s / 1e12, 2),
         f"{args.code}_frac_of_peak": round(int8_ops / step_s / work["gate_up"][3], 4)

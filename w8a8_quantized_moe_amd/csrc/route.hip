@@ -300,10 +300,10 @@ __global__ __launch_bounds__(256) void router_w_planes(const float* __restrict__
 
 // Workgroup: 128 tokens x 32*EB experts, 8 waves = 4 token quarters x 2
 // expert halves; a wave owns 32 tokens x 16*EB experts (2 x EB blocks of
-// v_mfma_f32_16x16x32_bf16), as above.  blockIdx.x is token tile * expert
-// tiles + expert tile (so the workgroups that share an activation tile are
-// dispatched together; one grid dimension, as the token tiles can exceed the
-// 65535 limit of the others), blockIdx.y the split of H.  A stage holds the
+// v_mfma_f32_16x16x32_bf16), as above.  blockIdx.x names the (token tile,
+// expert tile) pair, the expert tiles of a token tile on one XCD (one grid
+// dimension, as the token tiles can exceed the 65535 limit of the others),
+// blockIdx.y the split of H.  A stage holds the
 // activation tile (16 copy blocks of 8 rows, swizzled as above) and the
 // expert tile's 6*EB plane fragments, padded with repeat copies to a whole
 // number of blocks per wave (the repeats land in slots nobody reads).
@@ -330,8 +330,19 @@ __global__ __launch_bounds__(512) void router_planes(const float* __restrict__ x
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wt = w >> 1, we = w & 1;
     const int etiles = NEB / (2 * EB);
-    const int e_tile = (int)(blockIdx.x % etiles);
-    const int m0 = (int)(blockIdx.x / etiles) * 128;
+    // With several expert tiles, the tiles of one token tile (which read the
+    // same activation rows) go to one XCD, so the rows come from HBM once and
+    // from that XCD's L2 after: workgroup b runs on XCD b % 8, and slot b / 8
+    // of XCD x takes token tile (slot / etiles) * 8 + x, expert tile
+    // slot % etiles (token tiles past the end exit).
+    int tt = (int)blockIdx.x, e_tile = 0;
+    if (etiles > 1) {
+        const int slot = (int)(blockIdx.x >> 3);
+        tt = (slot / etiles) * 8 + (int)(blockIdx.x & 7);
+        e_tile = slot % etiles;
+        if (tt * 128 >= T) return;
+    }
+    const int m0 = tt * 128;
     const int kbeg = blockIdx.y * ksplit_len;
     const int nk = ksplit_len / RBK, ks0 = kbeg / RBK;
 
@@ -689,7 +700,8 @@ hipError_t launch_route(const RouteInputs& in, const RouteBuffers& b, hipStream_
         int8_t* planes = static_cast<int8_t*>(b.wplanes);
         const int64_t n = (int64_t)(H / RBK) * neb * 64;
         router_w_planes<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>(wr, E, H, neb, planes);
-        const dim3 grid((unsigned)(etiles * ((T + 127) / 128)), S);
+        const int ttiles = (T + 127) / 128;
+        const dim3 grid((unsigned)(etiles > 1 ? etiles * ((ttiles + 7) / 8 * 8) : ttiles), S);
         if (eb == 1) router_planes<1><<<grid, 512, 0, s>>>(xx, planes, rb, T, H, E, neb, H / S, out);
         else if (eb == 2) router_planes<2><<<grid, 512, 0, s>>>(xx, planes, rb, T, H, E, neb, H / S, out);
         else router_planes<4><<<grid, 512, 0, s>>>(xx, planes, rb, T, H, E, neb, H / S, out);
