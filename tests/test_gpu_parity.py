@@ -396,6 +396,9 @@ def test_moe_edge_cases(w8, case):
 # split sums along H.
 ROUTER_PLANES = [
     dict(T=2048, H=256, E=256, k=8, I=128),
+    # two expert tiles over 18 token tiles (not a multiple of the 8 XCDs the
+    # token tiles are dealt to) with a ragged last tile
+    dict(T=2230, H=256, E=256, k=4, I=128),
     dict(T=2100, H=512, E=24, k=2, I=128),
     dict(T=2049, H=1024, E=50, k=4, I=128),
     dict(T=4096, H=384, E=200, k=6, I=128),
