@@ -55,6 +55,20 @@ def _check_all(*specs):
     for sp in specs:
         if not sp[0].is_cuda:
             raise ValueError(f"{sp[2]} must be a GPU tensor")
+    _check_device(*[(sp[0], sp[2]) for sp in specs])
+
+
+def _check_device(*named):
+    """The library runs on the current device's current stream: every tensor
+    (name pairs; None skipped) must live on that device."""
+    dev = None
+    for t, name in named:
+        if t is None:
+            continue
+        if dev is None:
+            dev = torch.cuda.current_device()
+        if t.device.index != dev:
+            raise ValueError(f"{name} is on {t.device}, the current device is cuda:{dev}")
 
 
 def quantize_rows(x: torch.Tensor, q: Optional[torch.Tensor] = None,
@@ -83,6 +97,9 @@ def quantize_rows(x: torch.Tensor, q: Optional[torch.Tensor] = None,
     _check_all((q, torch.uint8 if fp8 else torch.int8, "q", (rows, cols)), (scale, torch.float32, "scale", (rows,)))
     if col_reciprocal and col_mul is None:
         raise ValueError("col_reciprocal needs col_mul")
+    if col_mul is not None:
+        _dev(col_mul, torch.float32, "col_mul", shape=(cols,))
+    _check_device((x, "x"), (col_mul, "col_mul"))
     if col_mul is not None or scale_mode != _lib.SCALE_DYNAMIC:
         if col_mul is not None:
             _dev(col_mul, torch.float32, "col_mul", shape=(cols,))
@@ -104,6 +121,7 @@ def pack_weights(w: torch.Tensor, kind: int = _lib.PACK_PLAIN) -> torch.Tensor:
     if w.dtype == torch.uint8:  # FP8 codes: the packing moves bytes
         w = w.view(torch.int8)
     _dev(w, torch.int8, "w")
+    _check_device((w, "w"))
     g, n, k = w.shape
     nbytes = ctypes.c_size_t()
     check(lib.w8a8_pack_weights_size(g, n, k, kind, ctypes.byref(nbytes)))
