@@ -84,7 +84,7 @@ W8A8_API int w8a8_abi_version(void);
  * x      device, fp32, rows x cols with leading dimension ld (elements)
  * q      device, int8, rows x cols, dense (leading dimension cols)
  * scale  device, fp32, rows
- * rows >= 0 (0 is a no-op), 1 <= cols <= 2^24, ld >= cols.
+ * 0 <= rows <= 2^24 (0 is a no-op), 1 <= cols <= 2^24, ld >= cols.
  * Inputs must be finite (NaN/Inf give unspecified codes).
  * ------------------------------------------------------------------------- */
 W8A8_API w8a8_status w8a8_quantize_rows(const float* x, int64_t rows, int64_t cols, int64_t ld, int8_t* q,
@@ -234,7 +234,8 @@ W8A8_API w8a8_status w8a8_gemm_fp8_fast(const uint8_t* a_q, const float* s_a, co
  *   7. y[t] = sum over j = 0..k-1 (in order) of o[t*k+j]   ([HUNYUAN] 1.3)
  *
  * Layouts (all device memory, row-major, 16-byte aligned):
- *   x [T][H] fp32 in, y [T][H] fp32 out (y may not alias x)
+ *   x [T][H] fp32 in, y [T][H] fp32 out (x, y and the workspace must not
+ *   overlap: W8A8_ERR_INVALID_ARGUMENT)
  *   router_w [E][H] fp32, router_b [E] fp32 or NULL (zero bias)
  *   w_gate_up: w8a8_pack_weights([E][2I][H], GATE_UP); s_gate_up [E][2I]
  *   w_down:    w8a8_pack_weights([E][H][I], PLAIN);    s_down    [E][H]

@@ -127,6 +127,8 @@ def test_workspace_holds_router_planes_from_2048_tokens(E, etile):
     (16, 128, 4, 5, 256, 2),      # k > E
     (16, 128, 8, 0, 256, 2),      # k = 0
     (1 << 22, 128, 8, 8, 256, 2),  # T*k > 2^24
+    (1 << 61, 128, 8, 8, 256, 2),  # T*k would overflow int64
+    ((1 << 24) + 1, 128, 8, 1, 256, 2),  # T > 2^24
     (-1, 128, 8, 2, 256, 1),      # negative size
 ])
 def test_workspace_query_rejects(T, H, E, k, I, status):
@@ -164,6 +166,15 @@ def test_forward_checks_workspace_and_alignment():
     assert st == 4
     st = lib.w8a8_moe_forward(sh, ctypes.byref(w), base, base, base + 2 * 65536, 1 << 30, None)
     assert st == 1  # y aliases x
+    # partial overlaps: y inside x (16 x 128 fp32 = 8 KiB), y or x inside the workspace
+    st = lib.w8a8_moe_forward(sh, ctypes.byref(w), base, base + 4096, base + 2 * 65536, 1 << 30, None)
+    assert st == 1 and "overlap x" in lib.w8a8_last_error().decode()
+    st = lib.w8a8_moe_forward(sh, ctypes.byref(w), base, base + 2 * 65536 + 1024, base + 2 * 65536,
+                              1 << 30, None)
+    assert st == 1 and "workspace" in lib.w8a8_last_error().decode()
+    st = lib.w8a8_moe_forward(sh, ctypes.byref(w), base + 2 * 65536 + 4096, base, base + 2 * 65536,
+                              1 << 30, None)
+    assert st == 1 and "workspace" in lib.w8a8_last_error().decode()
     smooth_bad = _lib.MoeWeights(base, None, base, base, base, base, 0, base + 4, 0, 0.0)
     st = lib.w8a8_moe_forward(sh, ctypes.byref(smooth_bad), base, base + 65536, base + 2 * 65536,
                               1 << 30, None)
@@ -181,7 +192,7 @@ def test_forward_checks_workspace_and_alignment():
     for c in (_lib.CODE_FP8, _lib.CODE_FP8_FAST):
         ok = _lib.MoeWeights(base, None, base, base, base, base, c)
         st = lib.w8a8_moe_forward(sh, ctypes.byref(ok), base, base, base + 2 * 65536, 1 << 30, None)
-        assert st == 1 and "alias" in lib.w8a8_last_error().decode()
+        assert st == 1 and "overlap x" in lib.w8a8_last_error().decode()
     # the gate-up accumulator capture: INT8 codes only, a non-NULL output, a
     # large enough aligned workspace
     acc = lib.w8a8_moe_gate_up_acc
@@ -216,6 +227,8 @@ def test_gemm_and_quant_argument_checks():
     assert lib.w8a8_quantize_rows(base, 4, 16, 8, base, base, None) == 1           # ld < cols
     assert lib.w8a8_quantize_rows(None, 0, 16, 16, None, None, None) == 0          # rows = 0
     assert lib.w8a8_quantize_rows(base + 2, 4, 16, 16, base, base, None) == 4
+    assert lib.w8a8_quantize_rows(base, (1 << 24) + 1, 16, 16, base, base, None) == 2  # rows > 2^24
+    assert lib.w8a8_quantize_rows_ex(base, 1 << 40, 16, 16, None, 0, 0.0, 0, base, base, None) == 2
     # scale options: unknown mode, missing or non-finite bound, unknown code, misaligned factor
     assert lib.w8a8_quantize_rows_ex(base, 4, 16, 16, None, 3, 1.0, 0, base, base, None) == 1
     assert lib.w8a8_quantize_rows_ex(base, 4, 16, 16, None, 1, 0.0, 0, base, base, None) == 1

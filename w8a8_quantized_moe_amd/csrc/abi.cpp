@@ -34,6 +34,12 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// [p, p + np) and [q, q + nq) share a byte
+bool overlap(const void* p, size_t np, const void* q, size_t nq) {
+    const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+    return a < b + nq && b < a + np;
+}
+
 int64_t max_m_tiles(int64_t rows, int64_t groups, int64_t bm) {
     // sum over groups of ceil(count/bm) <= (rows + groups*(bm-1)) / bm, and <= rows
     const int64_t bound = (rows + groups * (bm - 1)) / bm;
@@ -67,7 +73,8 @@ w8a8_status check_moe_shape(const w8a8_moe_shape* sh) {
     if (sh->top_k < 1 || sh->top_k > sh->E || sh->top_k > w8a8::MAX_TOPK)
         return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "top_k=%lld: need 1 <= top_k <= min(E, 8)",
                     (long long)sh->top_k);
-    if (sh->T * sh->top_k > (int64_t(1) << 24))
+    // T first: T * top_k of an unchecked T could overflow
+    if (sh->T > (int64_t(1) << 24) || sh->T * sh->top_k > (int64_t(1) << 24))
         return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "T*top_k=%lld exceeds 2^24",
                     (long long)(sh->T * sh->top_k));
     return W8A8_OK;
@@ -152,6 +159,10 @@ static w8a8_status quantize_rows_code(const float* x, int64_t rows, int64_t cols
         return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "cols=%lld: need 1 <= cols <= 2^24", (long long)cols);
     if (ld < cols) return fail(W8A8_ERR_INVALID_ARGUMENT, "ld=%lld < cols=%lld", (long long)ld,
                                (long long)cols);
+    // the long-row kernel runs one workgroup per row: 2^24 rows of 256 threads
+    // is the 32-bit work-item count of a launch
+    if (rows > (int64_t(1) << 24))
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "rows=%lld: need rows <= 2^24", (long long)rows);
     if (rows == 0) return W8A8_OK;
     if (!x || !q || !scale) return fail(W8A8_ERR_INVALID_ARGUMENT, "NULL pointer");
     if (!aligned(x, 4) || !aligned(scale, 4)) return fail(W8A8_ERR_MISALIGNED, "x/scale not 4-byte aligned");
@@ -318,11 +329,17 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     x_opt.col_mul = wts->x_smooth;
     x_opt.mode = wts->x_scale_mode;
     x_opt.clip = wts->x_clip;
-    if (x == y) return fail(W8A8_ERR_INVALID_ARGUMENT, "y must not alias x");
     const MoePlan plan = plan_moe(shape);
     if (workspace_bytes < plan.lay.total_bytes)
         return fail(W8A8_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < required %zu", workspace_bytes,
                     plan.lay.total_bytes);
+    // x is read while the workspace is written, and y is written while o (in
+    // the workspace) is read: none of the three may share memory
+    const size_t xy_bytes = (size_t)shape->T * (size_t)shape->H * 4;
+    if (overlap(x, xy_bytes, y, xy_bytes)) return fail(W8A8_ERR_INVALID_ARGUMENT, "y must not overlap x");
+    if (overlap(x, xy_bytes, workspace, plan.lay.total_bytes) ||
+        overlap(y, xy_bytes, workspace, plan.lay.total_bytes))
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "x and y must not overlap the workspace");
 
     const int T = (int)shape->T, H = (int)shape->H, E = (int)shape->E, k = (int)shape->top_k,
               I = (int)shape->I;
