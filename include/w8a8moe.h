@@ -346,7 +346,8 @@ W8A8_API w8a8_status w8a8_moe_forward_static(const w8a8_moe_shape* shape, const 
  *        up channel c: acc[r][c] = sum_h x_q[t][h] * W_gate_up[e][c][h] with
  *        W_gate_up the unpacked [E][2I][H] codes.
  * Errors: as w8a8_moe_forward; W8A8_ERR_INVALID_ARGUMENT for E4M3 weights
- * (their accumulators are fp32) and a NULL acc.
+ * (their accumulators are fp32), a NULL acc, and an acc that overlaps the
+ * workspace.
  * ------------------------------------------------------------------------- */
 W8A8_API w8a8_status w8a8_moe_gate_up_acc(const w8a8_moe_shape* shape, const w8a8_moe_weights* weights,
                                           const void* workspace, size_t workspace_bytes, int32_t* acc,

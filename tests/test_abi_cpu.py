@@ -202,6 +202,8 @@ def test_forward_checks_workspace_and_alignment():
     assert acc(sh, ctypes.byref(w), base + 2 * 65536, 16, base, None) == 3
     assert acc(sh, ctypes.byref(w), base + 2 * 65536 + 16, 1 << 30, base, None) == 4
     assert acc(sh, ctypes.byref(w), base + 2 * 65536, 1 << 30, base + 2, None) == 4
+    st = acc(sh, ctypes.byref(w), base + 2 * 65536, 1 << 30, base + 2 * 65536 + 4096, None)
+    assert st == 1 and "overlap" in lib.w8a8_last_error().decode()
     assert acc(ctypes.byref(_shape(0, 128, 8, 2, 256)), None, None, 0, None, None) == 0
     # the allocation-free entry point: a layer whose workspace exceeds the static
     # scratch is refused before any device call

@@ -548,6 +548,8 @@ w8a8_status w8a8_moe_gate_up_acc(const w8a8_moe_shape* shape, const w8a8_moe_wei
     const int T = (int)shape->T, H = (int)shape->H, E = (int)shape->E, k = (int)shape->top_k,
               I = (int)shape->I;
     const int64_t A = (int64_t)T * k;
+    if (overlap(acc, (size_t)A * 2 * I * 4, workspace, plan.lay.total_bytes))
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "acc must not overlap the workspace");
     const int bm = moe_bm(A, E);
     const char* ws = (const char*)workspace;
     const w8a8_moe_workspace_layout& L = plan.lay;
