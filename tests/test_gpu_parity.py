@@ -477,6 +477,32 @@ def _wide_range_case(w8, T):
     check_moe(w8, inp)
 
 
+@pytest.mark.parametrize("T,E,k", [(16, 8, 2), (300, 64, 4), (2100, 200, 8)])
+def test_moe_exact_logit_ties_go_to_the_lower_expert(w8, T, E, k):
+    """Zero router weights make every logit exactly its bias; a bias drawn
+    from four values makes exact ties.  The top-k must order by descending
+    logit with ties to the lower expert index (the oracle's reading), for the
+    fused single-chunk routing (T = 16), the chunked one (T = 300) and the
+    weight-plane router (T = 2100).  Tied tokens are excluded from the
+    near-tie-tolerant checks elsewhere, so this pins the tie rule itself."""
+    _say(f"exact logit ties: T={T} E={E} k={k}")
+    inp = synth.moe_inputs("ties", device="cuda", T=T, H=256, E=E, k=k, I=128, n_outlier=0,
+                           outlier_scale=1.0, bf16_x=False, bias="zero", weights="int8")
+    inp["wr"].zero_()
+    b = np.random.default_rng(7 + E).integers(0, 4, size=E).astype(np.float32)
+    inp["b"] = torch.from_numpy(b).cuda()
+    wts, codes = _weights(w8, inp)
+    g = _gpu_moe(w8, inp, wts)
+    assert np.array_equal(g["logits"], np.broadcast_to(b, (T, E)))
+    want = np.argsort(-b, kind="stable")[:k]  # descending, ties to the lower index
+    assert np.array_equal(g["topk_ids"], np.broadcast_to(want, (T, k)))
+    o = oracle.moe_forward(to_np(inp["x"]), to_np(inp["wr"]), b, to_np(codes["w_gu"]), to_np(codes["s_gu"]),
+                           to_np(codes["w_d"]), to_np(codes["s_d"]), k)
+    assert np.array_equal(o["ids"], g["topk_ids"])
+    assert np.abs(g["topk_w"].astype(np.float64) - o["w"]).max() <= 1e-6
+    assert max(rel_metric(g["y"], o["y"])) <= Y_TOL
+
+
 def test_moe_zero_input_gives_zero(w8):
     inp = synth.moe_inputs("edge0", device="cuda", T=50, H=256, E=8, k=2, I=256, n_outlier=0,
                            outlier_scale=1.0, bf16_x=False, bias="zero", weights="int8")
