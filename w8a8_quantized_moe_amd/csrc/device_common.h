@@ -131,50 +131,80 @@ __device__ __forceinline__ void write_ranked_tables(int cnt, int off, int mc, in
     }
 }
 
+// One step of a wave-wide maximum through a DPP lane permutation (a VALU
+// operand modifier, no LDS traffic): lanes whose source lane is out of range,
+// and rows outside ROW_MASK, keep their own value.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float max_dpp(float x) {
+    const int y = __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, ROW_MASK, 0xF, false);
+    return fmaxf(x, __int_as_float(y));
+}
+
+// The maximum over the 64 lanes of a wave, returned to every lane: the
+// maximum of each quad (quad_perm), half row and row (mirrors), then rows 0-1
+// into row 1 and rows 2-3 into row 3 (row_bcast:15), then row 1 into rows 2-3
+// (row_bcast:31); lane 63 ends with the whole wave's maximum.
+__device__ __forceinline__ float wave_max_dpp(float x) {
+    x = max_dpp<0xB1, 0xF>(x);   // quad_perm [1,0,3,2]
+    x = max_dpp<0x4E, 0xF>(x);   // quad_perm [2,3,0,1]
+    x = max_dpp<0x141, 0xF>(x);  // row_half_mirror
+    x = max_dpp<0x140, 0xF>(x);  // row_mirror
+    x = max_dpp<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+    x = max_dpp<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
 // k rounds of a wave-wide arg-max over the logits of N tokens of one wave
 // (token u's lane l holds experts l, l+64, l+128, l+192 in v[u][0..3], -inf
 // past E); ties go to the lower expert index.  Lane 0 writes the picks in
-// descending order to ids/vals.  The rounds of the N tokens run in lockstep,
-// so their shuffle chains overlap instead of following one another.
-// Token u writes to ids/vals + u * ustride, and only if u < n_valid.
+// descending order to ids/vals.  The rounds of the N tokens run in lockstep.
+// A round takes the wave maximum m of the lanes' best values (DPP, no LDS
+// traffic), then the lowest expert index holding m: the lowest lane among
+// those whose best is m in slot 0, else in slot 1, ... (an index in slot s
+// is below every index in slot s+1), from one ballot per slot.  Token u
+// writes to ids/vals + u * ustride, and only if u < n_valid.
 template <int N>
 __device__ __forceinline__ void wave_topk_n(float (&v)[N][4], int lane, int E, int k, int n_valid,
                                             int* ids, float* vals, int ustride) {
 #pragma unroll 1
     for (int j = 0; j < k; ++j) {
-        float bv[N];
-        int bi[N];
+        float bv[N], m[N];
+        int bs[N];
 #pragma unroll
         for (int u = 0; u < N; ++u) {
+            // the lane's best slot, the lower slot on ties
             bv[u] = v[u][0];
-            bi[u] = lane;
-            if (v[u][1] > bv[u]) { bv[u] = v[u][1]; bi[u] = lane + 64; }
-            if (v[u][2] > bv[u]) { bv[u] = v[u][2]; bi[u] = lane + 128; }
-            if (v[u][3] > bv[u]) { bv[u] = v[u][3]; bi[u] = lane + 192; }
-            if (bi[u] >= E) bi[u] = 0x7fffffff;  // padding never wins a tie
+            bs[u] = 0;
+            if (v[u][1] > bv[u]) { bv[u] = v[u][1]; bs[u] = 1; }
+            if (v[u][2] > bv[u]) { bv[u] = v[u][2]; bs[u] = 2; }
+            if (v[u][3] > bv[u]) { bv[u] = v[u][3]; bs[u] = 3; }
         }
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
+        for (int u = 0; u < N; ++u) m[u] = wave_max_dpp(bv[u]);
 #pragma unroll
-            for (int u = 0; u < N; ++u) {
-                const float ov = __shfl_xor(bv[u], o, 64);
-                const int oi = __shfl_xor(bi[u], o, 64);
-                if (ov > bv[u] || (ov == bv[u] && oi < bi[u])) {
-                    bv[u] = ov;
-                    bi[u] = oi;
+        for (int u = 0; u < N; ++u) {
+            // lowest (slot, lane) holding the maximum; padding (index >= E)
+            // never counts.  Lane 0, slot 0 if none does (non-finite logits).
+            int wl = 0, ws = 0;
+#pragma unroll
+            for (int s = 3; s >= 0; --s) {
+                const unsigned long long msk = __ballot(bv[u] == m[u] && bs[u] == s && lane + 64 * s < E);
+                if (msk) {
+                    wl = __ffsll((long long)msk) - 1;
+                    ws = s;
                 }
             }
-        }
-#pragma unroll
-        for (int u = 0; u < N; ++u) {
+            const float val = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv[u]), wl));
             if (lane == 0 && u < n_valid) {
-                ids[u * ustride + j] = bi[u];
-                vals[u * ustride + j] = bv[u];
+                ids[u * ustride + j] = wl + 64 * ws;
+                vals[u * ustride + j] = val;
             }
-            if (bi[u] == lane) v[u][0] = -INFINITY;
-            if (bi[u] == lane + 64) v[u][1] = -INFINITY;
-            if (bi[u] == lane + 128) v[u][2] = -INFINITY;
-            if (bi[u] == lane + 192) v[u][3] = -INFINITY;
+            if (lane == wl) {
+                if (ws == 0) v[u][0] = -INFINITY;
+                else if (ws == 1) v[u][1] = -INFINITY;
+                else if (ws == 2) v[u][2] = -INFINITY;
+                else v[u][3] = -INFINITY;
+            }
         }
     }
 }
