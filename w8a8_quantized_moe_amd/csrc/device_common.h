@@ -8,15 +8,56 @@
 namespace w8a8 {
 
 // Block-wide exclusive scan of one int per thread (NW waves of 64).
+// One step of a wave-wide maximum through a DPP lane permutation (a VALU
+// operand modifier, no LDS traffic): lanes whose source lane is out of range,
+// and rows outside ROW_MASK, keep their own value.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float max_dpp(float x) {
+    const int y = __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, ROW_MASK, 0xF, false);
+    return fmaxf(x, __int_as_float(y));
+}
+
+// The maximum over the 64 lanes of a wave, returned to every lane: the
+// maximum of each quad (quad_perm), half row and row (mirrors), then rows 0-1
+// into row 1 and rows 2-3 into row 3 (row_bcast:15), then row 1 into rows 2-3
+// (row_bcast:31); lane 63 ends with the whole wave's maximum.
+__device__ __forceinline__ float wave_max_dpp(float x) {
+    x = max_dpp<0xB1, 0xF>(x);   // quad_perm [1,0,3,2]
+    x = max_dpp<0x4E, 0xF>(x);   // quad_perm [2,3,0,1]
+    x = max_dpp<0x141, 0xF>(x);  // row_half_mirror
+    x = max_dpp<0x140, 0xF>(x);  // row_mirror
+    x = max_dpp<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+    x = max_dpp<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+// One step of a wave-wide inclusive sum through a DPP lane permutation:
+// lanes outside ROW_MASK / BANK_MASK, and lanes whose source lane is out of
+// range, add 0.
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ int add_dpp(int acc, int src) {
+    return acc + __builtin_amdgcn_update_dpp(0, src, CTRL, ROW_MASK, BANK_MASK, true);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: sums of 4 within each row
+// (row_shr 1..3 of the input), of 8 and 16 (row_shr 4 and 8 of the partial
+// sums, upper banks only), then the totals of row 0 into row 1 and of row 2
+// into row 3 (row_bcast:15) and of rows 0-1 into rows 2-3 (row_bcast:31).
+__device__ __forceinline__ int wave_inclusive_scan_dpp(int x) {
+    int s = add_dpp<0x111, 0xF, 0xF>(x, x);   // row_shr:1
+    s = add_dpp<0x112, 0xF, 0xF>(s, x);       // row_shr:2
+    s = add_dpp<0x113, 0xF, 0xF>(s, x);       // row_shr:3
+    s = add_dpp<0x114, 0xF, 0xE>(s, s);       // row_shr:4, lanes 4-15 of each row
+    s = add_dpp<0x118, 0xF, 0xC>(s, s);       // row_shr:8, lanes 8-15 of each row
+    s = add_dpp<0x142, 0xA, 0xF>(s, s);       // row_bcast:15 into rows 1 and 3
+    s = add_dpp<0x143, 0xC, 0xF>(s, s);       // row_bcast:31 into rows 2 and 3
+    return s;
+}
+
 template <int NW>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* lds /* >= NW ints */) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int u = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += u;
-    }
+    const int incl = wave_inclusive_scan_dpp(v);
     if (lane == 63) lds[w] = incl;
     __syncthreads();
     int base = 0, tot = 0;
@@ -131,29 +172,6 @@ __device__ __forceinline__ void write_ranked_tables(int cnt, int off, int mc, in
     }
 }
 
-// One step of a wave-wide maximum through a DPP lane permutation (a VALU
-// operand modifier, no LDS traffic): lanes whose source lane is out of range,
-// and rows outside ROW_MASK, keep their own value.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float max_dpp(float x) {
-    const int y = __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, ROW_MASK, 0xF, false);
-    return fmaxf(x, __int_as_float(y));
-}
-
-// The maximum over the 64 lanes of a wave, returned to every lane: the
-// maximum of each quad (quad_perm), half row and row (mirrors), then rows 0-1
-// into row 1 and rows 2-3 into row 3 (row_bcast:15), then row 1 into rows 2-3
-// (row_bcast:31); lane 63 ends with the whole wave's maximum.
-__device__ __forceinline__ float wave_max_dpp(float x) {
-    x = max_dpp<0xB1, 0xF>(x);   // quad_perm [1,0,3,2]
-    x = max_dpp<0x4E, 0xF>(x);   // quad_perm [2,3,0,1]
-    x = max_dpp<0x141, 0xF>(x);  // row_half_mirror
-    x = max_dpp<0x140, 0xF>(x);  // row_mirror
-    x = max_dpp<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
-    x = max_dpp<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
-}
-
 // k rounds of a wave-wide arg-max over the logits of N tokens of one wave
 // (token u's lane l holds experts l, l+64, l+128, l+192 in v[u][0..3], -inf
 // past E); ties go to the lower expert index.  Lane 0 writes the picks in
@@ -219,11 +237,7 @@ __device__ __forceinline__ void topk_weights(const float* vals, int k, float* w)
     for (int j = 0; j < k; ++j) w[j] = expf(vals[j] - mx) / z;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
+__device__ __forceinline__ float wave_max(float v) { return wave_max_dpp(v); }
 
 __device__ __forceinline__ int quant_one(float v, float s) {
     if (s == 0.0f) return 0;
