@@ -353,6 +353,31 @@ W8A8_API w8a8_status w8a8_moe_gate_up_acc(const w8a8_moe_shape* shape, const w8a
                                           const void* workspace, size_t workspace_bytes, int32_t* acc,
                                           w8a8_stream stream);
 
+/* -------------------------------------------------------------------------
+ * w8a8_moe_forward_fused: the same layer as w8a8_moe_forward for a
+ * decode-sized batch (T <= 64), in one persistent launch ("Tencent Hunyuan AI
+ * Infra ... Hopper", sec. 1.3: gate, top-k, the index preparation, the expert
+ * GEMMs and the combine in a single FusedMoE kernel).  A cooperative launch
+ * (all workgroups resident) whose phases -- quantisation and router; top-k and
+ * the permutation; gate-up; requantisation of h; down; combine -- are
+ * separated by grid barriers; every workgroup ranks the routing itself, in its
+ * own LDS.  Preceded on the stream by a one-workgroup launch that clears the
+ * barrier words.
+ *   Arguments, layouts, ownership and the workspace as for w8a8_moe_forward
+ *   (the workspace holds the same intermediates afterwards).  Results: x_q,
+ *   h, h_q, o and y as w8a8_moe_forward computes them from the same routing;
+ *   the logits are fp64 sums of the fp32 products rounded once to fp32 (the
+ *   multi-launch router's bf16 three-term split agrees with them within the
+ *   fp32 error bound), so top-k picks can differ only at near ties.
+ *   Calls that share a workspace must not overlap.  The launch is
+ *   cooperative, so it cannot be captured where cooperative launches are not.
+ * Errors: as w8a8_moe_forward; W8A8_ERR_UNSUPPORTED_SHAPE for T > 64;
+ * W8A8_ERR_HIP if the device cannot hold the cooperative grid.
+ * ------------------------------------------------------------------------- */
+W8A8_API w8a8_status w8a8_moe_forward_fused(const w8a8_moe_shape* shape, const w8a8_moe_weights* weights,
+                                            const float* x, float* y, void* workspace, size_t workspace_bytes,
+                                            w8a8_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

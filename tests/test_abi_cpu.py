@@ -46,7 +46,7 @@ def exported_symbols():
 
 def test_header_parses():
     fns = header_functions()
-    assert len(fns) == 17, sorted(fns)
+    assert len(fns) == 18, sorted(fns)
 
 
 def test_every_declared_function_is_exported():
@@ -250,6 +250,26 @@ def test_gemm_and_quant_argument_checks():
     assert lib.w8a8_quantize_rows_ex(base, 4, 16, 16, None, 0x10, 0.0, 0, base, base, None) == 1
     assert lib.w8a8_quantize_rows_ex(base, 4, 16, 16, base, 0x13, 1.0, 0, base, base, None) == 1
     assert lib.w8a8_quantize_rows_ex(None, 0, 16, 16, base, 0x10, 0.0, 0, None, None, None) == 0
+
+
+def test_fused_entry_point_checks():
+    """The single-launch layer: T above 64 is refused, and the multi-launch
+    layer's argument checks apply, all before any launch."""
+    base = 1 << 40
+    fused = lib.w8a8_moe_forward_fused
+    w = _lib.MoeWeights(base, None, base, base, base, base)
+    big = ctypes.byref(_shape(65, 128, 8, 2, 256))
+    assert fused(big, ctypes.byref(w), base, base + 65536, base + 2 * 65536, 1 << 30, None) == 2
+    assert "64" in lib.w8a8_last_error().decode()
+    sh = ctypes.byref(_shape(16, 128, 8, 2, 256))
+    assert fused(sh, ctypes.byref(w), None, None, None, 0, None) == 1            # NULL pointers
+    assert fused(sh, ctypes.byref(w), base, base + 65536, base + 2 * 65536, 16, None) == 3  # workspace
+    assert fused(sh, ctypes.byref(w), base + 4, base + 65536, base + 2 * 65536, 1 << 30, None) == 4
+    st = fused(sh, ctypes.byref(w), base, base + 4096, base + 2 * 65536, 1 << 30, None)
+    assert st == 1 and "overlap" in lib.w8a8_last_error().decode()
+    assert fused(ctypes.byref(_shape(0, 128, 8, 2, 256)), None, None, None, None, 0, None) == 0
+    assert fused(ctypes.byref(_shape(16, 100, 8, 2, 256)), ctypes.byref(w), base, base + 65536,
+                 base + 2 * 65536, 1 << 30, None) == 2                            # H % 128
 
 
 def test_pack_size():

@@ -200,12 +200,14 @@ def _oracle_codes(inp, codes, qopts=None):
     return {n: to_np(v) for n, v in codes.items()}
 
 
-def check_moe(w8, inp, tokens=None, report=None, qopts=None):
+def check_moe(w8, inp, tokens=None, report=None, qopts=None, run=None):
+    """The layer on the GPU against the oracle.  run(w8, inp, wts, codes)
+    replaces the multi-launch layer (_gpu_moe) with another entry point."""
     T, H, E, k, I = inp["T"], inp["H"], inp["E"], inp["k"], inp["I"]
     _say(f"moe T={T} H={H} E={E} k={k} I={I} tokens={'all' if tokens is None else len(tokens)}"
          f"{'' if not qopts else ' x options ' + str(sorted(qopts))}")
     wts, codes = _weights(w8, inp, qopts)
-    g = _gpu_moe(w8, inp, wts)
+    g = run(w8, inp, wts, codes) if run is not None else _gpu_moe(w8, inp, wts)
     oc = _oracle_codes(inp, codes, qopts)
     x = to_np(inp["x"])
     b = to_np(inp["b"])

@@ -90,7 +90,11 @@ SIGNATURES = {
                                             ctypes.c_size_t, _P, _P]),
     "w8a8_moe_forward_static": (ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeWeights), _P, _P,
                                                _P]),
+    "w8a8_moe_forward_fused": (ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeWeights), _P, _P,
+                                              _P, ctypes.c_size_t, _P]),
 }
+
+FUSED_MAX_T = 64  # the single-launch layer's token limit
 
 STATIC_WORKSPACE_BYTES = 64 << 20  # W8A8_STATIC_WORKSPACE_BYTES
 

@@ -14,7 +14,7 @@ from ._lib import check, lib
 
 __all__ = [
     "quantize_rows", "pack_weights", "gemm", "gemm_i32", "MoEWeights", "moe_workspace_layout",
-    "moe_forward", "moe_forward_static", "moe_gate_up_acc", "workspace_views",
+    "moe_forward", "moe_forward_fused", "moe_forward_static", "moe_gate_up_acc", "workspace_views",
 ]
 
 
@@ -300,6 +300,33 @@ def moe_forward(x: torch.Tensor, weights: MoEWeights, top_k: int, y: Optional[to
     else:
         check(lib.w8a8_moe_forward_events(ctypes.byref(sh), ctypes.byref(wts), _ptr(x), _ptr(y),
                                           _ptr(workspace), workspace.numel(), events, _stream()))
+    return y
+
+
+def moe_forward_fused(x: torch.Tensor, weights: MoEWeights, top_k: int, y: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The layer of a decode-sized batch (T <= 64) in one persistent launch
+    (w8a8_moe_forward_fused); arguments and the workspace as for moe_forward."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D tensor [T, H]")
+    T, H = x.shape
+    specs = [(x, torch.float32, "x", (T, weights.H))] + weights.specs()
+    if y is not None:
+        specs.append((y, torch.float32, "y", (T, H)))
+    if workspace is not None:
+        specs.append((workspace, torch.uint8, "workspace"))
+    _check_all(*specs)
+    lay = moe_workspace_layout(T, H, weights.E, top_k, weights.I)
+    if T > 0 and workspace is not None and workspace.numel() < lay["total_bytes"]:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, the layer needs {lay['total_bytes']}")
+    if y is None:
+        y = torch.empty_like(x)
+    if workspace is None:
+        workspace = torch.empty((max(lay["total_bytes"], 256),), dtype=torch.uint8, device=x.device)
+    sh = _shape(T, H, weights.E, top_k, weights.I)
+    wts = weights._struct()
+    check(lib.w8a8_moe_forward_fused(ctypes.byref(sh), ctypes.byref(wts), _ptr(x), _ptr(y), _ptr(workspace),
+                                     workspace.numel(), _stream()))
     return y
 
 

@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libw8a8moe.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["abi.cpp", "quant.hip", "route.hip", "gemm.hip", "skinny.hip", "pack.hip", "combine.hip"]
+SOURCES = ["abi.cpp", "quant.hip", "route.hip", "gemm.hip", "skinny.hip", "pack.hip", "combine.hip",
+           "fused.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

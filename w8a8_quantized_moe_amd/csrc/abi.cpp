@@ -287,27 +287,14 @@ w8a8_status w8a8_gemm_i32(const int8_t* a_q, const int8_t* b_packed, int64_t M, 
                       nullptr, acc, stream);
 }
 
-w8a8_status w8a8_moe_workspace_query(const w8a8_moe_shape* shape, w8a8_moe_workspace_layout* layout) {
-    if (!layout) return fail(W8A8_ERR_INVALID_ARGUMENT, "layout is NULL");
-    w8a8_status st = check_moe_shape(shape);
-    if (st != W8A8_OK) return st;
-    *layout = plan_moe(shape).lay;
-    return W8A8_OK;
-}
-
-w8a8_status w8a8_moe_forward(const w8a8_moe_shape* shape, const w8a8_moe_weights* wts,
-                             const float* x, float* y, void* workspace, size_t workspace_bytes,
-                             w8a8_stream stream) {
-    return w8a8_moe_forward_events(shape, wts, x, y, workspace, workspace_bytes, nullptr, stream);
-}
-
-w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_weights* wts,
-                                    const float* x, float* y, void* workspace,
-                                    size_t workspace_bytes, void* const* events,
-                                    w8a8_stream stream) {
-    w8a8_status st = check_moe_shape(shape);
-    if (st != W8A8_OK) return st;
-    if (shape->T == 0) return W8A8_OK;
+// The argument checks of the layer entry points (after the shape check, for
+// T > 0): pointers, alignment, weight code and scale options, workspace size,
+// and that x, y and the workspace do not overlap.  On success *plan, *code and
+// *x_opt describe the call.
+static w8a8_status check_forward(const w8a8_moe_shape* shape, const w8a8_moe_weights* wts, const float* x,
+                                 const float* y, const void* workspace, size_t workspace_bytes,
+                                 MoePlan* plan_out, int* code_out, w8a8::QuantOpts* x_opt_out) {
+    w8a8_status st;
     if (!wts || !x || !y || !workspace || !wts->router_w || !wts->w_gate_up || !wts->s_gate_up ||
         !wts->w_down || !wts->s_down)
         return fail(W8A8_ERR_INVALID_ARGUMENT, "NULL pointer");
@@ -340,6 +327,38 @@ w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_
     if (overlap(x, xy_bytes, workspace, plan.lay.total_bytes) ||
         overlap(y, xy_bytes, workspace, plan.lay.total_bytes))
         return fail(W8A8_ERR_INVALID_ARGUMENT, "x and y must not overlap the workspace");
+    *plan_out = plan;
+    *code_out = code;
+    *x_opt_out = x_opt;
+    return W8A8_OK;
+}
+
+w8a8_status w8a8_moe_workspace_query(const w8a8_moe_shape* shape, w8a8_moe_workspace_layout* layout) {
+    if (!layout) return fail(W8A8_ERR_INVALID_ARGUMENT, "layout is NULL");
+    w8a8_status st = check_moe_shape(shape);
+    if (st != W8A8_OK) return st;
+    *layout = plan_moe(shape).lay;
+    return W8A8_OK;
+}
+
+w8a8_status w8a8_moe_forward(const w8a8_moe_shape* shape, const w8a8_moe_weights* wts,
+                             const float* x, float* y, void* workspace, size_t workspace_bytes,
+                             w8a8_stream stream) {
+    return w8a8_moe_forward_events(shape, wts, x, y, workspace, workspace_bytes, nullptr, stream);
+}
+
+w8a8_status w8a8_moe_forward_events(const w8a8_moe_shape* shape, const w8a8_moe_weights* wts,
+                                    const float* x, float* y, void* workspace,
+                                    size_t workspace_bytes, void* const* events,
+                                    w8a8_stream stream) {
+    w8a8_status st = check_moe_shape(shape);
+    if (st != W8A8_OK) return st;
+    if (shape->T == 0) return W8A8_OK;
+    MoePlan plan;
+    int code;
+    w8a8::QuantOpts x_opt;
+    if ((st = check_forward(shape, wts, x, y, workspace, workspace_bytes, &plan, &code, &x_opt)) != W8A8_OK)
+        return st;
 
     const int T = (int)shape->T, H = (int)shape->H, E = (int)shape->E, k = (int)shape->top_k,
               I = (int)shape->I;
@@ -576,6 +595,52 @@ w8a8_status w8a8_moe_gate_up_acc(const w8a8_moe_shape* shape, const w8a8_moe_wei
                          ? w8a8::launch_gemm_skinny(w8a8::EPI_GU_I32, gu, max_m_tiles(A, E, bm), s)
                          : w8a8::launch_gemm(w8a8::EPI_GU_I32, gu, max_m_tiles(A, E, bm), s),
                      "gate-up accumulators");
+}
+
+w8a8_status w8a8_moe_forward_fused(const w8a8_moe_shape* shape, const w8a8_moe_weights* wts, const float* x,
+                                   float* y, void* workspace, size_t workspace_bytes, w8a8_stream stream) {
+    w8a8_status st = check_moe_shape(shape);
+    if (st != W8A8_OK) return st;
+    if (shape->T == 0) return W8A8_OK;
+    if (shape->T > w8a8::FUSED_MAX_T)
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "T=%lld: the single-launch layer takes at most %d tokens",
+                    (long long)shape->T, w8a8::FUSED_MAX_T);
+    MoePlan plan;
+    int code;
+    w8a8::QuantOpts x_opt;
+    if ((st = check_forward(shape, wts, x, y, workspace, workspace_bytes, &plan, &code, &x_opt)) != W8A8_OK)
+        return st;
+    char* ws = (char*)workspace;
+    const w8a8_moe_workspace_layout& L = plan.lay;
+    w8a8::FusedParams fp{};
+    fp.x = x;
+    fp.router_w = wts->router_w;
+    fp.router_b = wts->router_b;
+    fp.w_gu = wts->w_gate_up;
+    fp.s_gu = wts->s_gate_up;
+    fp.w_d = wts->w_down;
+    fp.s_d = wts->s_down;
+    fp.y = y;
+    fp.T = (int)shape->T;
+    fp.H = (int)shape->H;
+    fp.E = (int)shape->E;
+    fp.k = (int)shape->top_k;
+    fp.I = (int)shape->I;
+    fp.x_opt = x_opt;
+    fp.x_q = (int8_t*)(ws + L.x_q);
+    fp.x_scale = (float*)(ws + L.x_scale);
+    fp.logits = (float*)(ws + L.logits);
+    fp.topk_ids = (int32_t*)(ws + L.topk_ids);
+    fp.topk_w = (float*)(ws + L.topk_w);
+    fp.expert_counts = (int32_t*)(ws + L.expert_counts);
+    fp.expert_offsets = (int32_t*)(ws + L.expert_offsets);
+    fp.sorted_assign = (int32_t*)(ws + L.sorted_assign);
+    fp.h = (float*)(ws + L.h);
+    fp.h_q = (int8_t*)(ws + L.h_q);
+    fp.h_scale = (float*)(ws + L.h_scale);
+    fp.o = (float*)(ws + L.o);
+    fp.sync = (int32_t*)(ws + plan.tile_ctr);  // the tile queues' words, unused by this launch
+    return check_hip(w8a8::launch_moe_fused(fp, code, (hipStream_t)stream), "single-launch layer");
 }
 
 }  // extern "C"

@@ -306,5 +306,37 @@ static_assert(sizeof(MtInfo) == 16, "one 16-byte load per m-tile");
 
 hipError_t launch_combine(const float* o, int T, int k, int H, float* y, hipStream_t s);
 
+// ---- the whole layer in one launch (decode-sized batches) ----
+constexpr int FUSED_MAX_T = 64;     // tokens: one routing chunk, ranked in every workgroup's LDS
+constexpr int FUSED_WG_PER_CU = 2;  // workgroups per compute unit, all resident (cooperative launch)
+
+struct FusedParams {
+    const float* x;         // [T][H]
+    const float* router_w;  // [E][H]
+    const float* router_b;  // [E] or nullptr
+    const int8_t* w_gu;     // packed gate-up codes
+    const float* s_gu;      // [E][2I]
+    const int8_t* w_d;      // packed down codes
+    const float* s_d;       // [E][H]
+    float* y;               // [T][H]
+    int T, H, E, k, I;
+    QuantOpts x_opt;
+    // the intermediates, at the workspace offsets of the multi-launch layer
+    int8_t* x_q;
+    float* x_scale;
+    float* logits;
+    int32_t* topk_ids;
+    float* topk_w;
+    int32_t* expert_counts;
+    int32_t* expert_offsets;
+    int32_t* sorted_assign;
+    float* h;
+    int8_t* h_q;
+    float* h_scale;
+    float* o;
+    int32_t* sync;          // 2 words: barrier arrivals, timeout flag (zeroed by the launcher)
+};
+hipError_t launch_moe_fused(const FusedParams& p, int code, hipStream_t s);
+
 
 }  // namespace w8a8
