@@ -6,7 +6,8 @@
 // "Tencent Hunyuan AI Infra ... Hopper", sec. 1.3: a single persistent
 // FusedMoE kernel runs gate, top-k, gather, the expert GEMMs and the combine,
 // with the index preparation on chip.  Here:
-//  * one cooperative launch (every workgroup resident at once), phases
+//  * one cooperative launch of one 1024-thread workgroup per CU (every
+//    workgroup resident at once; 16 waves per CU stream the weights), phases
 //    separated by grid barriers: an arrival counter behind agent-scope
 //    release / acquire fences (the eight XCDs' L2 caches are not coherent
 //    with each other), each wait bounded so that every wave exits;
@@ -32,7 +33,7 @@
 namespace w8a8 {
 namespace {
 
-constexpr int FZ_THREADS = 256;  // four waves
+constexpr int FZ_THREADS = 1024;  // sixteen waves: four per SIMD stream the weights
 constexpr int FZ_WAVES = FZ_THREADS / 64;
 constexpr int FZ_TPW = FUSED_MAX_T / FZ_WAVES;                         // tokens per wave in the top-k
 constexpr int FZ_MAX_A = FUSED_MAX_T * MAX_TOPK;                       // assignments
@@ -68,11 +69,10 @@ template <int CODE>
 __device__ __forceinline__ void fused_quant_row(const float* row, int cols, const QuantOpts& opt, int8_t* q,
                                                 float* scale, float* wmax) {
     const int nv = cols / 4;
+    static_assert(4 * FZ_THREADS * 4 >= 16384, "four float4 per thread cover the longest row");
     if (nv <= FZ_THREADS) quant_row_wg<CODE, FZ_THREADS, 1>(row, cols, opt, q, scale, wmax);
     else if (nv <= 2 * FZ_THREADS) quant_row_wg<CODE, FZ_THREADS, 2>(row, cols, opt, q, scale, wmax);
-    else if (nv <= 4 * FZ_THREADS) quant_row_wg<CODE, FZ_THREADS, 4>(row, cols, opt, q, scale, wmax);
-    else if (nv <= 8 * FZ_THREADS) quant_row_wg<CODE, FZ_THREADS, 8>(row, cols, opt, q, scale, wmax);
-    else quant_row_wg<CODE, FZ_THREADS, 16>(row, cols, opt, q, scale, wmax);
+    else quant_row_wg<CODE, FZ_THREADS, 4>(row, cols, opt, q, scale, wmax);
     __syncthreads();  // every wave has read wmax before the next row writes it
 }
 

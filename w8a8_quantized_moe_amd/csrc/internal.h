@@ -308,7 +308,7 @@ hipError_t launch_combine(const float* o, int T, int k, int H, float* y, hipStre
 
 // ---- the whole layer in one launch (decode-sized batches) ----
 constexpr int FUSED_MAX_T = 64;     // tokens: one routing chunk, ranked in every workgroup's LDS
-constexpr int FUSED_WG_PER_CU = 2;  // workgroups per compute unit, all resident (cooperative launch)
+constexpr int FUSED_WG_PER_CU = 1;  // workgroups per compute unit, all resident (cooperative launch)
 
 struct FusedParams {
     const float* x;         // [T][H]
