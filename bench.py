@@ -90,7 +90,7 @@ KERNEL_SOURCES = ["w8a8_quantized_moe_amd/csrc/gemm.hip", "w8a8_quantized_moe_am
                   "w8a8_quantized_moe_amd/csrc/device_common.h", "w8a8_quantized_moe_amd/csrc/skinny_item.h",
                   "w8a8_quantized_moe_amd/csrc/route.hip", "w8a8_quantized_moe_amd/csrc/quant.hip",
                   "w8a8_quantized_moe_amd/csrc/combine.hip", "w8a8_quantized_moe_amd/csrc/skinny.hip",
-                  "w8a8_quantized_moe_amd/csrc/abi.cpp"]
+                  "w8a8_quantized_moe_amd/csrc/abi.cpp", "w8a8_quantized_moe_amd/csrc/fused.hip"]
 PEAK_CLOCK_MHZ = 2400.0  # the engine clock the published matrix peaks assume
 EVENT_EVERY = 5  # timed steps per step that records the dominant stage's events
 
@@ -329,6 +329,78 @@ def bench_dense(args, torch, synth, w8):
     print(json.dumps(out_line), flush=True)
 
 
+def time_stages(args, torch, w8, inp, wts, k, y, ws, hip, events, stages):
+    """The multi-launch layer: per-stage times from a separate pass with an
+    event at every stage boundary, then K timed steps recording the dominant
+    stage's two events in every EVENT_EVERY-th step.  Returns (stage_ms,
+    event_step_ms, dominant stage, ms per step, dominant stage's ms)."""
+    # Stage breakdown: a separate pass of K steps with an event at every stage
+    # boundary (each recorded event costs a few microseconds on the stream, a
+    # tenth of a decode step over the seven boundaries, so the timed pass
+    # below records only the two around the dominant stage).
+    log(f"[bench] stage breakdown over {args.steps} steps")
+    for i in range(args.steps):
+        w8.moe_forward(inp["x"], wts, k, y=y, workspace=ws, events=events[i])
+    torch.cuda.synchronize()
+    stage_ms = {s: 0.0 for s in stages}
+    event_step_ms = 0.0
+    for ev in events:
+        for j, s in enumerate(stages):
+            stage_ms[s] += hip.elapsed_ms(ev[j], ev[j + 1]) / args.steps
+        event_step_ms += hip.elapsed_ms(ev[0], ev[len(stages)]) / args.steps
+    dom = max(stages, key=lambda s: stage_ms[s])
+    jd = stages.index(dom)
+    # the timed pass: events only at the dominant stage's two boundaries, and
+    # only in every EVENT_EVERY-th step (each recorded event costs ~3 us on the
+    # stream: recorded in every step, the two would add 3% to a decode step)
+    timed_ev = []
+    for ev in events:
+        arr = (ctypes.c_void_p * (len(stages) + 1))()
+        arr[jd], arr[jd + 1] = ev[jd], ev[jd + 1]
+        timed_ev.append(arr)
+    sampled = [i for i in range(args.steps) if i % EVENT_EVERY == 0]
+
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        w8.moe_forward(inp["x"], wts, k, y=y, workspace=ws,
+                       events=timed_ev[i] if i % EVENT_EVERY == 0 else None)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    dom_ms = sum(hip.elapsed_ms(events[i][jd], events[i][jd + 1]) for i in sampled) / len(sampled)
+    for ev in events:
+        hip.destroy(ev)
+
+    return stage_ms, event_step_ms, dom, ms_per_step, dom_ms
+
+
+def time_fused(args, torch, w8, inp, wts, k, y, ws, hip, events):
+    """The single-launch layer: K timed steps; every EVENT_EVERY-th records two
+    events around the launch on the layer's stream (torch's current stream).
+    The layer is one kernel, so it is its own dominant stage."""
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    hip.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    sampled = [i for i in range(args.steps) if i % EVENT_EVERY == 0]
+    log(f"[bench] timing {args.steps} steps (single launch)")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if i % EVENT_EVERY == 0:
+            hip.hip.hipEventRecord(events[i][0], stream)
+        w8.moe_forward_fused(inp["x"], wts, k, y=y, workspace=ws)
+        if i % EVENT_EVERY == 0:
+            hip.hip.hipEventRecord(events[i][1], stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    dom_ms = sum(hip.elapsed_ms(events[i][0], events[i][1]) for i in sampled) / len(sampled)
+    for ev in events:
+        hip.destroy(ev)
+    return {"fused": round(dom_ms, 4)}, dom_ms, "fused", ms_per_step, dom_ms
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -344,6 +416,8 @@ def main():
                     help="expert weights of the decode, prefill and large layers: codes (int8 or E4M3 "
                          "codes drawn directly, with per-channel scales) or fp32 (fp32 N(0, 0.02) "
                          "weights quantised per output channel by the library's offline quantiser)")
+    ap.add_argument("--fused", action="store_true",
+                    help="run the layer as one persistent launch (w8a8_moe_forward_fused; T <= 64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels-only", action="store_true",
                     help="time the layer only: no device-copy rate, no rocminfo query, no CPU "
@@ -392,52 +466,25 @@ def main():
     events = [hip.create(len(stages) + 1) for _ in range(args.steps)]
 
     log(f"[bench] warmup {args.warmup} steps")
+    if args.fused and T > w8._lib.FUSED_MAX_T:
+        raise SystemExit(f"--fused runs layers of at most {w8._lib.FUSED_MAX_T} tokens (this one has {T})")
+    forward = w8.moe_forward_fused if args.fused else w8.moe_forward
     for _ in range(args.warmup):
-        w8.moe_forward(inp["x"], wts, k, y=y, workspace=ws)
+        forward(inp["x"], wts, k, y=y, workspace=ws)
     torch.cuda.synchronize()
 
-    # Stage breakdown: a separate pass of K steps with an event at every stage
-    # boundary (each recorded event costs a few microseconds on the stream, a
-    # tenth of a decode step over the seven boundaries, so the timed pass
-    # below records only the two around the dominant stage).
-    log(f"[bench] stage breakdown over {args.steps} steps")
-    for i in range(args.steps):
-        w8.moe_forward(inp["x"], wts, k, y=y, workspace=ws, events=events[i])
-    torch.cuda.synchronize()
-    stage_ms = {s: 0.0 for s in stages}
-    event_step_ms = 0.0
-    for ev in events:
-        for j, s in enumerate(stages):
-            stage_ms[s] += hip.elapsed_ms(ev[j], ev[j + 1]) / args.steps
-        event_step_ms += hip.elapsed_ms(ev[0], ev[len(stages)]) / args.steps
-    dom = max(stages, key=lambda s: stage_ms[s])
-    jd = stages.index(dom)
-    # the timed pass: events only at the dominant stage's two boundaries, and
-    # only in every EVENT_EVERY-th step (each recorded event costs ~3 us on the
-    # stream: recorded in every step, the two would add 3% to a decode step)
-    timed_ev = []
-    for ev in events:
-        arr = (ctypes.c_void_p * (len(stages) + 1))()
-        arr[jd], arr[jd + 1] = ev[jd], ev[jd + 1]
-        timed_ev.append(arr)
-    sampled = [i for i in range(args.steps) if i % EVENT_EVERY == 0]
-
-    log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        w8.moe_forward(inp["x"], wts, k, y=y, workspace=ws,
-                       events=timed_ev[i] if i % EVENT_EVERY == 0 else None)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    dom_ms = sum(hip.elapsed_ms(events[i][jd], events[i][jd + 1]) for i in sampled) / len(sampled)
-    for ev in events:
-        hip.destroy(ev)
+    if args.fused:
+        stage_ms, event_step_ms, dom, ms_per_step, dom_ms = time_fused(args, torch, w8, inp, wts, k, y, ws, hip,
+                                                                      events)
+    else:
+        stage_ms, event_step_ms, dom, ms_per_step, dom_ms = time_stages(args, torch, w8, inp, wts, k, y, ws, hip,
+                                                                       events, stages)
 
     counts = w8.workspace_views(ws, T, H, E, k, I)["expert_counts"].cpu()
     touched = int((counts > 0).sum())
     work = stage_work(T, H, E, k, I, touched, args.code)
+    alg_bytes = 8 * T * H + 4 * H * E + 4 * E + touched * (3 * H * I + 4 * (2 * I + H))
+    work["fused"] = ("hbm", alg_bytes, "GB/s", PEAK_HBM)
     bound, amount, unit, peak = work[dom]
     scale = 1e9 if unit == "GB/s" else 1e12
     achieved = amount / (dom_ms * 1e-3)
@@ -447,7 +494,6 @@ def main():
 
     step_s = ms_per_step * 1e-3
     int8_ops = 6 * A * H * I
-    alg_bytes = 8 * T * H + 4 * H * E + 4 * E + touched * (3 * H * I + 4 * (2 * I + H))
 
     out = {
         "metric": "MoE-layer tokens/s; INT8 TOPS & HBM GB/s as % of MI355X roofline",
@@ -470,6 +516,7 @@ def main():
                                   "fp8_fast": ", FP8 E4M3 codes on the FP8 matrix cores"}[args.code],
                    "T": T, "H": H, "E": E, "top_k": k, "I": I, "code": args.code,
                    "weights": "fp32 quantised" if "w_gu_f32" in inp else "codes",
+                   "launch": "one persistent launch" if args.fused else "one launch per stage",
                    "parallelism": "none (1 GPU)"},
         f"{args.code}_tops": round(int8_ops / step_s / 1e12, 2),
         f"{args.code}_frac_of_peak": round(int8_ops / step_s / work["gate_up"][3], 4)
