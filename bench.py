@@ -90,7 +90,9 @@ KERNEL_SOURCES = ["w8a8_quantized_moe_amd/csrc/gemm.hip", "w8a8_quantized_moe_am
                   "w8a8_quantized_moe_amd/csrc/device_common.h", "w8a8_quantized_moe_amd/csrc/skinny_item.h",
                   "w8a8_quantized_moe_amd/csrc/route.hip", "w8a8_quantized_moe_amd/csrc/quant.hip",
                   "w8a8_quantized_moe_amd/csrc/combine.hip", "w8a8_quantized_moe_amd/csrc/skinny.hip",
-                  "w8a8_quantized_moe_amd/csrc/abi.cpp", "w8a8_quantized_moe_amd/csrc/fused.hip"]
+                  "w8a8_quantized_moe_amd/csrc/abi.cpp"]
+# The single-launch layer (fused.hip) has a kernel trace but no counter record,
+# so its source is not part of the hash.
 PEAK_CLOCK_MHZ = 2400.0  # the engine clock the published matrix peaks assume
 EVENT_EVERY = 5  # timed steps per step that records the dominant stage's events
 

@@ -20,8 +20,10 @@
 //    needed between the routing and the gate-up GEMM; workgroup 0 also
 //    writes them to the workspace;
 //  * phases 3 and 5: the register-fed skinny GEMM's work items (16 rows x 32
-//    columns of one expert per wave) dealt round-robin over all waves, with
-//    the same epilogues as the separate launches;
+//    columns of one expert per wave) dealt round-robin over all waves,
+//    workgroup index fastest, so that the items beyond one per wave land on
+//    every CU rather than on the first few; the same epilogues as the
+//    separate launches;
 //  * phase 4: the requantisation of h (one row per workgroup); phase 6: the
 //    combine, summing each token's k rows in j order from 0.
 // Every value equals what the separate launches compute except the logits
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(FZ_THREADS) void moe_fused(FusedParams p) {
         gu.code = CODE;
         const int NC = 2 * I / 32;
         const int64_t total = (int64_t)total_rb * NC;
-        for (int64_t item = (int64_t)blockIdx.x * FZ_WAVES + w; item < total; item += (int64_t)nwg * FZ_WAVES)
+        for (int64_t item = (int64_t)w * nwg + blockIdx.x; item < total; item += (int64_t)nwg * FZ_WAVES)
             skinny_item<EPI_GATE_UP, 2, 4, CODE>(gu, item, NC, lane);
     }
     grid_sync(p.sync, 2);
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(FZ_THREADS) void moe_fused(FusedParams p) {
         dn.code = CODE;
         const int NC = H / 32;
         const int64_t total = (int64_t)total_rb * NC;
-        for (int64_t item = (int64_t)blockIdx.x * FZ_WAVES + w; item < total; item += (int64_t)nwg * FZ_WAVES)
+        for (int64_t item = (int64_t)w * nwg + blockIdx.x; item < total; item += (int64_t)nwg * FZ_WAVES)
             skinny_item<EPI_DOWN, 2, 4, CODE>(dn, item, NC, lane);
     }
     grid_sync(p.sync, 4);
